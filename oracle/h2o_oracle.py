@@ -1,0 +1,200 @@
+"""CPU oracle of one chunked H2O sparse-attention step.
+
+TEST INFRASTRUCTURE ONLY.  Nothing in the product path may import or call this
+module: it is used by ``tests/``, by ``__graft_entry__.smoke()`` and by the
+``cpu_baseline`` leg of ``bench.py``.  It shares no code with the HIP library.
+
+Sources (cited by page title and section; the pages are web copies of the
+paper "Learning how to Forget: Fine-tuning for Long-Context Sparse Attention",
+arXiv 2608.19920):
+
+* [LtF-zh] the Chinese translation page of the paper:
+  §1 (sparse attention keeps K/V in a fixed number of slots; when the cache is
+  full a policy evicts slots), §1 contributions (the H2O kernel returns the
+  summed attention weights), §2 (SnapKV uses H2O-like summed attention
+  weights; grouped attention heads; FlashInfer's 1 << N_q << N_k regime).
+* [LtF-ko] the Korean summary page of the same paper: the glossary entry for
+  H2O (slots are scored by how often and how strongly they were attended to,
+  and the low scorers are evicted), Table 1 / Table 5 captions (sequences are
+  processed in chunks of S = 2048, 1024 or 128 tokens).
+
+The pages define the policy only in these words; the section that details H2O
+is not part of them.  Where they are silent this oracle takes the plainest
+reading, listed here and implemented below:
+
+  R1  score of a slot = raw sum of the softmax weights it received since it
+      was inserted (no normalisation, no decay);
+  R2  scores are kept per (batch, KV head): the weights of the G query heads
+      that share a KV head are summed together;
+  R3  query head a reads KV head a // G (contiguous groups);
+  R4  logits are tau * <q, k> with tau = 1/sqrt(D) unless a scale is given;
+  R5  every valid cache slot is visible to every chunk query; inside the chunk
+      query i sees chunk keys t <= i;
+  R6  a freshly inserted token starts with the weight its own chunk gave it
+      (the chunk columns of the summed weights);
+  R7  scores are accumulated first, then the S slots to overwrite are chosen
+      among the C cache slots; the chunk itself is always inserted;
+  R8  empty slots (index >= n_valid) are taken first, in slot order; then
+      valid slots in increasing (score, slot) order, NaN scores last;
+  R9  the chosen slots are listed in increasing slot order and chunk token t
+      goes to the t-th of them;
+  R10 positions are absolute token indices; -1 marks an empty slot.
+
+Arithmetic is float64 by default.  ``dtype=np.float32`` runs the same code in
+float32 (the timed CPU baseline).  Inputs are the bf16-rounded values the
+device sees, passed in as float arrays.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+
+# ---------------------------------------------------------------------------
+# a1 + a2: attention of the chunk over (valid cache slots) + (causal chunk)
+# ---------------------------------------------------------------------------
+def attention_chunk(q, k_cache, v_cache, k_new, v_new, n_valid, scale=None,
+                    dtype=np.float64):
+    """Causal GQA attention of a query chunk against cache slots and chunk.
+
+    Shapes: q [B, Hq, S, D]; k_cache, v_cache [B, Hkv, C, D];
+    k_new, v_new [B, Hkv, S, D]; 0 <= n_valid <= C.
+
+    Returns ``(out, lse, wsum)``:
+      out  [B, Hq, S, D]   softmax(logits) @ values over the visible keys (R5);
+      lse  [B, Hq, S]      natural-log log-sum-exp of each row's logits;
+      wsum [B, Hkv, C + S] summed attention weights per key (R1, R2): column
+           j < n_valid is cache slot j, n_valid <= j < C is 0 (empty slot),
+           column C + t is chunk token t.
+
+    Follows [LtF-zh] §1 contributions (attention that also returns the summed
+    attention weights) and §2 (SnapKV's summed attention weights; grouped
+    query heads).
+    """
+    B, Hq, S, D = q.shape
+    Hkv, C = k_cache.shape[1], k_cache.shape[2]
+    G = Hq // Hkv
+    n = int(n_valid)
+    tau = (1.0 / math.sqrt(D)) if (scale is None or scale <= 0) else float(scale)
+    out = np.zeros((B, Hq, S, D), dtype)
+    lse = np.zeros((B, Hq, S), dtype)
+    wsum = np.zeros((B, Hkv, C + S), dtype)
+    # visible[i, j]: all n cache slots, then chunk key t visible iff t <= i
+    visible = np.concatenate([np.ones((S, n), bool),
+                              np.tril(np.ones((S, S), bool))], axis=1)
+    for b in range(B):
+        for a in range(Hq):
+            h = a // G                                            # R3
+            keys = np.concatenate([k_cache[b, h, :n], k_new[b, h]]).astype(dtype)
+            vals = np.concatenate([v_cache[b, h, :n], v_new[b, h]]).astype(dtype)
+            s = dtype(tau) * (q[b, a].astype(dtype) @ keys.T)     # [S, n+S]
+            s = np.where(visible, s, dtype(-np.inf))
+            m = s.max(axis=1, keepdims=True)
+            L = m + np.log(np.exp(s - m).sum(axis=1, keepdims=True))
+            p = np.exp(s - L)                                     # masked -> 0
+            out[b, a] = p @ vals
+            lse[b, a] = L[:, 0]
+            col = p.sum(axis=0)                                   # over queries
+            wsum[b, h, :n] += col[:n]                             # R2
+            wsum[b, h, C:] += col[n:]
+    return out, lse, wsum
+
+
+# ---------------------------------------------------------------------------
+# a3: score accumulation
+# ---------------------------------------------------------------------------
+def score_accumulate(scores, wsum, n_valid):
+    """Add this step's summed weights to the scores of the valid slots (R1)
+    and return the starting scores of the chunk tokens (R6).
+
+    scores [B, Hkv, C] (not modified); wsum [B, Hkv, C + S].
+    Returns ``(scores_after, new_scores [B, Hkv, S])``.
+    [LtF-ko] glossary (H2O scores slots by accumulated attention);
+    [LtF-zh] §2 (summed attention weights as the score).
+    """
+    C = scores.shape[-1]
+    n = int(n_valid)
+    acc = scores.astype(wsum.dtype, copy=True)
+    acc[..., :n] += wsum[..., :n]
+    return acc, wsum[..., C:].copy()
+
+
+# ---------------------------------------------------------------------------
+# a4: eviction choice
+# ---------------------------------------------------------------------------
+def evict_select(scores, n_valid, S):
+    """The S slots each (batch, KV head) overwrites this step (R7-R9).
+
+    Empty slots come first in slot order; the rest are the lowest-scoring valid
+    slots, ties broken towards the lower slot index and NaN scores taken last.
+    The result [B, Hkv, S] (int64) is sorted by slot index.
+    [LtF-zh] §1 (evict slots only when the cache is full);
+    [LtF-ko] glossary (low-scoring entries are the ones evicted).
+    """
+    B, Hkv, C = scores.shape
+    n = int(n_valid)
+    out = np.empty((B, Hkv, S), np.int64)
+    free = np.arange(n, C, dtype=np.int64)
+    for b in range(B):
+        for h in range(Hkv):
+            if free.size >= S:
+                chosen = free[:S]
+            else:
+                need = S - free.size
+                # stable sort: equal scores keep slot order; NaN sorts last
+                order = np.argsort(scores[b, h, :n], kind="stable")
+                chosen = np.concatenate([free, order[:need].astype(np.int64)])
+            out[b, h] = np.sort(chosen)
+    return out
+
+
+# ---------------------------------------------------------------------------
+# a5: scatter of the chunk into the chosen slots
+# ---------------------------------------------------------------------------
+def kv_scatter(k_cache, v_cache, scores, pos, k_new, v_new, new_scores,
+               evict_idx, p0):
+    """Write chunk token t into slot evict_idx[..., t] (R9, R10), in place.
+
+    k_cache, v_cache [B, Hkv, C, D]; scores, pos [B, Hkv, C];
+    k_new, v_new [B, Hkv, S, D]; new_scores [B, Hkv, S].
+    [LtF-zh] §1 (the chunk's K/V take the evicted slots).
+    """
+    B, Hkv, S = evict_idx.shape
+    for b in range(B):
+        for h in range(Hkv):
+            for t in range(S):
+                j = int(evict_idx[b, h, t])
+                k_cache[b, h, j] = k_new[b, h, t]
+                v_cache[b, h, j] = v_new[b, h, t]
+                scores[b, h, j] = new_scores[b, h, t]
+                pos[b, h, j] = p0 + t
+
+
+# ---------------------------------------------------------------------------
+# the whole step
+# ---------------------------------------------------------------------------
+def h2o_step(k_cache, v_cache, scores, pos, n_valid, q, k_new, v_new, p0,
+             scale=None, dtype=np.float64):
+    """One chunk step: attend, accumulate, choose, scatter.
+
+    The cache arrays are not modified; updated copies are returned.
+    Returns a dict with out, lse, wsum, scores_acc (after accumulation, before
+    the scatter), new_scores, evict_idx and the next state (k_cache, v_cache,
+    scores, pos, n_valid).
+    """
+    C = k_cache.shape[2]
+    S = q.shape[2]
+    out, lse, wsum = attention_chunk(q, k_cache, v_cache, k_new, v_new,
+                                     n_valid, scale, dtype)
+    acc, new_scores = score_accumulate(scores, wsum, n_valid)
+    evict = evict_select(acc, n_valid, S)
+    kc = k_cache.copy()
+    vc = v_cache.copy()
+    sc = acc.copy()
+    ps = pos.copy()
+    kv_scatter(kc, vc, sc, ps, k_new, v_new, new_scores, evict, p0)
+    return dict(out=out, lse=lse, wsum=wsum, scores_acc=acc,
+                new_scores=new_scores, evict_idx=evict, k_cache=kc,
+                v_cache=vc, scores=sc, pos=ps,
+                n_valid=min(C, int(n_valid) + S))
