@@ -1,0 +1,217 @@
+#!/usr/bin/env python3
+"""Throughput of the H2O chunk step on one MI355X.
+
+A step is one chunk of S new tokens pushed through every layer of the
+workload: per layer, the four C-ABI calls (attention with summed weights,
+score accumulation, slot choice, scatter) on that layer's full cache.  The
+default workload is the Qwen3-4B-shaped 128k-context case: 32 query / 8 KV
+heads, head_dim 128, 16384 cache slots, chunks of 1024 tokens, 36 layers, in
+the steady state (cache full, every step evicts 1024 slots per KV head).
+Inputs are synthetic (seeded, N(0,1) Q/K/V with 5% of K rows scaled x4) and
+resident in device memory before the timed region starts.
+
+Prints one JSON line.  ``value`` is tokens per second through all layers.
+``roofline`` is for the dominant kernel (pass 1 of the attention: QK^T and PV
+on MFMA), timed with HIP events around each of its launches inside the timed
+region.  ``cpu_baseline`` is the CPU oracle on a bounded sample of the same
+workload (one KV head of one layer-step), scaled to tokens/s.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="qwen3_4b_128k")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+def pairs_per_layer_step(B, Hq, C, S, n):
+    """Causally visible (query, key) pairs of one layer-step."""
+    return B * Hq * S * (n + (S + 1) / 2.0)
+
+
+def make_inputs(wl, steps, gen):
+    import torch
+    B, Hq, Hkv, D, S = wl.batch, wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.chunk_len
+    std = wl.value_std
+    out = []
+    for _ in range(steps):
+        per_layer = []
+        for _ in range(wl.layers):
+            q = (torch.randn((B, Hq, S, D), generator=gen, device="cuda") * std).to(torch.bfloat16)
+            k = torch.randn((B, Hkv, S, D), generator=gen, device="cuda") * std
+            heavy = torch.rand((B, Hkv, S, 1), generator=gen, device="cuda") < wl.heavy_frac
+            k = torch.where(heavy, k * wl.heavy_scale, k).to(torch.bfloat16)
+            v = (torch.randn((B, Hkv, S, D), generator=gen, device="cuda") * std).to(torch.bfloat16)
+            per_layer.append((q, k, v))
+        out.append(per_layer)
+    return out
+
+
+def make_layer_state(wl, gen):
+    import torch
+    B, Hkv, D, C = wl.batch, wl.n_kv_heads, wl.head_dim, wl.cache_len
+    std = wl.value_std
+    k = torch.randn((B, Hkv, C, D), generator=gen, device="cuda") * std
+    heavy = torch.rand((B, Hkv, C, 1), generator=gen, device="cuda") < wl.heavy_frac
+    k = torch.where(heavy, k * wl.heavy_scale, k).to(torch.bfloat16)
+    v = (torch.randn((B, Hkv, C, D), generator=gen, device="cuda") * std).to(torch.bfloat16)
+    scores = torch.rand((B, Hkv, C), generator=gen, device="cuda") * 8.0
+    pos = torch.arange(C, device="cuda", dtype=torch.int64).expand(B, Hkv, C).contiguous()
+    return dict(k=k, v=v, scores=scores, pos=pos)
+
+
+def cpu_baseline(wl, min_seconds=10.0, max_heads=24):
+    """The oracle (float64, as it stands) on single-KV-head slices of steady
+    layer-steps, repeated until about ``min_seconds`` of CPU work; scaled to
+    tokens/s of the whole workload."""
+    import numpy as np
+    import oracle
+    import synth
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = len(os.sched_getaffinity(0))
+    G = wl.group
+    sub = wl.with_(n_kv_heads=1, n_q_heads=G, batch=1)
+    st = synth.steady_state(sub)
+    k, v, sc = st.k, st.v, st.scores.astype(np.float64)
+    spent, heads = 0.0, 0
+    while heads < max_heads and (spent < min_seconds or heads == 0):
+        ch = synth.gen_chunk(sub, 0, sub.fill_steps + 2 + heads)
+        t0 = time.perf_counter()
+        oracle.h2o_step(k, v, sc, st.pos, st.n_valid, ch.q, ch.k, ch.v, ch.p0)
+        spent += time.perf_counter() - t0
+        heads += 1
+    per_head = spent / heads
+    total = per_head * wl.n_kv_heads * wl.batch * wl.layers   # s per step, all heads/layers
+    return {"value": wl.chunk_len / total, "unit": "tokens/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": (f"{heads} steady layer-steps of one KV head each ({G} query heads, "
+                       f"C={wl.cache_len}, S={wl.chunk_len}), float64, {spent:.1f} s; "
+                       f"scaled x{wl.n_kv_heads * wl.batch} heads x{wl.layers} layers")}
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: the H2O step shards by KV head or by "
+              "sequence with no exchange, and runs on more than one GPU are not "
+              "part of this build (use --gpus 1).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import synth
+    import h2o_kv_cache_amd as h2o
+
+    wl = synth.WORKLOADS[args.workload]
+    h2o.load_library()
+    torch.cuda.set_device(0)
+    B, Hq, Hkv, D, C, S, L = (wl.batch, wl.n_q_heads, wl.n_kv_heads, wl.head_dim,
+                              wl.cache_len, wl.chunk_len, wl.layers)
+    shape = h2o.Shape(B, Hq, Hkv, D, C, S, C)   # steady state: cache full
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(20261203)
+    layers = [make_layer_state(wl, gen) for _ in range(L)]
+    inputs = make_inputs(wl, args.warmup + args.steps, gen)
+    out = torch.empty((B, Hq, S, D), dtype=torch.float32, device="cuda")
+    lse = torch.empty((B, Hq, S), dtype=torch.float32, device="cuda")
+    wsum = torch.empty((B, Hkv, C + S), dtype=torch.float32, device="cuda")
+    new_scores = torch.empty((B, Hkv, S), dtype=torch.float32, device="cuda")
+    evict = torch.empty((B, Hkv, S), dtype=torch.int32, device="cuda")
+    ws = torch.empty(h2o.h2o_workspace_size(shape), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+    p0_base = (C // S + 2) * S
+
+    def run_step(i):
+        p0 = p0_base + i * S
+        for li, st in enumerate(layers):
+            q, kn, vn = inputs[i][li]
+            h2o.h2o_attn_chunk(shape, q, st["k"], st["v"], kn, vn, out, lse, wsum, ws, stream)
+            h2o.h2o_score_accumulate(shape, st["scores"], new_scores, wsum, stream)
+            h2o.h2o_evict_select(shape, st["scores"], evict, stream)
+            h2o.kv_scatter(shape, st["k"], st["v"], st["scores"], st["pos"], kn, vn,
+                           new_scores, evict, p0, stream)
+
+    for i in range(args.warmup):
+        run_step(i)
+    torch.cuda.synchronize()
+
+    h2o.h2o_timing_start(args.steps * L)
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_stop = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for i in range(args.steps):
+        run_step(args.warmup + i)
+    t_stop.record(stream)
+    torch.cuda.synchronize()
+    kernel_ms, calls = h2o.h2o_timing_stop()
+    elapsed_ms = t_start.elapsed_time(t_stop)
+
+    ms_per_step = elapsed_ms / args.steps
+    tokens_per_s = S * args.steps / (elapsed_ms / 1e3)
+    pairs = pairs_per_layer_step(B, Hq, C, S, C)
+    fwd_ms = kernel_ms["attn_fwd"] / calls
+    fwd_flop = 4.0 * D * pairs                   # QK^T + PV, 2 flop per MAC
+    achieved = fwd_flop / (fwd_ms * 1e-3) / 1e12
+    per_layer = {k: v / calls for k, v in kernel_ms.items()}
+    per_layer["policy_and_gaps"] = ms_per_step / L - sum(per_layer.values())
+    total_flop_exec = 6.0 * D * pairs
+    step_tflops = total_flop_exec * L / (ms_per_step * 1e-3) / 1e12
+
+    result = {
+        "metric": "H2O chunk-step tokens/s (attn+scores+evict) at 128k ctx; % MFMA/HBM peak",
+        "value": tokens_per_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": wl.name, "batch": B, "q_heads": Hq, "kv_heads": Hkv, "head_dim": D,
+            "cache_len": C, "chunk_len": S, "layers": L, "context": wl.seq_len,
+            "phase": "steady state: cache full, S slots evicted per KV head per layer",
+            "ms_per_layer_step": per_layer,
+            "executed_mfma_tflops_whole_step": step_tflops,
+            "executed_mfma_frac_whole_step": step_tflops / PEAK_BF16_TFLOPS,
+        },
+        "roofline": {
+            "kernel": "attn_fwd_kernel<128> (pass 1: QK^T, online softmax, PV)",
+            "bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None,
+            "per_launch_flop": fwd_flop, "avg_launch_ms": fwd_ms, "launches": calls,
+        },
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(wl)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

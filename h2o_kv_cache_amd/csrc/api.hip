@@ -1,0 +1,195 @@
+// C ABI of libh2o.so (declared in include/h2o.h): argument validation on the
+// host, workspace sizing, and kernel launches on the caller's stream.
+// Nothing here allocates, frees or synchronises (unless H2O_SYNC_DEBUG=1 is
+// set in the environment, which synchronises after every launch to pin a
+// fault to its kernel).
+#include "h2o.h"
+#include "h2o_launch.h"
+
+#include <stdlib.h>
+
+#include <vector>
+
+namespace {
+
+bool sync_debug() {
+    static const bool on = [] {
+        const char* e = getenv("H2O_SYNC_DEBUG");
+        return e && e[0] == '1';
+    }();
+    return on;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Shape checks shared by every entry point.
+h2o_status_t check_shape(const h2o_shape_t* s) {
+    if (!s) return H2O_ERR_INVALID_ARG;
+    if (s->batch < 1 || s->n_q_heads < 1 || s->n_kv_heads < 1 || s->cache_len < 1 ||
+        s->chunk_len < 1)
+        return H2O_ERR_INVALID_ARG;
+    if (s->n_q_heads % s->n_kv_heads != 0) return H2O_ERR_INVALID_ARG;
+    if (s->chunk_len > s->cache_len) return H2O_ERR_INVALID_ARG;
+    if (s->n_valid < 0 || s->n_valid > s->cache_len) return H2O_ERR_INVALID_ARG;
+    if (!(s->scale == s->scale)) return H2O_ERR_INVALID_ARG;   // NaN scale
+    if (s->head_dim != 64 && s->head_dim != 128) return H2O_ERR_UNSUPPORTED;
+    // 32-bit index limits used inside the kernels
+    const long long BH = (long long)s->batch * s->n_kv_heads;
+    const long long W = (long long)s->cache_len + s->chunk_len;
+    if (BH * W >= (1ll << 31) || (long long)s->n_q_heads / s->n_kv_heads * s->chunk_len >= (1ll << 30) ||
+        BH >= 65536)
+        return H2O_ERR_UNSUPPORTED;
+    return H2O_OK;
+}
+
+h2o_status_t from_hip(hipError_t e) { return e == hipSuccess ? H2O_OK : H2O_ERR_HIP; }
+
+// Event timing of the attention kernels (diagnostics, one thread).
+struct Timing {
+    bool on = false;
+    int max_calls = 0;
+    int used = 0;
+    std::vector<hipEvent_t> ev;
+};
+Timing g_timing;
+
+hipEvent_t* timing_slot() {
+    if (!g_timing.on || g_timing.used >= g_timing.max_calls) return nullptr;
+    return &g_timing.ev[(size_t)5 * g_timing.used++];
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t h2o_workspace_size(const h2o_shape_t* s) {
+    if (check_shape(s) != H2O_OK) return 0;
+    h2o::AttnPlan pl;
+    h2o::make_attn_plan(s->batch, s->n_q_heads, s->n_kv_heads, s->head_dim, s->cache_len,
+                        s->chunk_len, s->n_valid, s->scale, &pl);
+    return pl.bytes;
+}
+
+h2o_status_t h2o_attn_chunk(const h2o_shape_t* s, const uint16_t* q, const uint16_t* k_cache,
+                            const uint16_t* v_cache, const uint16_t* k_new,
+                            const uint16_t* v_new, float* out, float* lse, float* wsum,
+                            void* ws, size_t ws_bytes, void* stream) {
+    h2o_status_t st = check_shape(s);
+    if (st != H2O_OK) return st;
+    if (!q || !k_cache || !v_cache || !k_new || !v_new || !out || !wsum)
+        return H2O_ERR_INVALID_ARG;
+    if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(k_new) ||
+        !aligned16(v_new) || !aligned16(out) || !aligned16(wsum) || (lse && !aligned16(lse)))
+        return H2O_ERR_INVALID_ARG;
+    h2o::AttnPlan pl;
+    h2o::make_attn_plan(s->batch, s->n_q_heads, s->n_kv_heads, s->head_dim, s->cache_len,
+                        s->chunk_len, s->n_valid, s->scale, &pl);
+    if (!ws || ((uintptr_t)ws & 255u) || ws_bytes < pl.bytes) return H2O_ERR_WORKSPACE;
+    return from_hip(h2o::launch_attention(pl, q, k_cache, v_cache, k_new, v_new, out, lse,
+                                          wsum, ws, (hipStream_t)stream, sync_debug(),
+                                          timing_slot()));
+}
+
+h2o_status_t h2o_score_accumulate(const h2o_shape_t* s, float* scores, float* new_scores,
+                                  const float* wsum, void* stream) {
+    h2o_status_t st = check_shape(s);
+    if (st != H2O_OK) return st;
+    if (!scores || !new_scores || !wsum) return H2O_ERR_INVALID_ARG;
+    if (!aligned16(scores) || !aligned16(new_scores) || !aligned16(wsum))
+        return H2O_ERR_INVALID_ARG;
+    hipError_t e = h2o::launch_score_accumulate(s->batch * s->n_kv_heads, s->cache_len,
+                                                s->chunk_len, s->n_valid, scores, new_scores,
+                                                wsum, (hipStream_t)stream);
+    if (e == hipSuccess && sync_debug()) e = hipStreamSynchronize((hipStream_t)stream);
+    return from_hip(e);
+}
+
+h2o_status_t h2o_evict_select(const h2o_shape_t* s, const float* scores, int32_t* evict_idx,
+                              void* stream) {
+    h2o_status_t st = check_shape(s);
+    if (st != H2O_OK) return st;
+    if (!scores || !evict_idx) return H2O_ERR_INVALID_ARG;
+    if (!aligned16(scores) || !aligned16(evict_idx)) return H2O_ERR_INVALID_ARG;
+    hipError_t e = h2o::launch_evict_select(s->batch * s->n_kv_heads, s->cache_len,
+                                            s->chunk_len, s->n_valid, scores, evict_idx,
+                                            (hipStream_t)stream);
+    if (e == hipSuccess && sync_debug()) e = hipStreamSynchronize((hipStream_t)stream);
+    return from_hip(e);
+}
+
+h2o_status_t kv_scatter(const h2o_shape_t* s, uint16_t* k_cache, uint16_t* v_cache,
+                        float* scores, int64_t* pos, const uint16_t* k_new,
+                        const uint16_t* v_new, const float* new_scores,
+                        const int32_t* evict_idx, int64_t p0, void* stream) {
+    h2o_status_t st = check_shape(s);
+    if (st != H2O_OK) return st;
+    if (!k_cache || !v_cache || !scores || !k_new || !v_new || !new_scores || !evict_idx)
+        return H2O_ERR_INVALID_ARG;
+    if (!aligned16(k_cache) || !aligned16(v_cache) || !aligned16(scores) ||
+        !aligned16(k_new) || !aligned16(v_new) || !aligned16(new_scores) ||
+        !aligned16(evict_idx) || (pos && !aligned16(pos)))
+        return H2O_ERR_INVALID_ARG;
+    if (p0 < 0) return H2O_ERR_INVALID_ARG;
+    hipError_t e = h2o::launch_kv_scatter(s->batch * s->n_kv_heads, s->head_dim, s->cache_len,
+                                          s->chunk_len, k_cache, v_cache, scores, pos, k_new,
+                                          v_new, new_scores, evict_idx, p0,
+                                          (hipStream_t)stream);
+    if (e == hipSuccess && sync_debug()) e = hipStreamSynchronize((hipStream_t)stream);
+    return from_hip(e);
+}
+
+h2o_status_t h2o_timing_start(int32_t max_calls) {
+    if (max_calls < 1 || max_calls > (1 << 20) || g_timing.on) return H2O_ERR_INVALID_ARG;
+    g_timing.ev.assign((size_t)5 * max_calls, nullptr);
+    for (auto& e : g_timing.ev) {
+        if (hipEventCreate(&e) != hipSuccess) {
+            for (auto& x : g_timing.ev)
+                if (x) hipEventDestroy(x);
+            g_timing.ev.clear();
+            return H2O_ERR_HIP;
+        }
+    }
+    g_timing.max_calls = max_calls;
+    g_timing.used = 0;
+    g_timing.on = true;
+    return H2O_OK;
+}
+
+h2o_status_t h2o_timing_stop(double* ms, int32_t* calls) {
+    if (!g_timing.on || !ms || !calls) return H2O_ERR_INVALID_ARG;
+    h2o_status_t st = H2O_OK;
+    for (int k = 0; k < 4; ++k) ms[k] = 0.0;
+    if (g_timing.used > 0 &&
+        hipEventSynchronize(g_timing.ev[(size_t)5 * g_timing.used - 1]) != hipSuccess)
+        st = H2O_ERR_HIP;
+    for (int c = 0; c < g_timing.used && st == H2O_OK; ++c) {
+        for (int k = 0; k < 4; ++k) {
+            float t = 0.f;
+            if (hipEventElapsedTime(&t, g_timing.ev[(size_t)5 * c + k],
+                                    g_timing.ev[(size_t)5 * c + k + 1]) != hipSuccess) {
+                st = H2O_ERR_HIP;
+                break;
+            }
+            ms[k] += t;
+        }
+    }
+    *calls = g_timing.used;
+    for (auto& e : g_timing.ev) hipEventDestroy(e);
+    g_timing.ev.clear();
+    g_timing.on = false;
+    g_timing.used = 0;
+    return st;
+}
+
+const char* h2o_status_string(h2o_status_t st) {
+    switch (st) {
+        case H2O_OK: return "ok";
+        case H2O_ERR_INVALID_ARG: return "invalid argument";
+        case H2O_ERR_UNSUPPORTED: return "unsupported shape";
+        case H2O_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
+        case H2O_ERR_HIP: return "HIP launch failed";
+    }
+    return "unknown status";
+}
+
+}  // extern "C"

@@ -1,0 +1,56 @@
+// Host-side launchers of the gfx950 kernels (internal to libh2o.so).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace h2o {
+
+// Tiling shared by the attention kernels.
+constexpr int kKeyTile = 64;        // keys per LDS tile
+constexpr int kRowsPerWave = 32;    // query rows (head, query) per wave
+constexpr int kWaves = 4;           // waves per workgroup
+constexpr int kRowsPerBlock = kRowsPerWave * kWaves;
+
+// Rows of a (b, kv head) are r = i * G + g: query i of head h*G + g.
+struct AttnGeom {
+    int B, Hq, Hkv, G, D, C, S, n;
+    int R;          // G * S rows per (b, kv head)
+    int n_qt;       // row tiles: ceil(R / kRowsPerBlock)
+    int rows_pad;   // n_qt * kRowsPerBlock
+    float c;        // logit scale * log2(e)
+};
+
+struct AttnPlan {
+    AttnGeom g;
+    int split1;     // key splits of pass 1 (log-sum-exp and output)
+    int split2;     // key splits of pass 2 (summed weights)
+    size_t off_o, off_ml, off_l2, off_wp, bytes;
+};
+
+bool make_attn_plan(int B, int Hq, int Hkv, int D, int C, int S, int n,
+                    float scale, AttnPlan* plan);
+
+hipError_t launch_attention(const AttnPlan& plan, const uint16_t* q,
+                            const uint16_t* kc, const uint16_t* vc,
+                            const uint16_t* kn, const uint16_t* vn, float* out,
+                            float* lse, float* wsum, void* ws,
+                            hipStream_t stream, bool sync_debug,
+                            hipEvent_t* ev5 /* nullable: 5 timing events */);
+
+hipError_t launch_score_accumulate(int BH, int C, int S, int n, float* scores,
+                                   float* new_scores, const float* wsum,
+                                   hipStream_t stream);
+
+hipError_t launch_evict_select(int BH, int C, int S, int n,
+                               const float* scores, int32_t* evict_idx,
+                               hipStream_t stream);
+
+hipError_t launch_kv_scatter(int BH, int D, int C, int S, uint16_t* kc,
+                             uint16_t* vc, float* scores, int64_t* pos,
+                             const uint16_t* kn, const uint16_t* vn,
+                             const float* new_scores, const int32_t* evict_idx,
+                             int64_t p0, hipStream_t stream);
+
+}  // namespace h2o

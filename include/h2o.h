@@ -1,0 +1,171 @@
+/*
+ * h2o.h -- C ABI of libh2o.so: one chunked step of Heavy-Hitter Oracle (H2O)
+ * sparse attention over a fixed-size KV cache, for AMD Instinct MI355X
+ * (gfx950).
+ *
+ * The method: "Learning how to Forget: Fine-tuning for Long-Context Sparse
+ * Attention" (arXiv 2608.19920).  Its Chinese translation page, §1, keeps K/V
+ * in a fixed number of cache slots and evicts slots by a policy once the cache
+ * is full; §1 (contributions) gives H2O an attention kernel that also returns
+ * the summed attention weights; §2 describes those summed weights as the
+ * H2O-style score.  The Korean summary page's glossary describes H2O as
+ * scoring entries by how often and how strongly they were attended to and
+ * evicting the low scorers; its Table 1 / Table 5 captions process sequences
+ * in chunks of S tokens.
+ *
+ * A step, for every (batch b, KV head h), with G = n_q_heads / n_kv_heads
+ * query heads per KV head (query head a reads KV head a / G):
+ *   1. h2o_attn_chunk       attention of the S chunk queries over the valid
+ *                           cache slots [0, n_valid) plus the chunk keys t <= i
+ *                           (causal inside the chunk); returns the output, the
+ *                           log-sum-exp and the summed attention weights.
+ *   2. h2o_score_accumulate scores[j] += wsum[j] for valid slots; the chunk
+ *                           tokens' starting scores are their own columns.
+ *   3. h2o_evict_select     the S slots to overwrite: empty slots first (slot
+ *                           order), then the lowest (score, slot) valid slots;
+ *                           listed in increasing slot order.
+ *   4. kv_scatter           chunk token t -> slot evict_idx[t]: K, V, score
+ *                           and absolute position.
+ * The caller advances n_valid to min(cache_len, n_valid + chunk_len) after the
+ * step.  All four calls use the same h2o_shape_t (same n_valid).
+ *
+ * Conventions shared by every entry point
+ *   - All tensor pointers are DEVICE pointers to caller-owned memory, dense
+ *     and row-major in the layouts given below, 16-byte aligned.  "bf16" is
+ *     the 16-bit bfloat16 bit pattern (uint16_t).
+ *   - Nothing allocates or frees memory and nothing synchronises: every call
+ *     only enqueues kernels on `stream` (a hipStream_t; NULL = the legacy
+ *     default stream) and returns.  The calls can be captured in a HIP graph.
+ *   - Argument errors are found on the host before anything is enqueued; the
+ *     call then returns a non-zero status and touches no buffer.
+ *     H2O_ERR_HIP means a launch failed (hipGetLastError after the launch).
+ *     Faults inside kernels surface at the caller's next synchronisation.
+ *   - Supported: head_dim in {64, 128}; 1 <= chunk_len <= cache_len;
+ *     0 <= n_valid <= cache_len; n_q_heads a multiple of n_kv_heads.
+ *   - Calls are asynchronous and stream-ordered; two calls that share buffers
+ *     must be ordered by the caller (same stream or events).
+ */
+#ifndef H2O_H
+#define H2O_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    H2O_OK = 0,
+    H2O_ERR_INVALID_ARG = 1,   /* null/misaligned pointer, bad sizes        */
+    H2O_ERR_UNSUPPORTED = 2,   /* valid but unsupported (e.g. head_dim 96)  */
+    H2O_ERR_WORKSPACE = 3,     /* workspace missing or smaller than needed  */
+    H2O_ERR_HIP = 4            /* a HIP launch failed                        */
+} h2o_status_t;
+
+typedef struct {
+    int32_t batch;       /* B  >= 1                                        */
+    int32_t n_q_heads;   /* Hq >= 1, multiple of n_kv_heads                */
+    int32_t n_kv_heads;  /* Hkv >= 1                                       */
+    int32_t head_dim;    /* D in {64, 128}                                 */
+    int32_t cache_len;   /* C  >= 1: slots per (b, kv head)                */
+    int32_t chunk_len;   /* S in [1, C]: tokens in this chunk              */
+    int32_t n_valid;     /* n in [0, C]: filled slots before the step      */
+    float   scale;       /* logit scale; <= 0 selects 1/sqrt(D)            */
+} h2o_shape_t;
+
+/* Bytes of device workspace h2o_attn_chunk needs for this shape.  Depends on
+ * (B, Hq, Hkv, D, C, S) only, not on n_valid, so one allocation serves every
+ * step of a run.  Returns 0 for an invalid shape. */
+size_t h2o_workspace_size(const h2o_shape_t* shape);
+
+/* Step 1 -- attention of the chunk plus summed attention weights.
+ * ([LtF] Chinese page §1 contributions: an SDPA kernel that returns the summed
+ * attention weights; §2: FlashInfer's few-queries-many-keys regime.)
+ *   q        [B, Hq, S, D]   bf16  chunk queries
+ *   k_cache  [B, Hkv, C, D]  bf16  cache keys; slots >= n_valid are ignored
+ *   v_cache  [B, Hkv, C, D]  bf16  cache values
+ *   k_new    [B, Hkv, S, D]  bf16  chunk keys
+ *   v_new    [B, Hkv, S, D]  bf16  chunk values
+ *   out      [B, Hq, S, D]   fp32  softmax-weighted values (written)
+ *   lse      [B, Hq, S]      fp32  natural log-sum-exp of each query's scaled
+ *                                  logits (written; may be NULL)
+ *   wsum     [B, Hkv, C + S] fp32  summed weights (written): column j < n is
+ *                                  cache slot j summed over the G query heads
+ *                                  and S queries; n <= j < C is 0; column
+ *                                  C + t is chunk token t
+ *   ws, ws_bytes                   device workspace of at least
+ *                                  h2o_workspace_size(shape) bytes, 256-byte
+ *                                  aligned; its contents are scratch.
+ * Logits are scale * <q, k>; visible keys of query i are the n cache slots and
+ * chunk tokens t <= i.  Reductions run in a fixed order: repeated calls give
+ * bit-identical results. */
+h2o_status_t h2o_attn_chunk(const h2o_shape_t* shape,
+                            const uint16_t* q, const uint16_t* k_cache,
+                            const uint16_t* v_cache, const uint16_t* k_new,
+                            const uint16_t* v_new, float* out, float* lse,
+                            float* wsum, void* ws, size_t ws_bytes,
+                            void* stream);
+
+/* Step 2 -- score accumulation.
+ * ([LtF] Korean page glossary: H2O scores entries by accumulated attention;
+ * Chinese page §2: summed attention weights as the score.)
+ *   scores     [B, Hkv, C]     fp32  in/out: scores[j] += wsum[j] for j < n;
+ *                                    slots >= n are left untouched
+ *   new_scores [B, Hkv, S]     fp32  out: new_scores[t] = wsum[C + t]
+ *   wsum       [B, Hkv, C + S] fp32  in: from h2o_attn_chunk */
+h2o_status_t h2o_score_accumulate(const h2o_shape_t* shape, float* scores,
+                                  float* new_scores, const float* wsum,
+                                  void* stream);
+
+/* Step 3 -- choice of the S slots to overwrite, per (b, kv head).
+ * ([LtF] Chinese page §1: evict by policy only when the cache is full;
+ * Korean page glossary: the low scorers are evicted.)
+ *   scores    [B, Hkv, C] fp32   in (after h2o_score_accumulate)
+ *   evict_idx [B, Hkv, S] int32  out: slot indices in increasing order.
+ * Empty slots n..C-1 are taken first; the rest are the valid slots with the
+ * smallest (score, slot) pairs -- equal scores go to the lower slot, -0.0
+ * equals +0.0 and NaN ranks above +inf.  While n + S <= C this is simply
+ * n, n+1, ..., n+S-1. */
+h2o_status_t h2o_evict_select(const h2o_shape_t* shape, const float* scores,
+                              int32_t* evict_idx, void* stream);
+
+/* Step 4 -- write the chunk into the chosen slots (in place).
+ * ([LtF] Chinese page §1: the chunk's K/V replace the evicted slots.)
+ *   k_cache, v_cache [B, Hkv, C, D] bf16   in/out
+ *   scores           [B, Hkv, C]    fp32   in/out: scores[e_t] = new_scores[t]
+ *   pos              [B, Hkv, C]    int64  in/out: pos[e_t] = p0 + t (may be
+ *                                          NULL: positions not tracked)
+ *   k_new, v_new     [B, Hkv, S, D] bf16   chunk rows
+ *   new_scores       [B, Hkv, S]    fp32   from h2o_score_accumulate
+ *   evict_idx        [B, Hkv, S]    int32  distinct slots in [0, C), from
+ *                                          h2o_evict_select; an index outside
+ *                                          [0, C) writes nothing for its token
+ *   p0               absolute position of the chunk's first token */
+h2o_status_t kv_scatter(const h2o_shape_t* shape, uint16_t* k_cache,
+                        uint16_t* v_cache, float* scores, int64_t* pos,
+                        const uint16_t* k_new, const uint16_t* v_new,
+                        const float* new_scores, const int32_t* evict_idx,
+                        int64_t p0, void* stream);
+
+/* Diagnostics: per-kernel timing of h2o_attn_chunk with HIP events.
+ * h2o_timing_start(max_calls) creates 5 * max_calls events (call it outside
+ * any timed or captured region); until h2o_timing_stop, each h2o_attn_chunk
+ * call records an event before its first kernel and after each of its four
+ * kernels on its stream (pass 1: output and log-sum-exp; split merge; pass 2:
+ * summed-weight partials; partial reduction), for the first max_calls calls.
+ * h2o_timing_stop(ms, calls) waits for the last recorded event, writes the
+ * summed milliseconds of the four kernels to ms[0..3] and the number of timed
+ * calls to *calls, and destroys the events.  Not thread-safe; meant for one
+ * benchmarking thread. */
+h2o_status_t h2o_timing_start(int32_t max_calls);
+h2o_status_t h2o_timing_stop(double* ms, int32_t* calls);
+
+/* Static, human-readable name of a status code. */
+const char* h2o_status_string(h2o_status_t status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* H2O_H */

@@ -228,5 +228,16 @@ def steady_state(wl: Workload, layer: int = 0, step: int | None = None) -> Cache
     return st
 
 
+def partial_state(wl: Workload, n_valid: int, layer: int = 0) -> CacheState:
+    """A cache filled up to ``n_valid`` slots during the fill phase: slot j holds
+    position j, valid slots have positive scores, the rest are empty (-1)."""
+    st = steady_state(wl, layer, wl.fill_steps + 2)
+    st.n_valid = int(n_valid)
+    st.pos[...] = -1
+    st.pos[..., :n_valid] = np.arange(n_valid, dtype=np.int64)
+    st.scores[..., n_valid:] = 0.0
+    return st
+
+
 def chunk_start(wl: Workload, step: int) -> int:
     return (wl.cache_len + step) if wl.prefilled else step * wl.chunk_len

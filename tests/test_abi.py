@@ -1,0 +1,126 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+include/h2o.h declares, sizes workspaces, and rejects bad arguments on the
+host before enqueuing anything (no kernel is launched by these tests)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from h2o_kv_cache_amd import _lib
+from h2o_kv_cache_amd._lib import H2OShape
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "h2o.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return _lib.load()
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\**\s+\**\s*([A-Za-z_][A-Za-z0-9_]*)\s*\(",
+                       text, flags=re.M)
+    return sorted(set(names))
+
+
+def test_header_declares_the_boundary():
+    names = _declared_functions()
+    assert set(names) == set(_lib.EXPORTED), names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in _declared_functions():
+        assert hasattr(lib, name), name
+        assert ctypes.cast(getattr(lib, name), ctypes.c_void_p).value
+
+
+def _shape(**kw):
+    d = dict(batch=1, n_q_heads=32, n_kv_heads=8, head_dim=128, cache_len=16384,
+             chunk_len=1024, n_valid=16384, scale=0.0)
+    d.update(kw)
+    return H2OShape(**d)
+
+
+def test_status_strings(lib):
+    for st in range(5):
+        assert lib.h2o_status_string(st)
+    assert lib.h2o_status_string(99) == b"unknown status"
+
+
+def test_workspace_size_depends_on_shape_not_fill(lib):
+    a = lib.h2o_workspace_size(ctypes.byref(_shape(n_valid=0)))
+    b = lib.h2o_workspace_size(ctypes.byref(_shape(n_valid=16384)))
+    c = lib.h2o_workspace_size(ctypes.byref(_shape(n_valid=777)))
+    assert a == b == c > 0
+    assert a % 256 == 0
+
+
+@pytest.mark.parametrize("bad", [
+    dict(batch=0), dict(n_q_heads=0), dict(n_kv_heads=0), dict(n_q_heads=12, n_kv_heads=8),
+    dict(cache_len=0), dict(chunk_len=0), dict(chunk_len=20000), dict(n_valid=-1),
+    dict(n_valid=16385), dict(scale=float("nan"))])
+def test_invalid_shapes_rejected(lib, bad):
+    sh = _shape(**bad)
+    assert lib.h2o_workspace_size(ctypes.byref(sh)) == 0
+    P = ctypes.c_void_p(256)
+    st = lib.h2o_attn_chunk(ctypes.byref(sh), P, P, P, P, P, P, P, P, P, 1 << 40, None)
+    assert st == _lib.H2O_ERR_INVALID_ARG
+    assert lib.h2o_score_accumulate(ctypes.byref(sh), P, P, P, None) == _lib.H2O_ERR_INVALID_ARG
+    assert lib.h2o_evict_select(ctypes.byref(sh), P, P, None) == _lib.H2O_ERR_INVALID_ARG
+    assert lib.kv_scatter(ctypes.byref(sh), P, P, P, P, P, P, P, P, 0, None) == _lib.H2O_ERR_INVALID_ARG
+
+
+def test_unsupported_head_dim(lib):
+    sh = _shape(head_dim=96)
+    assert lib.h2o_workspace_size(ctypes.byref(sh)) == 0
+    P = ctypes.c_void_p(256)
+    assert lib.h2o_evict_select(ctypes.byref(sh), P, P, None) == _lib.H2O_ERR_UNSUPPORTED
+
+
+def test_null_shape(lib):
+    P = ctypes.c_void_p(256)
+    assert lib.h2o_workspace_size(None) == 0
+    assert lib.h2o_evict_select(None, P, P, None) == _lib.H2O_ERR_INVALID_ARG
+
+
+def test_null_and_misaligned_pointers(lib):
+    sh = _shape()
+    A = ctypes.c_void_p(4096)
+    M = ctypes.c_void_p(4098)          # not 16-byte aligned
+    N = ctypes.c_void_p(None)
+    ws = lib.h2o_workspace_size(ctypes.byref(sh))
+    # attention: each required pointer null / misaligned in turn
+    for k in range(8):
+        for bad in (N, M):
+            if k == 6 and bad is N:
+                continue  # lse may be NULL
+            args = [A] * 8
+            args[k] = bad
+            st = lib.h2o_attn_chunk(ctypes.byref(sh), *args, A, ws, None)
+            assert st == _lib.H2O_ERR_INVALID_ARG, (k, bad)
+    assert lib.h2o_score_accumulate(ctypes.byref(sh), A, N, A, None) == _lib.H2O_ERR_INVALID_ARG
+    assert lib.h2o_score_accumulate(ctypes.byref(sh), A, A, M, None) == _lib.H2O_ERR_INVALID_ARG
+    assert lib.h2o_evict_select(ctypes.byref(sh), N, A, None) == _lib.H2O_ERR_INVALID_ARG
+    assert lib.h2o_evict_select(ctypes.byref(sh), A, M, None) == _lib.H2O_ERR_INVALID_ARG
+    for k in range(8):
+        for bad in (N, M):
+            if k == 3 and bad is N:
+                continue  # pos may be NULL
+            args = [A] * 8
+            args[k] = bad
+            assert lib.kv_scatter(ctypes.byref(sh), *args, 0, None) == _lib.H2O_ERR_INVALID_ARG
+    assert lib.kv_scatter(ctypes.byref(sh), *([A] * 8), -1, None) == _lib.H2O_ERR_INVALID_ARG
+
+
+def test_workspace_checks(lib):
+    sh = _shape()
+    A = ctypes.c_void_p(4096)
+    need = lib.h2o_workspace_size(ctypes.byref(sh))
+    assert lib.h2o_attn_chunk(ctypes.byref(sh), *([A] * 8), None, need, None) == _lib.H2O_ERR_WORKSPACE
+    assert lib.h2o_attn_chunk(ctypes.byref(sh), *([A] * 8), A, need - 1, None) == _lib.H2O_ERR_WORKSPACE
+    assert lib.h2o_attn_chunk(ctypes.byref(sh), *([A] * 8), ctypes.c_void_p(4096 + 16), need,
+                              None) == _lib.H2O_ERR_WORKSPACE
