@@ -39,8 +39,8 @@ namespace h2o {
 namespace {
 
 constexpr int KT = kKeyTile;
-constexpr int KPAD = 8;   // bf16 pad per K row in LDS (bank spread)
-constexpr int VPAD = 8;   // bf16 pad per V^T row in LDS
+constexpr int RB = kRowBlocks;
+constexpr int NT = kWaves * 64;   // threads per workgroup
 
 // Key tiles seen by one row tile: cache tiles [0, n_ct), then the chunk tiles
 // up to the last query of the row tile (causal).
@@ -57,45 +57,188 @@ __device__ __forceinline__ TileRange tile_range(const AttnGeom& g, int qt) {
     return t;
 }
 
-// Cooperative copy of a KT x D bf16 key tile into LDS (rows >= lim -> 0).
+// Workgroups are dispatched round-robin over the 8 XCDs (linear id L runs on
+// XCD L % 8).  Re-index so that each XCD receives one contiguous run of the
+// (bh, split, qt) work list: the row tiles that read the same K/V tiles then
+// share one XCD's L2.
+__device__ __forceinline__ void decode_block(int n_qt, int nsplit, int& qt, int& bh,
+                                             int& split) {
+    const int L = blockIdx.x, N = gridDim.x;
+    const int q8 = N >> 3, r8 = N & 7, x = L & 7, j = L >> 3;
+    const int lam = x * q8 + min(x, r8) + j;
+    qt = lam % n_qt;
+    const int rest = lam / n_qt;
+    split = rest % nsplit;
+    bh = rest / nsplit;
+}
+
+// LDS tiles are KT x D bf16, row-major, with the 16-byte chunks of row `key`
+// XOR-swizzled by (key mod chunks-per-row) so that the MFMA operand reads of
+// 32 consecutive rows hit distinct banks.  Element offset of (key, chunk):
 template <int D>
-__device__ __forceinline__ void load_k_tile(uint16_t (*Ks)[D + KPAD],
-                                            const uint16_t* __restrict__ base,
-                                            int key0, int lim, int tid) {
-    constexpr int CPR = D / 8;  // 16-byte chunks per row
+__device__ __forceinline__ int tile_off(int key, int chunk) {
+    constexpr int CPR = D / 8;
+    return key * D + ((chunk ^ (key & (CPR - 1))) << 3);
+}
+
+// Issue the HBM -> LDS copy of one KT x D tile with global_load_lds_dwordx4:
+// each wave instruction fills 1 KiB of LDS (lane l -> bytes 16*l), and each
+// lane fetches the global chunk that belongs at its LDS slot.  Rows past
+// `lim` re-read row lim-1, a valid row whose weight is masked to zero.  The
+// copy is asynchronous: wait_tiles() + a barrier publish it.
+template <int D>
+__device__ __forceinline__ void issue_tile(uint16_t* tile, const uint16_t* __restrict__ src,
+                                           int key0, int lim, int wave, int lane) {
+    constexpr int CPR = D / 8;
+    constexpr int ITER = KT * CPR / NT;
 #pragma unroll
-    for (int c = tid; c < KT * CPR; c += kWaves * 64) {
-        const int kr = c / CPR, dc = c % CPR;
-        const int key = key0 + kr;
-        u32x4 v = {0u, 0u, 0u, 0u};
-        if (key < lim) v = *(const u32x4*)(base + (size_t)key * D + dc * 8);
-        *(u32x4*)&Ks[kr][dc * 8] = v;
+    for (int it = 0; it < ITER; ++it) {
+        const int blk = it * kWaves + wave;          // 1 KiB block of the tile
+        const int p = blk * 64 + lane;               // LDS chunk slot
+        const int key = p / CPR;
+        const int chunk = (p % CPR) ^ (key & (CPR - 1));
+        const int gkey = min(key0 + key, lim - 1);
+        __builtin_amdgcn_global_load_lds(
+            (const void*)(src + (size_t)gkey * D + chunk * 8),
+            (__attribute__((address_space(3))) void*)(tile + blk * 64 * 8), 16, 0, 0);
     }
 }
 
-// Cooperative transposed copy of a KT x D bf16 value tile: Vt[d][key].
-// Each unit moves 4 keys x 8 dims with 4 16-byte loads and 8 8-byte stores.
+__device__ __forceinline__ void wait_tiles() { __builtin_amdgcn_s_waitcnt(0); }
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+
+// Transposed read of 4 keys x 1 dim per lane from a row-major V tile.  In each
+// 16-lane group, input lane j reads dims 4*(j%4)..+3 of key kbase + j/4; the
+// hardware hands output lane i dim dbase + i of keys kbase..kbase+3.
 template <int D>
-__device__ __forceinline__ void load_vt_tile(uint16_t (*Vt)[KT + VPAD],
-                                             const uint16_t* __restrict__ base,
-                                             int key0, int lim, int tid) {
-    constexpr int UNITS = (KT / 4) * (D / 8);
+__device__ __forceinline__ u32x2 read_vt4(const uint16_t* tile, int kbase, int dbase, int j) {
+    const int key = kbase + (j >> 2);
+    const int d = dbase + 4 * (j & 3);
+    const uint16_t* a = tile + tile_off<D>(key, d >> 3) + (d & 7);
+    const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) i16x4*)a);
+    return __builtin_bit_cast(u32x2, v);
+}
+
+// Q fragments of this lane: row rbase + rb*32 + l32, dims 16*ks + 8*half + [0, 8).
+// Serve as the B operand of S^T = K Q^T and the A operand of S = Q K^T.
+template <int D>
+__device__ __forceinline__ void load_q(bf16x8 (&qf)[RB][D / 16], const uint16_t* __restrict__ q,
+                                       const AttnGeom& g, int b, int h, int rbase, int l32,
+                                       int half) {
 #pragma unroll
-    for (int u = tid; u < UNITS; u += kWaves * 64) {
-        const int kg = u % (KT / 4), dg = u / (KT / 4);
-        u32x4 r[4];
+    for (int rb = 0; rb < RB; ++rb) {
+        const int r = rbase + rb * 32 + l32;
+        const bool ok = r < g.R;
+        const uint16_t* qrow =
+            q + (((size_t)b * g.Hq + (size_t)h * g.G + (r % g.G)) * g.S + r / g.G) * D;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int key = key0 + 4 * kg + e;
-            r[e] = (key < lim) ? *(const u32x4*)(base + (size_t)key * D + dg * 8)
-                               : u32x4{0u, 0u, 0u, 0u};
+        for (int ks = 0; ks < D / 16; ++ks) {
+            u32x4 v = {0u, 0u, 0u, 0u};
+            if (ok) v = *(const u32x4*)(qrow + ks * 16 + half * 8);
+            qf[rb][ks] = as_bf16x8(v);
         }
+    }
+}
+
+// One KT-key tile of pass 1 for one wave, a 32-key block at a time:
+// S^T = K Q^T, online softmax in base 2, O^T += V^T P^T.  MASKED handles the
+// last partial cache tile and the causal chunk tiles.
+template <int D>
+__device__ __forceinline__ void fwd_tile(const uint16_t* Ks, const uint16_t* Vs,
+                                         const bf16x8 (&qf)[RB][D / 16],
+                                         f32x16 (&o_acc)[RB][D / 32], float (&m_ref)[RB],
+                                         float (&l_acc)[RB], float c, bool masked, int key0,
+                                         int lim, bool chunk, int G, int rbase, int lane) {
+    const int l32 = lane & 31, half = lane >> 5;
 #pragma unroll
-        for (int w = 0; w < 4; ++w) {   // dword w holds dims 2w, 2w+1
-            u32x2 even = {pack_lo(r[0][w], r[1][w]), pack_lo(r[2][w], r[3][w])};
-            u32x2 odd = {pack_hi(r[0][w], r[1][w]), pack_hi(r[2][w], r[3][w])};
-            *(u32x2*)&Vt[dg * 8 + 2 * w][4 * kg] = even;
-            *(u32x2*)&Vt[dg * 8 + 2 * w + 1][4 * kg] = odd;
+    for (int kb = 0; kb < KT / 32; ++kb) {
+        f32x16 s[RB];
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) s[rb][v] = 0.f;
+#pragma unroll
+        for (int ks = 0; ks < D / 16; ++ks) {
+            const bf16x8 kf =
+                as_bf16x8(*(const u32x4*)(Ks + tile_off<D>(kb * 32 + l32, 2 * ks + half)));
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb) s[rb] = mfma32x32x16(kf, qf[rb][ks], s[rb]);
+        }
+
+        // mask (uniform branch: last partial cache tile, chunk tiles), then
+        // row max over raw logits (c > 0)
+        if (masked) {
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb) {
+                const int r = rbase + rb * 32 + l32;
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    const int key = key0 + kb * 32 + acc_row(v, half);
+                    const bool ok = key < lim && (!chunk || key * G <= r);
+                    s[rb][v] = ok ? s[rb][v] : -INFINITY;
+                }
+            }
+        }
+        float mt[RB];
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+            float mx = s[rb][0];
+#pragma unroll
+            for (int v = 1; v < 16; ++v) mx = fmaxf(mx, s[rb][v]);
+            mx = fmaxf(mx, xor32(mx));
+            mt[rb] = mx * c;
+        }
+
+        // move the reference max only when it grows by more than 2^8, so
+        // P = 2^(u - m_ref) stays <= 256 and rescaling is rare
+        bool need = false;
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) need |= mt[rb] > m_ref[rb] + 8.f;
+        if (__any(need)) {
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb) {
+                const float m_new = fmaxf(m_ref[rb], mt[rb]);
+                const float m_safe = (m_new == -INFINITY) ? 0.f : m_new;
+                const float alpha = fast_exp2(m_ref[rb] - m_safe);
+                l_acc[rb] *= alpha;
+#pragma unroll
+                for (int db = 0; db < D / 32; ++db) o_acc[rb][db] *= alpha;
+                m_ref[rb] = m_new;
+            }
+        }
+
+        // P = 2^(s*c - m), row sums, P^T fragments in bf16: element v of the
+        // accumulator is key 8*(v/4) + 4*half + v%4 of the block, i.e. entry
+        // v%8 of k-step v/8
+        bf16x8 pf[2][RB];
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+            const float m_use = (m_ref[rb] == -INFINITY) ? 0.f : m_ref[rb];
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const float p = fast_exp2(fmaf(s[rb][v], c, -m_use));
+                l_acc[rb] += p;
+                pf[v >> 3][rb][v & 7] = (__bf16)p;
+            }
+        }
+
+        // k-step hs covers keys kb*32 + 16*hs + [0, 16) in the order lane-half
+        // h supplies them: 8*gg + 4*h + e
+#pragma unroll
+        for (int hs = 0; hs < 2; ++hs) {
+            const int kcol = kb * 32 + 16 * hs + 4 * half;
+#pragma unroll
+            for (int db = 0; db < D / 32; ++db) {
+                const int dbase = db * 32 + (lane & 16);
+                const u32x2 lo = read_vt4<D>(Vs, kcol, dbase, lane & 15);
+                const u32x2 hi = read_vt4<D>(Vs, kcol + 8, dbase, lane & 15);
+                const bf16x8 vf = as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]});
+#pragma unroll
+                for (int rb = 0; rb < RB; ++rb)
+                    o_acc[rb][db] = mfma32x32x16(vf, pf[hs][rb], o_acc[rb][db]);
+            }
         }
     }
 }
@@ -104,152 +247,88 @@ __device__ __forceinline__ void load_vt_tile(uint16_t (*Vt)[KT + VPAD],
 // pass 1: partial (O, m, l) per key split
 // ---------------------------------------------------------------------------
 template <int D>
-__global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
+__global__ __launch_bounds__(NT, 1) void attn_fwd_kernel(
     const AttnGeom g, const int nsplit, const uint16_t* __restrict__ q,
     const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc,
     const uint16_t* __restrict__ kn, const uint16_t* __restrict__ vn,
     float* __restrict__ o_part, float* __restrict__ ml_part) {
-    __shared__ __attribute__((aligned(16))) uint16_t Ks[KT][D + KPAD];
-    __shared__ __attribute__((aligned(16))) uint16_t Vt[D][KT + VPAD];
+    __shared__ __attribute__((aligned(16))) uint16_t Ks[2][KT * D];
+    __shared__ __attribute__((aligned(16))) uint16_t Vs[2][KT * D];
 
-    const int qt = blockIdx.x, bh = blockIdx.y, split = blockIdx.z;
+    int qt, bh, split;
+    decode_block(g.n_qt, nsplit, qt, bh, split);
     const int BH = g.B * g.Hkv;
     const int b = bh / g.Hkv, h = bh % g.Hkv;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int half = lane >> 5, l32 = lane & 31;
+    const int rbase = qt * kRowsPerBlock + wave * kRowsPerWave;
+    // row blocks of this wave that hold any real row (uniform per wave)
+    const int live = min(RB, max(0, (g.R - rbase + 31) / 32));
 
-    // this lane's query row (column of S^T)
-    const int r = qt * kRowsPerBlock + wave * kRowsPerWave + l32;
-    const bool row_ok = r < g.R;
-    const int qi = r / g.G;
-    bf16x8 qf[D / 16];
-    {
-        const uint16_t* qrow =
-            q + (((size_t)b * g.Hq + (size_t)h * g.G + (r % g.G)) * g.S + qi) * D;
-#pragma unroll
-        for (int ks = 0; ks < D / 16; ++ks) {
-            u32x4 v = {0u, 0u, 0u, 0u};
-            if (row_ok) v = *(const u32x4*)(qrow + ks * 16 + half * 8);
-            qf[ks] = as_bf16x8(v);
-        }
-    }
+    bf16x8 qf[RB][D / 16];
+    load_q<D>(qf, q, g, b, h, rbase, l32, half);
 
     const TileRange tr = tile_range(g, qt);
     const int t_begin = (int)((long)split * tr.total / nsplit);
     const int t_end = (int)((long)(split + 1) * tr.total / nsplit);
-
     const uint16_t* kc_bh = kc + (size_t)bh * g.C * D;
     const uint16_t* vc_bh = vc + (size_t)bh * g.C * D;
     const uint16_t* kn_bh = kn + (size_t)bh * g.S * D;
     const uint16_t* vn_bh = vn + (size_t)bh * g.S * D;
 
-    float m_ref = -INFINITY;   // reference max (base 2), shared by both halves
-    float l_acc = 0.f;         // this lane's partial row sum
-    f32x16 o_acc[D / 32];
+    float m_ref[RB], l_acc[RB];
+    f32x16 o_acc[RB][D / 32];
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db)
+    for (int rb = 0; rb < RB; ++rb) {
+        m_ref[rb] = -INFINITY;
+        l_acc[rb] = 0.f;
 #pragma unroll
-        for (int v = 0; v < 16; ++v) o_acc[db][v] = 0.f;
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) o_acc[rb][db][v] = 0.f;
+    }
 
-    for (int t = t_begin; t < t_end; ++t) {
+    auto issue = [&](int t, int buf) {
         const bool chunk = t >= tr.n_ct;
         const int key0 = chunk ? (t - tr.n_ct) * KT : t * KT;
         const int lim = chunk ? g.S : g.n;
+        issue_tile<D>(Ks[buf], chunk ? kn_bh : kc_bh, key0, lim, wave, lane);
+        issue_tile<D>(Vs[buf], chunk ? vn_bh : vc_bh, key0, lim, wave, lane);
+    };
+    if (t_begin < t_end) issue(t_begin, 0);
+    wait_tiles();
+    __syncthreads();
+
+    for (int t = t_begin; t < t_end; ++t) {
+        const int buf = (t - t_begin) & 1;
+        const bool chunk = t >= tr.n_ct;
+        const int key0 = chunk ? (t - tr.n_ct) * KT : t * KT;
+        const int lim = chunk ? g.S : g.n;
+        if (t + 1 < t_end) issue(t + 1, buf ^ 1);   // next tile lands while this one is used
+        if (live > 0)
+            fwd_tile<D>(Ks[buf], Vs[buf], qf, o_acc, m_ref, l_acc, g.c,
+                        chunk || key0 + KT > g.n, key0, lim, chunk, g.G, rbase, lane);
+        wait_tiles();
         __syncthreads();
-        load_k_tile<D>(Ks, chunk ? kn_bh : kc_bh, key0, lim, tid);
-        load_vt_tile<D>(Vt, chunk ? vn_bh : vc_bh, key0, lim, tid);
-        __syncthreads();
-
-        // S^T block: 32 keys x 32 rows per key block
-        f32x16 s[KT / 32];
-#pragma unroll
-        for (int kb = 0; kb < KT / 32; ++kb) {
-#pragma unroll
-            for (int v = 0; v < 16; ++v) s[kb][v] = 0.f;
-#pragma unroll
-            for (int ks = 0; ks < D / 16; ++ks) {
-                const bf16x8 kf =
-                    as_bf16x8(*(const u32x4*)&Ks[kb * 32 + l32][ks * 16 + half * 8]);
-                s[kb] = mfma32x32x16(kf, qf[ks], s[kb]);
-            }
-        }
-
-        // scale, mask, tile max
-        const bool full = !chunk && (key0 + KT <= g.n);
-        float mt = -INFINITY;
-#pragma unroll
-        for (int kb = 0; kb < KT / 32; ++kb)
-#pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const int key = key0 + kb * 32 + acc_row(v, half);
-                const bool ok = full || (key < lim && (!chunk || key <= qi));
-                const float u = ok ? s[kb][v] * g.c : -INFINITY;
-                s[kb][v] = u;
-                mt = fmaxf(mt, u);
-            }
-        mt = fmaxf(mt, xor32(mt));
-
-        // move the reference max only when it grows by more than 2^8, so
-        // P = 2^(u - m_ref) stays <= 256 and rescaling is rare
-        if (__any(mt > m_ref + 8.f)) {
-            const float m_new = fmaxf(m_ref, mt);
-            const float m_safe = (m_new == -INFINITY) ? 0.f : m_new;
-            const float alpha = fast_exp2(m_ref - m_safe);
-            l_acc *= alpha;
-#pragma unroll
-            for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-                for (int v = 0; v < 16; ++v) o_acc[db][v] *= alpha;
-            m_ref = m_new;
-        }
-        const float m_use = (m_ref == -INFINITY) ? 0.f : m_ref;
-
-#pragma unroll
-        for (int kb = 0; kb < KT / 32; ++kb)
-#pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const float p = fast_exp2(s[kb][v] - m_use);
-                l_acc += p;
-                s[kb][v] = p;
-            }
-
-        // O^T += V^T P^T; k-step (kb, hs) covers keys kb*32 + 16*hs + [0, 16)
-        // in the order lane-half h supplies: 8*gg + 4*h + e, gg, e in 0..1, 0..3
-#pragma unroll
-        for (int kb = 0; kb < KT / 32; ++kb)
-#pragma unroll
-            for (int hs = 0; hs < 2; ++hs) {
-                bf16x8 pf;
-#pragma unroll
-                for (int gg = 0; gg < 2; ++gg)
-#pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        pf[4 * gg + e] = (__bf16)s[kb][4 * (2 * hs + gg) + e];
-                const int kcol = kb * 32 + 16 * hs + 4 * half;
-#pragma unroll
-                for (int db = 0; db < D / 32; ++db) {
-                    const u32x2 lo = *(const u32x2*)&Vt[db * 32 + l32][kcol];
-                    const u32x2 hi = *(const u32x2*)&Vt[db * 32 + l32][kcol + 8];
-                    const u32x4 vv = {lo[0], lo[1], hi[0], hi[1]};
-                    o_acc[db] = mfma32x32x16(as_bf16x8(vv), pf, o_acc[db]);
-                }
-            }
     }
 
-    l_acc += xor32(l_acc);
-    if (row_ok) {
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+        const float l = l_acc[rb] + xor32(l_acc[rb]);
+        const int r = rbase + rb * 32 + l32;
+        if (r >= g.R) continue;
         const size_t prow = ((size_t)split * BH + bh) * g.rows_pad + r;
         if (half == 0) {
-            ml_part[prow * 2 + 0] = m_ref;
-            ml_part[prow * 2 + 1] = l_acc;
+            ml_part[prow * 2 + 0] = m_ref[rb];
+            ml_part[prow * 2 + 1] = l;
         }
         float* orow = o_part + prow * D;
 #pragma unroll
         for (int db = 0; db < D / 32; ++db)
 #pragma unroll
             for (int gq = 0; gq < 4; ++gq) {
-                const f32x4 v4 = {o_acc[db][4 * gq + 0], o_acc[db][4 * gq + 1],
-                                  o_acc[db][4 * gq + 2], o_acc[db][4 * gq + 3]};
+                const f32x4 v4 = {o_acc[rb][db][4 * gq + 0], o_acc[rb][db][4 * gq + 1],
+                                  o_acc[rb][db][4 * gq + 2], o_acc[rb][db][4 * gq + 3]};
                 *(f32x4*)(orow + db * 32 + 8 * gq + 4 * half) = v4;
             }
     }
@@ -300,47 +379,79 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(
     }
 }
 
+// One KT-key tile of pass 2 for one wave: S = Q K^T per 32-key block, then
+// the column sums of P = 2^(S*c - L2) over this wave's rows into colp.
+// MASKED handles the last partial cache tile (G == 0) and chunk tiles (G > 0:
+// row r sees chunk key t iff t*G <= r).
+template <int D, bool MASKED>
+__device__ __forceinline__ void colsum_tile(const uint16_t* Ks, float* colp,
+                                            const bf16x8 (&qf)[RB][D / 16],
+                                            const float (&l2v)[RB][16], float c, int key0,
+                                            int lim, int G, int rbase, int l32, int half) {
+#pragma unroll
+    for (int kb = 0; kb < KT / 32; ++kb) {
+        f32x16 s[RB];
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) s[rb][v] = 0.f;
+#pragma unroll
+        for (int ks = 0; ks < D / 16; ++ks) {
+            const bf16x8 kf =
+                as_bf16x8(*(const u32x4*)(Ks + tile_off<D>(kb * 32 + l32, 2 * ks + half)));
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb) s[rb] = mfma32x32x16(qf[rb][ks], kf, s[rb]);
+        }
+        float col = 0.f;
+        const int key = key0 + kb * 32 + l32;
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const float p = fast_exp2(fmaf(s[rb][v], c, -l2v[rb][v]));
+                if (MASKED) {
+                    const int r = rbase + rb * 32 + acc_row(v, half);
+                    col += (key < lim && key * G <= r) ? p : 0.f;
+                } else {
+                    col += p;
+                }
+            }
+        col += xor32(col);
+        if (half == 0) colp[kb * 32 + l32] = col;
+    }
+}
+
 // ---------------------------------------------------------------------------
 // pass 2: column sums of P per row tile
 // ---------------------------------------------------------------------------
 template <int D>
-__global__ __launch_bounds__(256, 2) void attn_colsum_kernel(
+__global__ __launch_bounds__(NT, 2) void attn_colsum_kernel(
     const AttnGeom g, const int nsplit, const uint16_t* __restrict__ q,
     const uint16_t* __restrict__ kc, const uint16_t* __restrict__ kn,
     const float* __restrict__ l2, float* __restrict__ wpart) {
-    __shared__ __attribute__((aligned(16))) uint16_t Ks[KT][D + KPAD];
-    __shared__ float colp[kWaves][KT];
+    __shared__ __attribute__((aligned(16))) uint16_t Ks[2][KT * D];
+    __shared__ float colp[2][kWaves][KT];
 
-    const int qt = blockIdx.x, bh = blockIdx.y, split = blockIdx.z;
+    int qt, bh, split;
+    decode_block(g.n_qt, nsplit, qt, bh, split);
     const int BH = g.B * g.Hkv;
     const int b = bh / g.Hkv, h = bh % g.Hkv;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int half = lane >> 5, l32 = lane & 31;
     const int W = g.C + g.S;
-
     const int rbase = qt * kRowsPerBlock + wave * kRowsPerWave;
-    bf16x8 qf[D / 16];
-    {
-        const int r = rbase + l32;
-        const bool row_ok = r < g.R;
-        const uint16_t* qrow =
-            q + (((size_t)b * g.Hq + (size_t)h * g.G + (r % g.G)) * g.S + r / g.G) * D;
+    const int live = min(RB, max(0, (g.R - rbase + 31) / 32));
+
+    bf16x8 qf[RB][D / 16];
+    load_q<D>(qf, q, g, b, h, rbase, l32, half);
+    // base-2 LSE of the rows this lane holds in the S accumulators
+    // (padding rows carry +inf, so their weights are 0)
+    float l2v[RB][16];
 #pragma unroll
-        for (int ks = 0; ks < D / 16; ++ks) {
-            u32x4 v = {0u, 0u, 0u, 0u};
-            if (row_ok) v = *(const u32x4*)(qrow + ks * 16 + half * 8);
-            qf[ks] = as_bf16x8(v);
-        }
-    }
-    // rows held by this lane in the S accumulator, their base-2 LSE and query
-    float l2v[16];
-    int qiv[16];
+    for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-        const int rr = rbase + acc_row(v, half);
-        l2v[v] = l2[(size_t)bh * g.rows_pad + rr];
-        qiv[v] = rr / g.G;
-    }
+        for (int v = 0; v < 16; ++v)
+            l2v[rb][v] = l2[(size_t)bh * g.rows_pad + rbase + rb * 32 + acc_row(v, half)];
 
     const TileRange tr = tile_range(g, qt);
     const int t_begin = (int)((long)split * tr.total / nsplit);
@@ -349,52 +460,51 @@ __global__ __launch_bounds__(256, 2) void attn_colsum_kernel(
     const uint16_t* kn_bh = kn + (size_t)bh * g.S * D;
     float* wrow = wpart + ((size_t)qt * BH + bh) * W;
 
-    for (int t = t_begin; t < t_end; ++t) {
-        const bool chunk = t >= tr.n_ct;
-        const int key0 = chunk ? (t - tr.n_ct) * KT : t * KT;
-        const int lim = chunk ? g.S : g.n;
-        __syncthreads();
-        load_k_tile<D>(Ks, chunk ? kn_bh : kc_bh, key0, lim, tid);
-        __syncthreads();
-
-#pragma unroll
-        for (int kb = 0; kb < KT / 32; ++kb) {
-            f32x16 s;
-#pragma unroll
-            for (int v = 0; v < 16; ++v) s[v] = 0.f;
-#pragma unroll
-            for (int ks = 0; ks < D / 16; ++ks) {
-                const bf16x8 kf =
-                    as_bf16x8(*(const u32x4*)&Ks[kb * 32 + l32][ks * 16 + half * 8]);
-                s = mfma32x32x16(qf[ks], kf, s);
-            }
-            const int key = key0 + kb * 32 + l32;
-            float col = 0.f;
-            if (!chunk) {
-#pragma unroll
-                for (int v = 0; v < 16; ++v) col += fast_exp2(s[v] * g.c - l2v[v]);
-                col = (key < lim) ? col : 0.f;
-            } else {
-#pragma unroll
-                for (int v = 0; v < 16; ++v) {
-                    const float p = fast_exp2(s[v] * g.c - l2v[v]);
-                    col += (key < lim && key <= qiv[v]) ? p : 0.f;
-                }
-            }
-            col += xor32(col);
-            if (half == 0) colp[wave][kb * 32 + l32] = col;
-        }
-        __syncthreads();
+    // column sums of tile t are written to wpart after the barrier that ends it
+    auto flush = [&](int t, int buf) {
         if (tid < KT) {
-            const int key = key0 + tid;
-            if (key < lim) {
-                float tot = colp[0][tid];
+            const bool chunk = t >= tr.n_ct;
+            const int key = (chunk ? (t - tr.n_ct) * KT : t * KT) + tid;
+            if (key < (chunk ? g.S : g.n)) {
+                float tot = colp[buf][0][tid];
 #pragma unroll
-                for (int w = 1; w < kWaves; ++w) tot += colp[w][tid];
+                for (int w = 1; w < kWaves; ++w) tot += colp[buf][w][tid];
                 wrow[chunk ? g.C + key : key] = tot;
             }
         }
+    };
+    auto issue = [&](int t, int buf) {
+        const bool chunk = t >= tr.n_ct;
+        const int key0 = chunk ? (t - tr.n_ct) * KT : t * KT;
+        issue_tile<D>(Ks[buf], chunk ? kn_bh : kc_bh, key0, chunk ? g.S : g.n, wave, lane);
+    };
+    if (t_begin < t_end) issue(t_begin, 0);
+    wait_tiles();
+    __syncthreads();
+
+    for (int t = t_begin; t < t_end; ++t) {
+        const int buf = (t - t_begin) & 1;
+        const bool chunk = t >= tr.n_ct;
+        const int key0 = chunk ? (t - tr.n_ct) * KT : t * KT;
+        const int lim = chunk ? g.S : g.n;
+        if (t + 1 < t_end) issue(t + 1, buf ^ 1);
+        if (t > t_begin) flush(t - 1, buf ^ 1);
+        if (live == 0) {
+            if (half == 0) {
+                colp[buf][wave][l32] = 0.f;
+                colp[buf][wave][32 + l32] = 0.f;
+            }
+        } else if (!chunk && key0 + KT <= g.n) {
+            colsum_tile<D, false>(Ks[buf], colp[buf][wave], qf, l2v, g.c, 0, 0, 0, rbase, l32,
+                                  half);
+        } else {
+            colsum_tile<D, true>(Ks[buf], colp[buf][wave], qf, l2v, g.c, key0, lim,
+                                 chunk ? g.G : 0, rbase, l32, half);
+        }
+        wait_tiles();
+        __syncthreads();
     }
+    if (t_begin < t_end) flush(t_end - 1, (t_end - 1 - t_begin) & 1);
 }
 
 // ---------------------------------------------------------------------------
@@ -421,8 +531,7 @@ __global__ __launch_bounds__(256) void wsum_reduce_kernel(
     wsum[idx] = s;
 }
 
-int pick_split(int base_blocks, int max_tiles) {
-    const int target = 2 * 256;   // two workgroups per CU on 256 CUs
+int pick_split(int base_blocks, int max_tiles, int target) {
     int want = (target + base_blocks - 1) / base_blocks;
     int cap = max_tiles / 4;
     if (cap < 1) cap = 1;
@@ -455,7 +564,7 @@ hipError_t launch_attention_d(const AttnPlan& pl, const uint16_t* q,
     } while (0)
 
     if (ev) hipEventRecord(ev[0], stream);
-    hipLaunchKernelGGL(attn_fwd_kernel<D>, dim3(g.n_qt, BH, pl.split1), dim3(256), 0,
+    hipLaunchKernelGGL(attn_fwd_kernel<D>, dim3(g.n_qt * BH * pl.split1), dim3(NT), 0,
                        stream, g, pl.split1, q, kc, vc, kn, vn, o_part, ml_part);
     H2O_CHECK();
     if (ev) hipEventRecord(ev[1], stream);
@@ -467,7 +576,7 @@ hipError_t launch_attention_d(const AttnPlan& pl, const uint16_t* q,
         H2O_CHECK();
     }
     if (ev) hipEventRecord(ev[2], stream);
-    hipLaunchKernelGGL(attn_colsum_kernel<D>, dim3(g.n_qt, BH, pl.split2), dim3(256), 0,
+    hipLaunchKernelGGL(attn_colsum_kernel<D>, dim3(g.n_qt * BH * pl.split2), dim3(NT), 0,
                        stream, g, pl.split2, q, kc, kn, l2, wpart);
     H2O_CHECK();
     if (ev) hipEventRecord(ev[3], stream);
@@ -496,8 +605,9 @@ bool make_attn_plan(int B, int Hq, int Hkv, int D, int C, int S, int n, float sc
     g.c = tau * kLog2e;
     const int BH = B * Hkv;
     const int max_tiles = (C + KT - 1) / KT + (S + KT - 1) / KT;
-    pl->split1 = pick_split(g.n_qt * BH, max_tiles);
-    pl->split2 = pick_split(g.n_qt * BH, max_tiles);
+    // pass 1 holds one workgroup per CU, pass 2 two (register budgets)
+    pl->split1 = pick_split(g.n_qt * BH, max_tiles, 256);
+    pl->split2 = pick_split(g.n_qt * BH, max_tiles, 512);
     auto align = [](size_t x) { return (x + 255) & ~(size_t)255; };
     size_t off = 0;
     pl->off_o = off;

@@ -9,7 +9,8 @@ namespace h2o {
 
 // Tiling shared by the attention kernels.
 constexpr int kKeyTile = 64;        // keys per LDS tile
-constexpr int kRowsPerWave = 32;    // query rows (head, query) per wave
+constexpr int kRowBlocks = 2;       // 32-row MFMA blocks per wave
+constexpr int kRowsPerWave = 32 * kRowBlocks;   // query rows (head, query) per wave
 constexpr int kWaves = 4;           // waves per workgroup
 constexpr int kRowsPerBlock = kRowsPerWave * kWaves;
 
