@@ -72,38 +72,66 @@ __device__ __forceinline__ void decode_block(int n_qt, int nsplit, int& qt, int&
     bh = rest / nsplit;
 }
 
-// LDS tiles are KT x D bf16, row-major, with the 16-byte chunks of row `key`
-// XOR-swizzled by (key mod chunks-per-row) so that the MFMA operand reads of
-// 32 consecutive rows hit distinct banks.  Element offset of (key, chunk):
-template <int D>
-__device__ __forceinline__ int tile_off(int key, int chunk) {
+// LDS tiles are KT x D bf16, row-major, with the 16-byte chunks of each row
+// XOR-swizzled so that the MFMA operand reads hit distinct banks:
+//   K tiles (ds_read_b128 of one chunk from 16 consecutive rows):
+//       chunk ^ (key mod 16)
+//   V tiles (ds_read_b64_tr_b16: an aligned pair of chunks from 4 consecutive
+//       rows per 16-lane group): chunk ^ 2*(key mod 8), which keeps pairs
+//       together and gives the 4 rows distinct pairs.
+template <int D, bool VT>
+__device__ __forceinline__ int tile_swz(int key) {
     constexpr int CPR = D / 8;
-    return key * D + ((chunk ^ (key & (CPR - 1))) << 3);
+    return VT ? 2 * (key & (CPR / 2 - 1)) : (key & (CPR - 1));
 }
 
-// Issue the HBM -> LDS copy of one KT x D tile with global_load_lds_dwordx4:
-// each wave instruction fills 1 KiB of LDS (lane l -> bytes 16*l), and each
-// lane fetches the global chunk that belongs at its LDS slot.  Rows past
-// `lim` re-read row lim-1, a valid row whose weight is masked to zero.  The
-// copy is asynchronous: wait_tiles() + a barrier publish it.
-template <int D>
+// Element offset of (key, 16-byte chunk) in a K (VT = false) or V tile.
+template <int D, bool VT>
+__device__ __forceinline__ int tile_off(int key, int chunk) {
+    return key * D + ((chunk ^ tile_swz<D, VT>(key)) << 3);
+}
+
+// One 16-byte HBM -> LDS copy per lane (global_load_lds_dwordx4): lane l
+// writes bytes [16*l, 16*l + 16) past the wave-uniform LDS address `lds`.
+// Written as inline asm on purpose: the compiler then keeps no record of the
+// asynchronous LDS write, so it does not stall reads of the *other* tile
+// buffer behind it (it would otherwise wait for every outstanding load before
+// each transposed LDS read).  The asm has no register outputs; completion is
+// awaited explicitly with wait_tiles() before the barrier that publishes the
+// tile, and before the workgroup exits.
+__device__ __forceinline__ void dma16(const uint16_t* gptr, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
+                 :
+                 : "s"(lds), "v"(gptr)
+                 : "memory", "m0");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// Issue the HBM -> LDS copy of one KT x D tile: each wave instruction fills
+// 1 KiB of LDS, and each lane fetches the global chunk that belongs at its
+// LDS slot.  Rows past `lim` re-read row lim-1, a valid row whose weight is
+// masked to zero.
+template <int D, bool VT>
 __device__ __forceinline__ void issue_tile(uint16_t* tile, const uint16_t* __restrict__ src,
                                            int key0, int lim, int wave, int lane) {
     constexpr int CPR = D / 8;
     constexpr int ITER = KT * CPR / NT;
+    const uint32_t base = __builtin_amdgcn_readfirstlane(lds_addr(tile));
 #pragma unroll
     for (int it = 0; it < ITER; ++it) {
         const int blk = it * kWaves + wave;          // 1 KiB block of the tile
         const int p = blk * 64 + lane;               // LDS chunk slot
         const int key = p / CPR;
-        const int chunk = (p % CPR) ^ (key & (CPR - 1));
+        const int chunk = (p % CPR) ^ tile_swz<D, VT>(key);
         const int gkey = min(key0 + key, lim - 1);
-        __builtin_amdgcn_global_load_lds(
-            (const void*)(src + (size_t)gkey * D + chunk * 8),
-            (__attribute__((address_space(3))) void*)(tile + blk * 64 * 8), 16, 0, 0);
+        dma16(src + (size_t)gkey * D + chunk * 8, base + blk * 1024);
     }
 }
 
+// All of this wave's outstanding tile copies (and other memory ops) done.
 __device__ __forceinline__ void wait_tiles() { __builtin_amdgcn_s_waitcnt(0); }
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
@@ -115,7 +143,7 @@ template <int D>
 __device__ __forceinline__ u32x2 read_vt4(const uint16_t* tile, int kbase, int dbase, int j) {
     const int key = kbase + (j >> 2);
     const int d = dbase + 4 * (j & 3);
-    const uint16_t* a = tile + tile_off<D>(key, d >> 3) + (d & 7);
+    const uint16_t* a = tile + tile_off<D, true>(key, d >> 3) + (d & 7);
     const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
         (__attribute__((address_space(3))) i16x4*)a);
     return __builtin_bit_cast(u32x2, v);
@@ -142,15 +170,23 @@ __device__ __forceinline__ void load_q(bf16x8 (&qf)[RB][D / 16], const uint16_t*
     }
 }
 
+// Headroom (base 2) of the fixed per-row reference max in pass 1.
+constexpr float kHeadroom = 64.f;
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+constexpr bf16x2 kOnes2 = {(__bf16)1.0f, (__bf16)1.0f};
+
 // One KT-key tile of pass 1 for one wave, a 32-key block at a time:
 // S^T = K Q^T, online softmax in base 2, O^T += V^T P^T.  MASKED handles the
 // last partial cache tile and the causal chunk tiles.
-template <int D>
+template <int D, bool MASKED>
 __device__ __forceinline__ void fwd_tile(const uint16_t* Ks, const uint16_t* Vs,
                                          const bf16x8 (&qf)[RB][D / 16],
                                          f32x16 (&o_acc)[RB][D / 32], float (&m_ref)[RB],
-                                         float (&l_acc)[RB], float c, bool masked, int key0,
-                                         int lim, bool chunk, int G, int rbase, int lane) {
+                                         float (&m_seen)[RB], bool& overflow,
+                                         float (&l_acc)[RB], float (&lt_acc)[RB], float c,
+                                         int key0, int lim,
+                                         bool chunk, int G, int rbase, int lane) {
     const int l32 = lane & 31, half = lane >> 5;
 #pragma unroll
     for (int kb = 0; kb < KT / 32; ++kb) {
@@ -162,14 +198,14 @@ __device__ __forceinline__ void fwd_tile(const uint16_t* Ks, const uint16_t* Vs,
 #pragma unroll
         for (int ks = 0; ks < D / 16; ++ks) {
             const bf16x8 kf =
-                as_bf16x8(*(const u32x4*)(Ks + tile_off<D>(kb * 32 + l32, 2 * ks + half)));
+                as_bf16x8(*(const u32x4*)(Ks + tile_off<D, false>(kb * 32 + l32, 2 * ks + half)));
 #pragma unroll
             for (int rb = 0; rb < RB; ++rb) s[rb] = mfma32x32x16(kf, qf[rb][ks], s[rb]);
         }
 
-        // mask (uniform branch: last partial cache tile, chunk tiles), then
-        // row max over raw logits (c > 0)
-        if (masked) {
+        // mask (last partial cache tile, chunk tiles), then row max over raw
+        // logits (c > 0)
+        if (MASKED) {
 #pragma unroll
             for (int rb = 0; rb < RB; ++rb) {
                 const int r = rbase + rb * 32 + l32;
@@ -191,27 +227,23 @@ __device__ __forceinline__ void fwd_tile(const uint16_t* Ks, const uint16_t* Vs,
             mt[rb] = mx * c;
         }
 
-        // move the reference max only when it grows by more than 2^8, so
-        // P = 2^(u - m_ref) stays <= 256 and rescaling is rare
-        bool need = false;
+        // The reference max of a row is fixed by the first tile in which the
+        // row sees a key (O and l are still 0 then, so nothing is rescaled).
+        // Later tiles may exceed it by up to kHeadroom (P <= 2^64, far from
+        // fp32 overflow); beyond that the row is flagged and the workgroup
+        // redoes its tiles with the exact row max in m_seen.
 #pragma unroll
-        for (int rb = 0; rb < RB; ++rb) need |= mt[rb] > m_ref[rb] + 8.f;
-        if (__any(need)) {
-#pragma unroll
-            for (int rb = 0; rb < RB; ++rb) {
-                const float m_new = fmaxf(m_ref[rb], mt[rb]);
-                const float m_safe = (m_new == -INFINITY) ? 0.f : m_new;
-                const float alpha = fast_exp2(m_ref[rb] - m_safe);
-                l_acc[rb] *= alpha;
-#pragma unroll
-                for (int db = 0; db < D / 32; ++db) o_acc[rb][db] *= alpha;
-                m_ref[rb] = m_new;
-            }
+        for (int rb = 0; rb < RB; ++rb) {
+            m_seen[rb] = fmaxf(m_seen[rb], mt[rb]);
+            m_ref[rb] = (m_ref[rb] == -INFINITY) ? mt[rb] : m_ref[rb];
+            overflow |= mt[rb] > m_ref[rb] + kHeadroom;
         }
 
         // P = 2^(s*c - m), row sums, P^T fragments in bf16: element v of the
         // accumulator is key 8*(v/4) + 4*half + v%4 of the block, i.e. entry
-        // v%8 of k-step v/8
+        // v%8 of k-step v/8.  l_acc sums P exactly (for the log-sum-exp);
+        // lt_acc sums the bf16-rounded P that the PV MFMA sees, so that O is
+        // normalised by the weights it was built from.
         bf16x8 pf[2][RB];
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) {
@@ -222,6 +254,13 @@ __device__ __forceinline__ void fwd_tile(const uint16_t* Ks, const uint16_t* Vs,
                 l_acc[rb] += p;
                 pf[v >> 3][rb][v & 7] = (__bf16)p;
             }
+#pragma unroll
+            for (int hs = 0; hs < 2; ++hs)
+#pragma unroll
+                for (int e = 0; e < 8; e += 2) {
+                    const bf16x2 pair = {pf[hs][rb][e], pf[hs][rb][e + 1]};
+                    lt_acc[rb] = __builtin_amdgcn_fdot2_f32_bf16(pair, kOnes2, lt_acc[rb], false);
+                }
         }
 
         // k-step hs covers keys kb*32 + 16*hs + [0, 16) in the order lane-half
@@ -259,7 +298,8 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_kernel(
     decode_block(g.n_qt, nsplit, qt, bh, split);
     const int BH = g.B * g.Hkv;
     const int b = bh / g.Hkv, h = bh % g.Hkv;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform per wave
     const int half = lane >> 5, l32 = lane & 31;
     const int rbase = qt * kRowsPerBlock + wave * kRowsPerWave;
     // row blocks of this wave that hold any real row (uniform per wave)
@@ -276,52 +316,73 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_kernel(
     const uint16_t* kn_bh = kn + (size_t)bh * g.S * D;
     const uint16_t* vn_bh = vn + (size_t)bh * g.S * D;
 
-    float m_ref[RB], l_acc[RB];
+    float m_ref[RB], m_seen[RB], l_acc[RB], lt_acc[RB];
     f32x16 o_acc[RB][D / 32];
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-        m_ref[rb] = -INFINITY;
-        l_acc[rb] = 0.f;
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-            for (int v = 0; v < 16; ++v) o_acc[rb][db][v] = 0.f;
-    }
+    for (int rb = 0; rb < RB; ++rb) m_seen[rb] = -INFINITY;
 
     auto issue = [&](int t, int buf) {
         const bool chunk = t >= tr.n_ct;
         const int key0 = chunk ? (t - tr.n_ct) * KT : t * KT;
         const int lim = chunk ? g.S : g.n;
-        issue_tile<D>(Ks[buf], chunk ? kn_bh : kc_bh, key0, lim, wave, lane);
-        issue_tile<D>(Vs[buf], chunk ? vn_bh : vc_bh, key0, lim, wave, lane);
+        issue_tile<D, false>(Ks[buf], chunk ? kn_bh : kc_bh, key0, lim, wave, lane);
+        issue_tile<D, true>(Vs[buf], chunk ? vn_bh : vc_bh, key0, lim, wave, lane);
     };
-    if (t_begin < t_end) issue(t_begin, 0);
-    wait_tiles();
-    __syncthreads();
 
-    for (int t = t_begin; t < t_end; ++t) {
-        const int buf = (t - t_begin) & 1;
-        const bool chunk = t >= tr.n_ct;
-        const int key0 = chunk ? (t - tr.n_ct) * KT : t * KT;
-        const int lim = chunk ? g.S : g.n;
-        if (t + 1 < t_end) issue(t + 1, buf ^ 1);   // next tile lands while this one is used
-        if (live > 0)
-            fwd_tile<D>(Ks[buf], Vs[buf], qf, o_acc, m_ref, l_acc, g.c,
-                        chunk || key0 + KT > g.n, key0, lim, chunk, g.G, rbase, lane);
+    // sweep 0 fixes each row's reference max at its first visible tile; in the
+    // rare case a row's logits later overshoot it by more than kHeadroom, a
+    // second sweep reruns the tiles with the exact row max
+    for (int sweep = 0; sweep < 2; ++sweep) {
+        bool overflow = false;
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+            m_ref[rb] = (sweep == 0) ? -INFINITY : m_seen[rb];
+            l_acc[rb] = 0.f;
+            lt_acc[rb] = 0.f;
+#pragma unroll
+            for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) o_acc[rb][db][v] = 0.f;
+        }
+        if (t_begin < t_end) issue(t_begin, 0);
         wait_tiles();
         __syncthreads();
+
+        // full cache tiles first (no mask), then the partial and chunk tiles
+        const int n_full = g.n / KT;
+        const int t_mid = max(t_begin, min(t_end, n_full));
+        for (int t = t_begin; t < t_mid; ++t) {
+            const int buf = (t - t_begin) & 1;
+            if (t + 1 < t_end) issue(t + 1, buf ^ 1);   // next tile lands while this one is used
+            if (live > 0)
+                fwd_tile<D, false>(Ks[buf], Vs[buf], qf, o_acc, m_ref, m_seen, overflow, l_acc,
+                                   lt_acc, g.c, 0, 0, false, 0, rbase, lane);
+            wait_tiles();
+            __syncthreads();
+        }
+        for (int t = t_mid; t < t_end; ++t) {
+            const int buf = (t - t_begin) & 1;
+            const bool chunk = t >= tr.n_ct;
+            const int key0 = chunk ? (t - tr.n_ct) * KT : t * KT;
+            const int lim = chunk ? g.S : g.n;
+            if (t + 1 < t_end) issue(t + 1, buf ^ 1);
+            if (live > 0)
+                fwd_tile<D, true>(Ks[buf], Vs[buf], qf, o_acc, m_ref, m_seen, overflow, l_acc,
+                                  lt_acc, g.c, key0, lim, chunk, g.G, rbase, lane);
+            wait_tiles();
+            __syncthreads();
+        }
+        if (!__syncthreads_or(overflow)) break;
     }
 
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
         const float l = l_acc[rb] + xor32(l_acc[rb]);
+        const float lt = lt_acc[rb] + xor32(lt_acc[rb]);
         const int r = rbase + rb * 32 + l32;
         if (r >= g.R) continue;
         const size_t prow = ((size_t)split * BH + bh) * g.rows_pad + r;
-        if (half == 0) {
-            ml_part[prow * 2 + 0] = m_ref[rb];
-            ml_part[prow * 2 + 1] = l;
-        }
+        if (half == 0) *(f32x4*)(ml_part + prow * 4) = f32x4{m_ref[rb], l, lt, 0.f};
         float* orow = o_part + prow * D;
 #pragma unroll
         for (int db = 0; db < D / 32; ++db)
@@ -355,19 +416,22 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(
         if (dc == 0) l2[(size_t)bh * g.rows_pad + r] = INFINITY;
         return;
     }
+    // per split: (m, l, lt) with l the exact and lt the bf16-weight row sum
     float M = -INFINITY;
     for (int s = 0; s < nsplit; ++s)
-        M = fmaxf(M, ml_part[(((size_t)s * BH + bh) * g.rows_pad + r) * 2]);
-    float L = 0.f;
+        M = fmaxf(M, ml_part[(((size_t)s * BH + bh) * g.rows_pad + r) * 4]);
+    float L = 0.f, Lt = 0.f;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     for (int s = 0; s < nsplit; ++s) {
         const size_t prow = ((size_t)s * BH + bh) * g.rows_pad + r;
-        const float w = fast_exp2(ml_part[prow * 2] - M);
-        L += w * ml_part[prow * 2 + 1];
+        const f32x4 ml = *(const f32x4*)(ml_part + prow * 4);
+        const float w = fast_exp2(ml[0] - M);
+        L += w * ml[1];
+        Lt += w * ml[2];
         const f32x4 o = *(const f32x4*)(o_part + prow * D + dc * 4);
         acc += w * o;
     }
-    const float inv = 1.0f / L;
+    const float inv = 1.0f / Lt;
     const int b = bh / g.Hkv, h = bh % g.Hkv;
     const int i = r / g.G, a = h * g.G + r % g.G;
     const size_t orow = ((size_t)b * g.Hq + a) * g.S + i;
@@ -398,7 +462,7 @@ __device__ __forceinline__ void colsum_tile(const uint16_t* Ks, float* colp,
 #pragma unroll
         for (int ks = 0; ks < D / 16; ++ks) {
             const bf16x8 kf =
-                as_bf16x8(*(const u32x4*)(Ks + tile_off<D>(kb * 32 + l32, 2 * ks + half)));
+                as_bf16x8(*(const u32x4*)(Ks + tile_off<D, false>(kb * 32 + l32, 2 * ks + half)));
 #pragma unroll
             for (int rb = 0; rb < RB; ++rb) s[rb] = mfma32x32x16(qf[rb][ks], kf, s[rb]);
         }
@@ -436,7 +500,8 @@ __global__ __launch_bounds__(NT, 2) void attn_colsum_kernel(
     decode_block(g.n_qt, nsplit, qt, bh, split);
     const int BH = g.B * g.Hkv;
     const int b = bh / g.Hkv, h = bh % g.Hkv;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform per wave
     const int half = lane >> 5, l32 = lane & 31;
     const int W = g.C + g.S;
     const int rbase = qt * kRowsPerBlock + wave * kRowsPerWave;
@@ -476,7 +541,8 @@ __global__ __launch_bounds__(NT, 2) void attn_colsum_kernel(
     auto issue = [&](int t, int buf) {
         const bool chunk = t >= tr.n_ct;
         const int key0 = chunk ? (t - tr.n_ct) * KT : t * KT;
-        issue_tile<D>(Ks[buf], chunk ? kn_bh : kc_bh, key0, chunk ? g.S : g.n, wave, lane);
+        issue_tile<D, false>(Ks[buf], chunk ? kn_bh : kc_bh, key0, chunk ? g.S : g.n, wave,
+                             lane);
     };
     if (t_begin < t_end) issue(t_begin, 0);
     wait_tiles();
@@ -613,7 +679,7 @@ bool make_attn_plan(int B, int Hq, int Hkv, int D, int C, int S, int n, float sc
     pl->off_o = off;
     off = align(off + (size_t)pl->split1 * BH * g.rows_pad * D * sizeof(float));
     pl->off_ml = off;
-    off = align(off + (size_t)pl->split1 * BH * g.rows_pad * 2 * sizeof(float));
+    off = align(off + (size_t)pl->split1 * BH * g.rows_pad * 4 * sizeof(float));
     pl->off_l2 = off;
     off = align(off + (size_t)BH * g.rows_pad * sizeof(float));
     pl->off_wp = off;
