@@ -33,6 +33,7 @@ h2o_status_t check_shape(const h2o_shape_t* s) {
     if (s->n_valid < 0 || s->n_valid > s->cache_len) return H2O_ERR_INVALID_ARG;
     if (!(s->scale == s->scale)) return H2O_ERR_INVALID_ARG;   // NaN scale
     if (s->head_dim != 64 && s->head_dim != 128) return H2O_ERR_UNSUPPORTED;
+    if (s->cache_len > 65536) return H2O_ERR_UNSUPPORTED;   // slot choice holds keys in registers
     // 32-bit index limits used inside the kernels
     const long long BH = (long long)s->batch * s->n_kv_heads;
     const long long W = (long long)s->cache_len + s->chunk_len;

@@ -9,9 +9,9 @@ namespace h2o {
 
 // Tiling shared by the attention kernels.
 constexpr int kKeyTile = 64;        // keys per LDS tile
-constexpr int kRowBlocks = 2;       // 32-row MFMA blocks per wave
+constexpr int kRowBlocks = 1;       // 32-row MFMA blocks per wave
 constexpr int kRowsPerWave = 32 * kRowBlocks;   // query rows (head, query) per wave
-constexpr int kWaves = 4;           // waves per workgroup
+constexpr int kWaves = 8;           // waves per workgroup (2 per SIMD)
 constexpr int kRowsPerBlock = kRowsPerWave * kWaves;
 
 // Rows of a (b, kv head) are r = i * G + g: query i of head h*G + g.

@@ -77,11 +77,27 @@ __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t x, uint32_t* s
     return res;
 }
 
-// One workgroup per (b, kv head).  Radix select (4 passes of 8 bits) finds
-// the key T of the S-th smallest (key, slot) pair and how many slots with key
-// T are taken; a slot-ordered compaction then writes the chosen slots in
-// increasing order.  Each thread owns a contiguous run of slots, so block
-// prefix sums follow slot order.
+// Add 1 to hist[bin] for every active lane.  Lanes of the wave whose bin
+// equals the first active lane's bin are folded into a single atomic (the
+// top digits of real scores are nearly all equal, which would otherwise
+// serialise 64 same-address LDS atomics per instruction).
+__device__ __forceinline__ void hist_add(uint32_t* hist, uint32_t bin, bool active) {
+    const unsigned long long act = __ballot(active);
+    if (act == 0ull) return;
+    const int lead = __builtin_ctzll(act);
+    const uint32_t lead_bin = __shfl(bin, lead, 64);
+    const bool same = active && bin == lead_bin;
+    const unsigned long long m = __ballot(same);
+    if ((int)(threadIdx.x & 63) == lead) atomicAdd(&hist[lead_bin], (uint32_t)__popcll(m));
+    if (active && !same) atomicAdd(&hist[bin], 1u);
+}
+
+// One workgroup per (b, kv head).  Each thread holds the keys of a
+// contiguous run of KPT slots in registers.  Radix select (4 passes of 8
+// bits) finds the key T of the S-th smallest (key, slot) pair and how many
+// slots with key T are taken; a slot-ordered compaction (block prefix sums
+// over the threads' runs) then writes the chosen slots in increasing order.
+template <int KPT>
 __global__ __launch_bounds__(SEL_T) void evict_select_kernel(
     int C, int S, int n, const float* __restrict__ scores, int32_t* __restrict__ evict) {
     __shared__ uint32_t hist[256];
@@ -97,15 +113,22 @@ __global__ __launch_bounds__(SEL_T) void evict_select_kernel(
         for (int t = tid; t < S; t += SEL_T) out[t] = n + t;
         return;
     }
-    const int cpt = (C + SEL_T - 1) / SEL_T;
-    const int j0 = min(tid * cpt, C), j1 = min(j0 + cpt, C);
+    const int j0 = tid * KPT;
+    uint32_t key[KPT];
+#pragma unroll
+    for (int e = 0; e < KPT; ++e) {
+        const int j = j0 + e;
+        key[e] = (j < C) ? slot_key(sc, j, n) : 0xFFFFFFFFu;
+    }
+    // slots past C carry key ~0 and must never be counted or taken
+    const int cnt = max(0, min(KPT, C - j0));
 
     if (S == 1) {   // cache full (n == C): lexicographic min of (key, slot)
         unsigned long long best = ~0ull;
-        for (int j = j0; j < j1; ++j) {
-            const unsigned long long kj =
-                ((unsigned long long)slot_key(sc, j, n) << 32) | (unsigned)j;
-            best = kj < best ? kj : best;
+#pragma unroll
+        for (int e = 0; e < KPT; ++e) {
+            const unsigned long long kj = ((unsigned long long)key[e] << 32) | (unsigned)(j0 + e);
+            best = (e < cnt && kj < best) ? kj : best;
         }
 #pragma unroll
         for (int off = 32; off >= 1; off >>= 1) {
@@ -125,10 +148,9 @@ __global__ __launch_bounds__(SEL_T) void evict_select_kernel(
         const int shift = 24 - 8 * pass;
         for (int i = tid; i < 256; i += SEL_T) hist[i] = 0u;
         __syncthreads();
-        for (int j = j0; j < j1; ++j) {
-            const uint32_t key = slot_key(sc, j, n);
-            if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
-        }
+#pragma unroll
+        for (int e = 0; e < KPT; ++e)
+            hist_add(hist, (key[e] >> shift) & 255u, e < cnt && (key[e] & mask) == prefix);
         __syncthreads();
         if (tid < 64) {   // one wave finds the bucket holding rank k
             uint32_t h4[4], s4 = 0;
@@ -161,25 +183,25 @@ __global__ __launch_bounds__(SEL_T) void evict_select_kernel(
     const uint32_t T = prefix;
 
     uint32_t n_eq = 0, n_lt = 0;
-    for (int j = j0; j < j1; ++j) {
-        const uint32_t key = slot_key(sc, j, n);
-        n_eq += (key == T);
-        n_lt += (key < T);
+#pragma unroll
+    for (int e = 0; e < KPT; ++e) {
+        n_eq += (e < cnt && key[e] == T);
+        n_lt += (e < cnt && key[e] < T);
     }
     const uint32_t eq_before = block_exclusive_scan(n_eq, sh_wave);
-    const uint32_t eq_take =
-        (k > eq_before) ? min(k - eq_before, n_eq) : 0u;
+    const uint32_t eq_take = (k > eq_before) ? min(k - eq_before, n_eq) : 0u;
     const uint32_t out_before = block_exclusive_scan(n_lt + eq_take, sh_wave);
     uint32_t o = out_before, eq_seen = 0;
-    for (int j = j0; j < j1; ++j) {
-        const uint32_t key = slot_key(sc, j, n);
-        bool take = key < T;
-        if (key == T) {
+#pragma unroll
+    for (int e = 0; e < KPT; ++e) {
+        if (e >= cnt) break;
+        bool take = key[e] < T;
+        if (key[e] == T) {
             take = eq_seen < eq_take;
             ++eq_seen;
         }
         if (take) {
-            if (o < (uint32_t)S) out[o] = j;   // never past the row, whatever the counts
+            if (o < (uint32_t)S) out[o] = j0 + e;   // never past the row, whatever the counts
             ++o;
         }
     }
@@ -227,8 +249,19 @@ hipError_t launch_score_accumulate(int BH, int C, int S, int n, float* scores,
 
 hipError_t launch_evict_select(int BH, int C, int S, int n, const float* scores,
                                int32_t* evict_idx, hipStream_t stream) {
-    hipLaunchKernelGGL(evict_select_kernel, dim3(BH), dim3(SEL_T), 0, stream, C, S, n,
-                       scores, evict_idx);
+    // keys per thread: the smallest supported run that covers C
+    const int kpt = (C + SEL_T - 1) / SEL_T;
+    if (kpt <= 4)
+        hipLaunchKernelGGL(evict_select_kernel<4>, dim3(BH), dim3(SEL_T), 0, stream, C, S, n,
+                           scores, evict_idx);
+    else if (kpt <= 16)
+        hipLaunchKernelGGL(evict_select_kernel<16>, dim3(BH), dim3(SEL_T), 0, stream, C, S, n,
+                           scores, evict_idx);
+    else if (kpt <= 64)
+        hipLaunchKernelGGL(evict_select_kernel<64>, dim3(BH), dim3(SEL_T), 0, stream, C, S, n,
+                           scores, evict_idx);
+    else
+        return hipErrorInvalidValue;   // rejected earlier by the shape check
     return hipGetLastError();
 }
 

@@ -40,7 +40,7 @@
  *     call then returns a non-zero status and touches no buffer.
  *     H2O_ERR_HIP means a launch failed (hipGetLastError after the launch).
  *     Faults inside kernels surface at the caller's next synchronisation.
- *   - Supported: head_dim in {64, 128}; 1 <= chunk_len <= cache_len;
+ *   - Supported: head_dim in {64, 128}; 1 <= chunk_len <= cache_len <= 65536;
  *     0 <= n_valid <= cache_len; n_q_heads a multiple of n_kv_heads.
  *   - Calls are asynchronous and stream-ordered; two calls that share buffers
  *     must be ordered by the caller (same stream or events).

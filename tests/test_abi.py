@@ -74,8 +74,9 @@ def test_invalid_shapes_rejected(lib, bad):
     assert lib.kv_scatter(ctypes.byref(sh), P, P, P, P, P, P, P, P, 0, None) == _lib.H2O_ERR_INVALID_ARG
 
 
-def test_unsupported_head_dim(lib):
-    sh = _shape(head_dim=96)
+@pytest.mark.parametrize("bad", [dict(head_dim=96), dict(cache_len=65537, n_valid=0)])
+def test_unsupported_shapes(lib, bad):
+    sh = _shape(**bad)
     assert lib.h2o_workspace_size(ctypes.byref(sh)) == 0
     P = ctypes.c_void_p(256)
     assert lib.h2o_evict_select(ctypes.byref(sh), P, P, None) == _lib.H2O_ERR_UNSUPPORTED

@@ -175,10 +175,15 @@ def test_select_special_scores():
     import h2o_kv_cache_amd as h2o
     import oracle
     rng = np.random.default_rng(12)
-    for trial in range(30):
-        C = int(rng.integers(2, 3000))
-        S = int(rng.integers(1, min(C, 700) + 1))
-        n = int(rng.integers(max(0, C - S - 3), C + 1))
+    # sizes cover each keys-per-thread run of the kernel (4, 16, 64)
+    fixed = [(16384, 1024, 16384), (16384, 1, 16384), (40000, 2048, 40000), (65536, 3000, 65000)]
+    for trial in range(30 + len(fixed)):
+        if trial < len(fixed):
+            C, S, n = fixed[trial]
+        else:
+            C = int(rng.integers(2, 3000))
+            S = int(rng.integers(1, min(C, 700) + 1))
+            n = int(rng.integers(max(0, C - S - 3), C + 1))
         B, Hkv = 2, 3
         pool = np.array([0.0, -0.0, 1.0, np.inf, -np.inf, np.nan, 2.5, -1.0, 1e-30, 3.0],
                         np.float32)
