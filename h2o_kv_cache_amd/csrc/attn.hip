@@ -136,16 +136,40 @@ __device__ __forceinline__ void wait_tiles() { __builtin_amdgcn_s_waitcnt(0); }
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 
-// Transposed read of 4 keys x 1 dim per lane from a row-major V tile.  In each
-// 16-lane group, input lane j reads dims 4*(j%4)..+3 of key kbase + j/4; the
-// hardware hands output lane i dim dbase + i of keys kbase..kbase+3.
+// Per-lane byte offsets of the MFMA operand reads inside a tile.  Only these
+// depend on the lane; the key block, k-step and buffer add compile-time or
+// per-tile constants, which fold into the LDS instructions' immediate offset.
+//   k[ks]: K fragment of k-step ks (rows l32 of key block 0, dims
+//          16*ks + 8*half + [0, 8));
+//   v[db]: transposed V read of dim block db for keys 4*half + [0, 4) of key
+//          block 0.  In each 16-lane group, input lane j reads dims
+//          4*(j%4)..+3 of key j/4 of its group's 4 keys; the hardware hands
+//          output lane i dim i of those 4 keys (ds_read_b64_tr_b16).
 template <int D>
-__device__ __forceinline__ u32x2 read_vt4(const uint16_t* tile, int kbase, int dbase, int j) {
-    const int key = kbase + (j >> 2);
-    const int d = dbase + 4 * (j & 3);
-    const uint16_t* a = tile + tile_off<D, true>(key, d >> 3) + (d & 7);
+struct LdsOffsets {
+    uint32_t k[D / 16];
+    uint32_t v[D / 32];
+    __device__ __forceinline__ explicit LdsOffsets(int lane) {
+        const int l32 = lane & 31, half = lane >> 5, j = lane & 15;
+#pragma unroll
+        for (int ks = 0; ks < D / 16; ++ks)
+            k[ks] = 2u * (uint32_t)tile_off<D, false>(l32, 2 * ks + half);
+        const int key = 4 * half + (j >> 2);
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) {
+            const int d = db * 32 + (lane & 16) + 4 * (j & 3);
+            v[db] = 2u * (uint32_t)(tile_off<D, true>(key, d >> 3) + (d & 7));
+        }
+    }
+};
+
+__device__ __forceinline__ u32x4 lds_read16(const uint16_t* tile, uint32_t byte_off) {
+    return *(const u32x4*)((const char*)tile + byte_off);
+}
+
+__device__ __forceinline__ u32x2 lds_read_tr(const uint16_t* tile, uint32_t byte_off) {
     const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (__attribute__((address_space(3))) i16x4*)a);
+        (__attribute__((address_space(3))) i16x4*)((const char*)tile + byte_off));
     return __builtin_bit_cast(u32x2, v);
 }
 
@@ -181,6 +205,7 @@ constexpr bf16x2 kOnes2 = {(__bf16)1.0f, (__bf16)1.0f};
 // last partial cache tile and the causal chunk tiles.
 template <int D, bool MASKED>
 __device__ __forceinline__ void fwd_tile(const uint16_t* Ks, const uint16_t* Vs,
+                                         const LdsOffsets<D>& off,
                                          const bf16x8 (&qf)[RB][D / 16],
                                          f32x16 (&o_acc)[RB][D / 32], float (&m_ref)[RB],
                                          float (&m_seen)[RB], bool& overflow,
@@ -197,8 +222,7 @@ __device__ __forceinline__ void fwd_tile(const uint16_t* Ks, const uint16_t* Vs,
             for (int v = 0; v < 16; ++v) s[rb][v] = 0.f;
 #pragma unroll
         for (int ks = 0; ks < D / 16; ++ks) {
-            const bf16x8 kf =
-                as_bf16x8(*(const u32x4*)(Ks + tile_off<D, false>(kb * 32 + l32, 2 * ks + half)));
+            const bf16x8 kf = as_bf16x8(lds_read16(Ks, off.k[ks] + kb * 64 * D));
 #pragma unroll
             for (int rb = 0; rb < RB; ++rb) s[rb] = mfma32x32x16(kf, qf[rb][ks], s[rb]);
         }
@@ -267,12 +291,12 @@ __device__ __forceinline__ void fwd_tile(const uint16_t* Ks, const uint16_t* Vs,
         // h supplies them: 8*gg + 4*h + e
 #pragma unroll
         for (int hs = 0; hs < 2; ++hs) {
-            const int kcol = kb * 32 + 16 * hs + 4 * half;
+            // keys kb*32 + 16*hs + 8*gg + 4*half + [0, 4): rows (kb*32 + 16*hs + 8*gg) below
+            const uint32_t row_b = (uint32_t)(kb * 32 + 16 * hs) * 2 * D;
 #pragma unroll
             for (int db = 0; db < D / 32; ++db) {
-                const int dbase = db * 32 + (lane & 16);
-                const u32x2 lo = read_vt4<D>(Vs, kcol, dbase, lane & 15);
-                const u32x2 hi = read_vt4<D>(Vs, kcol + 8, dbase, lane & 15);
+                const u32x2 lo = lds_read_tr(Vs, off.v[db] + row_b);
+                const u32x2 hi = lds_read_tr(Vs, off.v[db] + row_b + 8 * 2 * D);
                 const bf16x8 vf = as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]});
 #pragma unroll
                 for (int rb = 0; rb < RB; ++rb)
@@ -307,6 +331,7 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_kernel(
 
     bf16x8 qf[RB][D / 16];
     load_q<D>(qf, q, g, b, h, rbase, l32, half);
+    const LdsOffsets<D> off(lane);
 
     const TileRange tr = tile_range(g, qt);
     const int t_begin = (int)((long)split * tr.total / nsplit);
@@ -355,7 +380,7 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_kernel(
             const int buf = (t - t_begin) & 1;
             if (t + 1 < t_end) issue(t + 1, buf ^ 1);   // next tile lands while this one is used
             if (live > 0)
-                fwd_tile<D, false>(Ks[buf], Vs[buf], qf, o_acc, m_ref, m_seen, overflow, l_acc,
+                fwd_tile<D, false>(Ks[buf], Vs[buf], off, qf, o_acc, m_ref, m_seen, overflow, l_acc,
                                    lt_acc, g.c, 0, 0, false, 0, rbase, lane);
             wait_tiles();
             __syncthreads();
@@ -367,7 +392,7 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_kernel(
             const int lim = chunk ? g.S : g.n;
             if (t + 1 < t_end) issue(t + 1, buf ^ 1);
             if (live > 0)
-                fwd_tile<D, true>(Ks[buf], Vs[buf], qf, o_acc, m_ref, m_seen, overflow, l_acc,
+                fwd_tile<D, true>(Ks[buf], Vs[buf], off, qf, o_acc, m_ref, m_seen, overflow, l_acc,
                                   lt_acc, g.c, key0, lim, chunk, g.G, rbase, lane);
             wait_tiles();
             __syncthreads();
@@ -448,7 +473,8 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(
 // MASKED handles the last partial cache tile (G == 0) and chunk tiles (G > 0:
 // row r sees chunk key t iff t*G <= r).
 template <int D, bool MASKED>
-__device__ __forceinline__ void colsum_tile(const uint16_t* Ks, float* colp,
+__device__ __forceinline__ void colsum_tile(const uint16_t* Ks, const LdsOffsets<D>& off,
+                                            float* colp,
                                             const bf16x8 (&qf)[RB][D / 16],
                                             const float (&l2v)[RB][16], float c, int key0,
                                             int lim, int G, int rbase, int l32, int half) {
@@ -461,8 +487,7 @@ __device__ __forceinline__ void colsum_tile(const uint16_t* Ks, float* colp,
             for (int v = 0; v < 16; ++v) s[rb][v] = 0.f;
 #pragma unroll
         for (int ks = 0; ks < D / 16; ++ks) {
-            const bf16x8 kf =
-                as_bf16x8(*(const u32x4*)(Ks + tile_off<D, false>(kb * 32 + l32, 2 * ks + half)));
+            const bf16x8 kf = as_bf16x8(lds_read16(Ks, off.k[ks] + kb * 64 * D));
 #pragma unroll
             for (int rb = 0; rb < RB; ++rb) s[rb] = mfma32x32x16(qf[rb][ks], kf, s[rb]);
         }
@@ -509,6 +534,7 @@ __global__ __launch_bounds__(NT, 2) void attn_colsum_kernel(
 
     bf16x8 qf[RB][D / 16];
     load_q<D>(qf, q, g, b, h, rbase, l32, half);
+    const LdsOffsets<D> off(lane);
     // base-2 LSE of the rows this lane holds in the S accumulators
     // (padding rows carry +inf, so their weights are 0)
     float l2v[RB][16];
@@ -561,10 +587,10 @@ __global__ __launch_bounds__(NT, 2) void attn_colsum_kernel(
                 colp[buf][wave][32 + l32] = 0.f;
             }
         } else if (!chunk && key0 + KT <= g.n) {
-            colsum_tile<D, false>(Ks[buf], colp[buf][wave], qf, l2v, g.c, 0, 0, 0, rbase, l32,
+            colsum_tile<D, false>(Ks[buf], off, colp[buf][wave], qf, l2v, g.c, 0, 0, 0, rbase, l32,
                                   half);
         } else {
-            colsum_tile<D, true>(Ks[buf], colp[buf][wave], qf, l2v, g.c, key0, lim,
+            colsum_tile<D, true>(Ks[buf], off, colp[buf][wave], qf, l2v, g.c, key0, lim,
                                  chunk ? g.G : 0, rbase, l32, half);
         }
         wait_tiles();
