@@ -104,7 +104,7 @@ def cpu_baseline(wl, min_seconds=10.0, max_heads=24):
         heads += 1
     per_head = spent / heads
     total = per_head * wl.n_kv_heads * wl.batch * wl.layers   # s per step, all heads/layers
-    return {"value": wl.chunk_len / total, "unit": "tokens/s", "cores": int(threads),
+    return {"value": wl.chunk_len * wl.batch / total, "unit": "tokens/s", "cores": int(threads),
             "kind": "oracle",
             "sample": (f"{heads} steady layer-steps of one KV head each ({G} query heads, "
                        f"C={wl.cache_len}, S={wl.chunk_len}), float64, {spent:.1f} s; "
@@ -130,6 +130,7 @@ def main():
     B, Hq, Hkv, D, C, S, L = (wl.batch, wl.n_q_heads, wl.n_kv_heads, wl.head_dim,
                               wl.cache_len, wl.chunk_len, wl.layers)
     shape = h2o.Shape(B, Hq, Hkv, D, C, S, C)   # steady state: cache full
+    tok_per_step = B * S
     gen = torch.Generator(device="cuda")
     gen.manual_seed(20261203)
     layers = [make_layer_state(wl, gen) for _ in range(L)]
@@ -170,12 +171,20 @@ def main():
     elapsed_ms = t_start.elapsed_time(t_stop)
 
     ms_per_step = elapsed_ms / args.steps
-    tokens_per_s = S * args.steps / (elapsed_ms / 1e3)
+    tokens_per_s = B * S * args.steps / (elapsed_ms / 1e3)
     pairs = pairs_per_layer_step(B, Hq, C, S, C)
     fwd_ms = kernel_ms["attn_fwd"] / calls
-    fwd_flop = 4.0 * D * pairs                   # QK^T + PV, 2 flop per MAC
-    achieved = fwd_flop / (fwd_ms * 1e-3) / 1e12
     per_layer = {k: v / calls for k, v in kernel_ms.items()}
+    # pass 1 reads every cached K/V row once plus the chunk's Q/K/V
+    fwd_bytes = 2.0 * (B * Hkv * (C + S) * D * 2) + B * Hq * S * D * 2
+    fwd_flop = 4.0 * D * pairs                   # QK^T + PV, 2 flop per MAC
+    if fwd_flop / fwd_bytes >= PEAK_BF16_TFLOPS / PEAK_HBM_GBS * 1e3:   # above the ridge
+        roof = {"bound": "mfma", "achieved": fwd_flop / (fwd_ms * 1e-3) / 1e12,
+                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "per_launch_flop": fwd_flop}
+    else:
+        roof = {"bound": "hbm", "achieved": fwd_bytes / (fwd_ms * 1e-3) / 1e9,
+                "peak": PEAK_HBM_GBS, "unit": "GB/s", "per_launch_bytes": fwd_bytes}
+    roof["frac"] = roof["achieved"] / roof["peak"]
     per_layer["policy_and_gaps"] = ms_per_step / L - sum(per_layer.values())
     total_flop_exec = 6.0 * D * pairs
     step_tflops = total_flop_exec * L / (ms_per_step * 1e-3) / 1e12
@@ -201,12 +210,10 @@ def main():
             "executed_mfma_tflops_whole_step": step_tflops,
             "executed_mfma_frac_whole_step": step_tflops / PEAK_BF16_TFLOPS,
         },
-        "roofline": {
-            "kernel": "attn_fwd_kernel<128> (pass 1: QK^T, online softmax, PV)",
-            "bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
-            "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None,
-            "per_launch_flop": fwd_flop, "avg_launch_ms": fwd_ms, "launches": calls,
-        },
+        "roofline": dict(
+            kernel=("attn_fwd_small_kernel<128>" if Hq // Hkv * S <= 32 else "attn_fwd_kernel<128>")
+            + " (pass 1: QK^T, online softmax, PV)",
+            traffic=None, avg_launch_ms=fwd_ms, launches=calls, **roof),
     }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wl)

@@ -114,15 +114,15 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 // 1 KiB of LDS, and each lane fetches the global chunk that belongs at its
 // LDS slot.  Rows past `lim` re-read row lim-1, a valid row whose weight is
 // masked to zero.
-template <int D, bool VT>
+template <int D, bool VT, int NW = kWaves>
 __device__ __forceinline__ void issue_tile(uint16_t* tile, const uint16_t* __restrict__ src,
                                            int key0, int lim, int wave, int lane) {
     constexpr int CPR = D / 8;
-    constexpr int ITER = KT * CPR / NT;
+    constexpr int ITER = KT * CPR / (NW * 64);
     const uint32_t base = __builtin_amdgcn_readfirstlane(lds_addr(tile));
 #pragma unroll
     for (int it = 0; it < ITER; ++it) {
-        const int blk = it * kWaves + wave;          // 1 KiB block of the tile
+        const int blk = it * NW + wave;              // 1 KiB block of the tile
         const int p = blk * 64 + lane;               // LDS chunk slot
         const int key = p / CPR;
         const int chunk = (p % CPR) ^ tile_swz<D, VT>(key);
@@ -200,21 +200,22 @@ constexpr float kHeadroom = 64.f;
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 constexpr bf16x2 kOnes2 = {(__bf16)1.0f, (__bf16)1.0f};
 
-// One KT-key tile of pass 1 for one wave, a 32-key block at a time:
+// One 32-key block (block kb of a KT-key tile) of pass 1 for one wave:
 // S^T = K Q^T, online softmax in base 2, O^T += V^T P^T.  MASKED handles the
-// last partial cache tile and the causal chunk tiles.
+// last partial cache tile and the causal chunk tiles.  With a non-null
+// `lg_row` the base-2 logits of this lane's row are also stored, at logits
+// columns col0 + (key - key0).
 template <int D, bool MASKED>
-__device__ __forceinline__ void fwd_tile(const uint16_t* Ks, const uint16_t* Vs,
-                                         const LdsOffsets<D>& off,
-                                         const bf16x8 (&qf)[RB][D / 16],
-                                         f32x16 (&o_acc)[RB][D / 32], float (&m_ref)[RB],
-                                         float (&m_seen)[RB], bool& overflow,
-                                         float (&l_acc)[RB], float (&lt_acc)[RB], float c,
-                                         int key0, int lim,
-                                         bool chunk, int G, int rbase, int lane) {
+__device__ __forceinline__ void fwd_block(const uint16_t* Ks, const uint16_t* Vs,
+                                          const LdsOffsets<D>& off,
+                                          const bf16x8 (&qf)[RB][D / 16],
+                                          f32x16 (&o_acc)[RB][D / 32], float (&m_ref)[RB],
+                                          float (&m_seen)[RB], bool& overflow,
+                                          float (&l_acc)[RB], float (&lt_acc)[RB], float c,
+                                          int kb, int key0, int lim, bool chunk, int G,
+                                          int rbase, int lane, float* lg_row, int col0) {
     const int l32 = lane & 31, half = lane >> 5;
-#pragma unroll
-    for (int kb = 0; kb < KT / 32; ++kb) {
+    {
         f32x16 s[RB];
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb)
@@ -239,6 +240,13 @@ __device__ __forceinline__ void fwd_tile(const uint16_t* Ks, const uint16_t* Vs,
                     const bool ok = key < lim && (!chunk || key * G <= r);
                     s[rb][v] = ok ? s[rb][v] : -INFINITY;
                 }
+            }
+        }
+        if (lg_row) {   // base-2 logits of the real keys (few-row path only)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int kl = kb * 32 + acc_row(v, half);
+                if (!MASKED || key0 + kl < lim) lg_row[col0 + kl] = s[0][v] * c;
             }
         }
         float mt[RB];
@@ -304,6 +312,22 @@ __device__ __forceinline__ void fwd_tile(const uint16_t* Ks, const uint16_t* Vs,
             }
         }
     }
+}
+
+// One KT-key tile of pass 1 for one wave: its 32-key blocks in order.
+template <int D, bool MASKED>
+__device__ __forceinline__ void fwd_tile(const uint16_t* Ks, const uint16_t* Vs,
+                                         const LdsOffsets<D>& off,
+                                         const bf16x8 (&qf)[RB][D / 16],
+                                         f32x16 (&o_acc)[RB][D / 32], float (&m_ref)[RB],
+                                         float (&m_seen)[RB], bool& overflow,
+                                         float (&l_acc)[RB], float (&lt_acc)[RB], float c,
+                                         int key0, int lim, bool chunk, int G, int rbase,
+                                         int lane) {
+#pragma unroll
+    for (int kb = 0; kb < KT / 32; ++kb)
+        fwd_block<D, MASKED>(Ks, Vs, off, qf, o_acc, m_ref, m_seen, overflow, l_acc, lt_acc, c,
+                             kb, key0, lim, chunk, G, rbase, lane, nullptr, 0);
 }
 
 // ---------------------------------------------------------------------------
@@ -418,6 +442,182 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_kernel(
                 *(f32x4*)(orow + db * 32 + 8 * gq + 4 * half) = v4;
             }
     }
+}
+
+// ---------------------------------------------------------------------------
+// pass 1, few rows (G * S <= 32, e.g. one decode token per sequence): a
+// single 32-row block per (b, kv head), so the waves of a workgroup take
+// different 32-key blocks of each KT-key tile, keep their own softmax state,
+// and merge it through LDS at the end.  The base-2 logits of the real rows
+// are also written out (16 B per key for 4 rows, against 256 B of K), so the
+// summed weights need no second read of K.
+// ---------------------------------------------------------------------------
+constexpr int NW_S = KT / 32;          // waves per workgroup (one key block each)
+constexpr int NT_S = NW_S * 64;
+constexpr int STAGES_S = 4;            // LDS tile buffers: 3 tiles in flight
+
+// s_waitcnt with vmcnt(n) (n < 64) and no wait on the other counters.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+template <int D>
+__global__ __launch_bounds__(NT_S, 1) void attn_fwd_small_kernel(
+    const AttnGeom g, const int nsplit, const uint16_t* __restrict__ q,
+    const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc,
+    const uint16_t* __restrict__ kn, const uint16_t* __restrict__ vn,
+    float* __restrict__ o_part, float* __restrict__ ml_part, float* __restrict__ logits) {
+    // stage b: K tile in KV[b], V tile in KV[STAGES_S + b]; reused for the final merge
+    __shared__ __attribute__((aligned(16))) uint16_t KV[2 * STAGES_S][KT * D];
+    uint16_t (*Ks)[KT * D] = KV;
+    uint16_t (*Vs)[KT * D] = KV + STAGES_S;
+    // this wave's copy instructions per tile (K and V)
+    constexpr int PER_TILE = 2 * KT * (D / 8) / NT_S;
+
+    int qt, bh, split;
+    decode_block(1, nsplit, qt, bh, split);
+    const int BH = g.B * g.Hkv;
+    const int b = bh / g.Hkv, h = bh % g.Hkv;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform per wave
+    const int l32 = lane & 31, half = lane >> 5;
+    const int W = g.C + g.S;
+
+    bf16x8 qf[RB][D / 16];
+    load_q<D>(qf, q, g, b, h, 0, l32, half);
+    const LdsOffsets<D> off(lane);
+    float* lg_row = (l32 < g.R) ? logits + ((size_t)bh * g.R + l32) * W : nullptr;
+
+    const TileRange tr = tile_range(g, 0);
+    const int t_begin = (int)((long)split * tr.total / nsplit);
+    const int t_end = (int)((long)(split + 1) * tr.total / nsplit);
+    const uint16_t* kc_bh = kc + (size_t)bh * g.C * D;
+    const uint16_t* vc_bh = vc + (size_t)bh * g.C * D;
+    const uint16_t* kn_bh = kn + (size_t)bh * g.S * D;
+    const uint16_t* vn_bh = vn + (size_t)bh * g.S * D;
+
+    float m_ref[RB], m_seen[RB], l_acc[RB], lt_acc[RB];
+    f32x16 o_acc[RB][D / 32];
+    m_seen[0] = -INFINITY;
+    auto issue = [&](int t, int buf) {
+        const bool chunk = t >= tr.n_ct;
+        const int key0 = chunk ? (t - tr.n_ct) * KT : t * KT;
+        const int lim = chunk ? g.S : g.n;
+        issue_tile<D, false, NW_S>(Ks[buf], chunk ? kn_bh : kc_bh, key0, lim, wave, lane);
+        issue_tile<D, true, NW_S>(Vs[buf], chunk ? vn_bh : vc_bh, key0, lim, wave, lane);
+    };
+    for (int sweep = 0; sweep < 2; ++sweep) {
+        bool overflow = false;
+        m_ref[0] = (sweep == 0) ? -INFINITY : m_seen[0];
+        l_acc[0] = 0.f;
+        lt_acc[0] = 0.f;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) o_acc[0][db][v] = 0.f;
+        // prologue: tiles t_begin .. t_begin+2 in flight, wait for the first
+        for (int i = 0; i < STAGES_S - 1 && t_begin + i < t_end; ++i) issue(t_begin + i, i);
+        wait_tiles();
+        __syncthreads();
+        for (int t = t_begin; t < t_end; ++t) {
+            const int buf = (t - t_begin) % STAGES_S;
+            const bool chunk = t >= tr.n_ct;
+            const int key0 = chunk ? (t - tr.n_ct) * KT : t * KT;
+            const int lim = chunk ? g.S : g.n;
+            const int col0 = chunk ? g.C + key0 : key0;
+            // the stage of tile t+3 was last read by tile t-1, which every wave
+            // finished before the barrier that ended it
+            if (t + STAGES_S - 1 < t_end) issue(t + STAGES_S - 1, (buf + STAGES_S - 1) % STAGES_S);
+            if (!chunk && key0 + KT <= g.n)
+                fwd_block<D, false>(Ks[buf], Vs[buf], off, qf, o_acc, m_ref, m_seen, overflow,
+                                    l_acc, lt_acc, g.c, wave, key0, lim, false, 0, 0, lane,
+                                    sweep == 0 ? lg_row : nullptr, col0);
+            else
+                fwd_block<D, true>(Ks[buf], Vs[buf], off, qf, o_acc, m_ref, m_seen, overflow,
+                                   l_acc, lt_acc, g.c, wave, key0, lim, chunk, g.G, 0, lane,
+                                   sweep == 0 ? lg_row : nullptr, col0);
+            // tile t+1 must have landed; tiles issued after it may stay in flight
+            // (loads complete in issue order)
+            const int later = min(STAGES_S - 2, t_end - 1 - (t + 1));
+            if (later >= 2)
+                wait_vm<2 * PER_TILE>();
+            else if (later == 1)
+                wait_vm<PER_TILE>();
+            else
+                wait_tiles();
+            __syncthreads();
+        }
+        if (!__syncthreads_or(overflow)) break;
+    }
+
+    // merge the waves' (m, l, lt, O) through LDS (the tiles are free now)
+    const float l = l_acc[0] + xor32(l_acc[0]);
+    const float lt = lt_acc[0] + xor32(lt_acc[0]);
+    constexpr int XS = D / 2 + 4;               // [NW_S][64 lanes][XS] floats
+    static_assert(NW_S * 64 * XS * 4 <= (int)sizeof(KV), "merge area exceeds the tiles");
+    float* xch = (float*)&KV[0][0];
+    float* mine = xch + ((size_t)wave * 64 + lane) * XS;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) mine[db * 16 + v] = o_acc[0][db][v];
+    mine[D / 2 + 0] = m_ref[0];
+    mine[D / 2 + 1] = l;
+    mine[D / 2 + 2] = lt;
+    __syncthreads();
+    if (wave != 0) return;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < NW_S; ++w) M = fmaxf(M, xch[((size_t)w * 64 + lane) * XS + D / 2]);
+    float wt[NW_S], L = 0.f, Lt = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW_S; ++w) {
+        const float* o = xch + ((size_t)w * 64 + lane) * XS;
+        wt[w] = (M == -INFINITY) ? 0.f : fast_exp2(o[D / 2] - M);
+        L += wt[w] * o[D / 2 + 1];
+        Lt += wt[w] * o[D / 2 + 2];
+    }
+    const int r = l32;
+    if (r >= g.R) return;
+    const size_t prow = ((size_t)split * BH + bh) * g.rows_pad + r;
+    if (half == 0) *(f32x4*)(ml_part + prow * 4) = f32x4{M, L, Lt, 0.f};
+    float* orow = o_part + prow * D;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int gq = 0; gq < 4; ++gq) {
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int w = 0; w < NW_S; ++w) {
+                const float* o = xch + ((size_t)w * 64 + lane) * XS + db * 16 + 4 * gq;
+                acc += wt[w] * f32x4{o[0], o[1], o[2], o[3]};
+            }
+            *(f32x4*)(orow + db * 32 + 8 * gq + 4 * half) = acc;
+        }
+}
+
+// Summed weights straight from the stored logits (few-row path): column j
+// sums 2^(u_rj - L2_r) over the rows that see it, in row order.
+__global__ __launch_bounds__(256) void wsum_from_logits_kernel(
+    const AttnGeom g, const float* __restrict__ logits, const float* __restrict__ l2,
+    float* __restrict__ wsum) {
+    const int W = g.C + g.S;
+    const long idx = (long)blockIdx.x * blockDim.x + threadIdx.x;
+    if (idx >= (long)g.B * g.Hkv * W) return;
+    const int j = (int)(idx % W);
+    const int bh = (int)(idx / W);
+    const float* lg = logits + (size_t)bh * g.R * W + j;
+    const float* lb = l2 + (size_t)bh * g.rows_pad;
+    float s = 0.f;
+    if (j < g.n) {
+        for (int r = 0; r < g.R; ++r) s += fast_exp2(lg[(size_t)r * W] - lb[r]);
+    } else if (j >= g.C) {
+        const int tG = (j - g.C) * g.G;   // row r sees chunk token t iff t*G <= r
+        for (int r = tG; r < g.R; ++r) s += fast_exp2(lg[(size_t)r * W] - lb[r]);
+    }
+    wsum[idx] = s;
 }
 
 // ---------------------------------------------------------------------------
@@ -656,8 +856,12 @@ hipError_t launch_attention_d(const AttnPlan& pl, const uint16_t* q,
     } while (0)
 
     if (ev) hipEventRecord(ev[0], stream);
-    hipLaunchKernelGGL(attn_fwd_kernel<D>, dim3(g.n_qt * BH * pl.split1), dim3(NT), 0,
-                       stream, g, pl.split1, q, kc, vc, kn, vn, o_part, ml_part);
+    if (pl.small)
+        hipLaunchKernelGGL(attn_fwd_small_kernel<D>, dim3(BH * pl.split1), dim3(NT_S), 0,
+                           stream, g, pl.split1, q, kc, vc, kn, vn, o_part, ml_part, wpart);
+    else
+        hipLaunchKernelGGL(attn_fwd_kernel<D>, dim3(g.n_qt * BH * pl.split1), dim3(NT), 0,
+                           stream, g, pl.split1, q, kc, vc, kn, vn, o_part, ml_part);
     H2O_CHECK();
     if (ev) hipEventRecord(ev[1], stream);
     {
@@ -668,13 +872,18 @@ hipError_t launch_attention_d(const AttnPlan& pl, const uint16_t* q,
         H2O_CHECK();
     }
     if (ev) hipEventRecord(ev[2], stream);
-    hipLaunchKernelGGL(attn_colsum_kernel<D>, dim3(g.n_qt * BH * pl.split2), dim3(NT), 0,
-                       stream, g, pl.split2, q, kc, kn, l2, wpart);
-    H2O_CHECK();
-    if (ev) hipEventRecord(ev[3], stream);
-    {
-        const long total = (long)BH * (g.C + g.S);
-        hipLaunchKernelGGL(wsum_reduce_kernel, dim3((unsigned)((total + 255) / 256)),
+    const long wtotal = (long)BH * (g.C + g.S);
+    if (pl.small) {
+        hipLaunchKernelGGL(wsum_from_logits_kernel, dim3((unsigned)((wtotal + 255) / 256)),
+                           dim3(256), 0, stream, g, wpart, l2, wsum);
+        H2O_CHECK();
+        if (ev) hipEventRecord(ev[3], stream);
+    } else {
+        hipLaunchKernelGGL(attn_colsum_kernel<D>, dim3(g.n_qt * BH * pl.split2), dim3(NT), 0,
+                           stream, g, pl.split2, q, kc, kn, l2, wpart);
+        H2O_CHECK();
+        if (ev) hipEventRecord(ev[3], stream);
+        hipLaunchKernelGGL(wsum_reduce_kernel, dim3((unsigned)((wtotal + 255) / 256)),
                            dim3(256), 0, stream, g, wpart, wsum);
         H2O_CHECK();
     }
@@ -691,15 +900,16 @@ bool make_attn_plan(int B, int Hq, int Hkv, int D, int C, int S, int n, float sc
     g.B = B; g.Hq = Hq; g.Hkv = Hkv; g.G = Hq / Hkv; g.D = D;
     g.C = C; g.S = S; g.n = n;
     g.R = g.G * S;
-    g.n_qt = (g.R + kRowsPerBlock - 1) / kRowsPerBlock;
-    g.rows_pad = g.n_qt * kRowsPerBlock;
+    pl->small = g.R <= 32;
+    g.n_qt = pl->small ? 1 : (g.R + kRowsPerBlock - 1) / kRowsPerBlock;
+    g.rows_pad = pl->small ? 32 : g.n_qt * kRowsPerBlock;
     const float tau = (scale > 0.f) ? scale : 1.0f / sqrtf((float)D);
     g.c = tau * kLog2e;
     const int BH = B * Hkv;
     const int max_tiles = (C + KT - 1) / KT + (S + KT - 1) / KT;
-    // pass 1 holds one workgroup per CU, pass 2 two (register budgets)
-    pl->split1 = pick_split(g.n_qt * BH, max_tiles, 256);
-    pl->split2 = pick_split(g.n_qt * BH, max_tiles, 512);
+    // pass 1 holds one workgroup per CU (few-row path: two), pass 2 two
+    pl->split1 = pick_split(g.n_qt * BH, max_tiles, pl->small ? 1024 : 256);
+    pl->split2 = pl->small ? 1 : pick_split(g.n_qt * BH, max_tiles, 512);
     auto align = [](size_t x) { return (x + 255) & ~(size_t)255; };
     size_t off = 0;
     pl->off_o = off;
@@ -708,8 +918,8 @@ bool make_attn_plan(int B, int Hq, int Hkv, int D, int C, int S, int n, float sc
     off = align(off + (size_t)pl->split1 * BH * g.rows_pad * 4 * sizeof(float));
     pl->off_l2 = off;
     off = align(off + (size_t)BH * g.rows_pad * sizeof(float));
-    pl->off_wp = off;
-    off = align(off + (size_t)g.n_qt * BH * (C + S) * sizeof(float));
+    pl->off_wp = off;   // row-tile partial sums, or the logits of the few-row path
+    off = align(off + (size_t)(pl->small ? g.R : g.n_qt) * BH * (C + S) * sizeof(float));
     pl->bytes = off;
     return true;
 }

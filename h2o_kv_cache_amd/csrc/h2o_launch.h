@@ -25,6 +25,7 @@ struct AttnGeom {
 
 struct AttnPlan {
     AttnGeom g;
+    bool small;     // G * S <= 32: one row block, logits stored for the weights
     int split1;     // key splits of pass 1 (log-sum-exp and output)
     int split2;     // key splits of pass 2 (summed weights)
     size_t off_o, off_ml, off_l2, off_wp, bytes;

@@ -120,6 +120,9 @@ EDGE = [
     ("s1_from_empty", 3, 8, 2, 128, 50, 1, 60, 1.0, 0.05),
     ("one_row_tile_tail", 1, 4, 1, 64, 300, 33, 12, 2.0, 0.1),
     ("big_group", 1, 16, 1, 128, 512, 40, 16, 1.0, 0.05),
+    # few query rows per KV head (G * S <= 32): the logits path
+    ("few_rows_causal", 2, 12, 3, 128, 300, 8, 40, 1.0, 0.05),
+    ("few_rows_ragged", 1, 6, 2, 64, 97, 5, 25, 1.0, 0.05),
 ]
 
 
