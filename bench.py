@@ -40,7 +40,59 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="qwen3_4b_128k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="copy a 1 GiB buffer once before timing (counter calibration)")
+    ap.add_argument("--summarize-stats", metavar="DIR",
+                    help="print a summary of a rocprofv3 --stats csv run and exit")
+    ap.add_argument("--summarize-pmc", metavar="DIR",
+                    help="print per-kernel FETCH_SIZE/WRITE_SIZE of a rocprofv3 --pmc csv run")
     return ap.parse_args()
+
+
+CALIB_BYTES = 1 << 30
+
+
+def _short(name):
+    name = name.replace("(anonymous namespace)::", "").replace("void ", "")
+    return name.split("(")[0].replace("h2o::", "")
+
+
+def summarize_stats(d):
+    """Kernel-time table from rocprofv3 --kernel-trace --stats --output-format csv."""
+    import csv
+    import glob
+    path = glob.glob(os.path.join(d, "**", "*kernel_stats.csv"), recursive=True)[0]
+    rows = list(csv.DictReader(open(path)))
+    print(f"# rocprofv3 kernel stats ({os.path.basename(path)})")
+    print(f"{'kernel':48s} {'calls':>6s} {'avg_us':>10s} {'total_ms':>10s} {'pct':>6s}")
+    for r in rows:
+        print(f"{_short(r['Name'])[:48]:48s} {int(r['Calls']):6d} "
+              f"{float(r['AverageNs']) / 1e3:10.2f} {float(r['TotalDurationNs']) / 1e6:10.3f} "
+              f"{float(r['Percentage']):6.2f}")
+
+
+def summarize_pmc(d):
+    """Average per-dispatch counter values per kernel, plus the calibration
+    factor from the 1 GiB copy (true bytes / counted bytes)."""
+    import collections
+    import csv
+    import glob
+    path = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)[0]
+    acc = collections.defaultdict(lambda: collections.defaultdict(list))
+    for r in csv.DictReader(open(path)):
+        acc[_short(r["Kernel_Name"])][r["Counter_Name"]].append(
+            (int(r["Dispatch_Id"]), float(r["Counter_Value"]), int(r["Grid_Size"])))
+    print(f"# rocprofv3 --pmc per-dispatch averages ({os.path.basename(path)})")
+    for k, ctrs in acc.items():
+        for c, vals in ctrs.items():
+            per = collections.defaultdict(float)
+            grid = {}
+            for did, v, gsz in vals:
+                per[did] += v
+                grid[did] = gsz
+            avg = sum(per.values()) / len(per)
+            print(f"{k[:60]:60s} {c:12s} dispatches {len(per):5d} avg_KiB {avg:14.1f}")
+
 
 
 def pairs_per_layer_step(B, Hq, C, S, n):
@@ -79,6 +131,31 @@ def make_layer_state(wl, gen):
     return dict(k=k, v=v, scores=scores, pos=pos)
 
 
+def measured_traffic(workload, kernel):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
+    summary (FETCH_SIZE + WRITE_SIZE, copy-calibrated), or None when there is
+    none for this workload or the kernel source changed since it was taken."""
+    import hashlib
+    import re
+    tag = {"qwen3_4b_128k": "qwen3_4b_128k"}.get(workload)
+    path = os.path.join(ROOT, "profiles", f"attn_fwd_{tag}_hbm_bytes.txt")
+    if tag is None or not os.path.exists(path):
+        return None
+    text = open(path).read()
+    src = os.path.join(ROOT, "h2o_kv_cache_amd", "csrc", "attn.hip")
+    sha = hashlib.sha1(open(src, "rb").read()).hexdigest()
+    m = re.search(r"^source_sha1 (\w+)", text, re.M)
+    if not m or m.group(1) != sha:
+        return None
+    m = re.search(rf"^{re.escape(kernel)}\s+fetch_bytes\s+(\d+)\s+write_bytes\s+(\d+)",
+                  text, re.M)
+    if not m:
+        return None
+    return {"fetch": int(m.group(1)), "write": int(m.group(2)),
+            "total": int(m.group(1)) + int(m.group(2)),
+            "source": os.path.relpath(path, ROOT)}
+
+
 def cpu_baseline(wl, min_seconds=10.0, max_heads=24):
     """The oracle (float64, as it stands) on single-KV-head slices of steady
     layer-steps, repeated until about ``min_seconds`` of CPU work; scaled to
@@ -113,6 +190,12 @@ def cpu_baseline(wl, min_seconds=10.0, max_heads=24):
 
 def main():
     args = parse()
+    if args.summarize_stats:
+        summarize_stats(args.summarize_stats)
+        return
+    if args.summarize_pmc:
+        summarize_pmc(args.summarize_pmc)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU: the H2O step shards by KV head or by "
@@ -154,6 +237,13 @@ def main():
             h2o.kv_scatter(shape, st["k"], st["v"], st["scores"], st["pos"], kn, vn,
                            new_scores, evict, p0, stream)
 
+    if args.calib_copy:   # a copy of known size, to scale the HBM byte counters
+        src = torch.empty(CALIB_BYTES // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     for i in range(args.warmup):
         run_step(i)
     torch.cuda.synchronize()
@@ -185,6 +275,8 @@ def main():
         roof = {"bound": "hbm", "achieved": fwd_bytes / (fwd_ms * 1e-3) / 1e9,
                 "peak": PEAK_HBM_GBS, "unit": "GB/s", "per_launch_bytes": fwd_bytes}
     roof["frac"] = roof["achieved"] / roof["peak"]
+    fwd_kernel = "attn_fwd_small_kernel<128>" if Hq // Hkv * S <= 32 else "attn_fwd_kernel<128>"
+    traffic = measured_traffic(wl.name, fwd_kernel)
     per_layer["policy_and_gaps"] = ms_per_step / L - sum(per_layer.values())
     total_flop_exec = 6.0 * D * pairs
     step_tflops = total_flop_exec * L / (ms_per_step * 1e-3) / 1e12
@@ -211,9 +303,9 @@ def main():
             "executed_mfma_frac_whole_step": step_tflops / PEAK_BF16_TFLOPS,
         },
         "roofline": dict(
-            kernel=("attn_fwd_small_kernel<128>" if Hq // Hkv * S <= 32 else "attn_fwd_kernel<128>")
-            + " (pass 1: QK^T, online softmax, PV)",
-            traffic=None, avg_launch_ms=fwd_ms, launches=calls, **roof),
+            kernel=fwd_kernel + " (pass 1: QK^T, online softmax, PV)",
+            traffic=(traffic["total"] if traffic else None), traffic_detail=traffic,
+            avg_launch_ms=fwd_ms, launches=calls, **roof),
     }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wl)
