@@ -678,6 +678,7 @@ __device__ __forceinline__ void colsum_tile(const uint16_t* Ks, const LdsOffsets
                                             const bf16x8 (&qf)[RB][D / 16],
                                             const float (&l2v)[RB][16], float c, int key0,
                                             int lim, int G, int rbase, int l32, int half) {
+    float col[KT / 32];
 #pragma unroll
     for (int kb = 0; kb < KT / 32; ++kb) {
         f32x16 s[RB];
@@ -691,7 +692,7 @@ __device__ __forceinline__ void colsum_tile(const uint16_t* Ks, const LdsOffsets
 #pragma unroll
             for (int rb = 0; rb < RB; ++rb) s[rb] = mfma32x32x16(qf[rb][ks], kf, s[rb]);
         }
-        float col = 0.f;
+        float cs = 0.f;
         const int key = key0 + kb * 32 + l32;
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb)
@@ -700,13 +701,18 @@ __device__ __forceinline__ void colsum_tile(const uint16_t* Ks, const LdsOffsets
                 const float p = fast_exp2(fmaf(s[rb][v], c, -l2v[rb][v]));
                 if (MASKED) {
                     const int r = rbase + rb * 32 + acc_row(v, half);
-                    col += (key < lim && key * G <= r) ? p : 0.f;
+                    cs += (key < lim && key * G <= r) ? p : 0.f;
                 } else {
-                    col += p;
+                    cs += p;
                 }
             }
-        col += xor32(col);
-        if (half == 0) colp[kb * 32 + l32] = col;
+        col[kb] = cs + xor32(cs);
+    }
+    // both halves hold the sums; the lower half stores them (one divergent
+    // region per tile, so the key blocks above schedule as one stretch)
+    if (half == 0) {
+#pragma unroll
+        for (int kb = 0; kb < KT / 32; ++kb) colp[kb * 32 + l32] = col[kb];
     }
 }
 
