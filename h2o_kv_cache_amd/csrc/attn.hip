@@ -860,8 +860,12 @@ hipError_t launch_attention_d(const AttnPlan& pl, const uint16_t* q,
             if (err != hipSuccess) return err;                   \
         }                                                        \
     } while (0)
+#define H2O_EVENT(i)                                                               \
+    do {                                                                           \
+        if (ev && (err = hipEventRecord(ev[i], stream)) != hipSuccess) return err; \
+    } while (0)
 
-    if (ev) hipEventRecord(ev[0], stream);
+    H2O_EVENT(0);
     if (pl.small)
         hipLaunchKernelGGL(attn_fwd_small_kernel<D>, dim3(BH * pl.split1), dim3(NT_S), 0,
                            stream, g, pl.split1, q, kc, vc, kn, vn, o_part, ml_part, wpart);
@@ -869,7 +873,7 @@ hipError_t launch_attention_d(const AttnPlan& pl, const uint16_t* q,
         hipLaunchKernelGGL(attn_fwd_kernel<D>, dim3(g.n_qt * BH * pl.split1), dim3(NT), 0,
                            stream, g, pl.split1, q, kc, vc, kn, vn, o_part, ml_part);
     H2O_CHECK();
-    if (ev) hipEventRecord(ev[1], stream);
+    H2O_EVENT(1);
     {
         const long total = (long)BH * g.rows_pad * (D / 4);
         hipLaunchKernelGGL(attn_combine_kernel<D>, dim3((unsigned)((total + 255) / 256)),
@@ -877,24 +881,25 @@ hipError_t launch_attention_d(const AttnPlan& pl, const uint16_t* q,
                            lse, l2);
         H2O_CHECK();
     }
-    if (ev) hipEventRecord(ev[2], stream);
+    H2O_EVENT(2);
     const long wtotal = (long)BH * (g.C + g.S);
     if (pl.small) {
         hipLaunchKernelGGL(wsum_from_logits_kernel, dim3((unsigned)((wtotal + 255) / 256)),
                            dim3(256), 0, stream, g, wpart, l2, wsum);
         H2O_CHECK();
-        if (ev) hipEventRecord(ev[3], stream);
+        H2O_EVENT(3);
     } else {
         hipLaunchKernelGGL(attn_colsum_kernel<D>, dim3(g.n_qt * BH * pl.split2), dim3(NT), 0,
                            stream, g, pl.split2, q, kc, kn, l2, wpart);
         H2O_CHECK();
-        if (ev) hipEventRecord(ev[3], stream);
+        H2O_EVENT(3);
         hipLaunchKernelGGL(wsum_reduce_kernel, dim3((unsigned)((wtotal + 255) / 256)),
                            dim3(256), 0, stream, g, wpart, wsum);
         H2O_CHECK();
     }
-    if (ev) hipEventRecord(ev[4], stream);
+    H2O_EVENT(4);
 #undef H2O_CHECK
+#undef H2O_EVENT
     return hipSuccess;
 }
 

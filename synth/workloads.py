@@ -83,6 +83,9 @@ WORKLOADS = {
     # Qwen3-4B-shaped layers at 128k: C=16384, S=1024, 36 layers
     "qwen3_4b_128k": Workload("qwen3_4b_128k", 3, 1, 32, 8, 128, 16384, 1024,
                               131072, 36, 1.0, 0.05, 4.0, False),
+    # small chunks at 64k: C=8192, S=128 (the pages' 128-token setting), 36 layers
+    "qwen3_4b_64k_s128": Workload("qwen3_4b_64k_s128", 5, 1, 32, 8, 128, 8192, 128,
+                                  65536, 36, 1.0, 0.05, 4.0, False),
     # decode: 16 sequences, cache pre-filled, one token per step, 4096 steps
     "decode": Workload("decode", 4, 16, 32, 8, 128, 16384, 1, 4096, 1,
                        1.0, 0.05, 4.0, True),

@@ -93,6 +93,17 @@ def test_qwen3_128k_fill_step():
     _steady(wl, heads=[1], step=9, n_valid=9 * wl.chunk_len)
 
 
+def test_qwen3_64k_small_chunk_steady_steps():
+    wl = WORKLOADS["qwen3_4b_64k_s128"]
+    for step in (wl.fill_steps + 2, wl.fill_steps + 301):
+        _steady(wl, heads=[3, 6], step=step, layer=5)
+
+
+def test_qwen3_64k_small_chunk_fill_step():
+    wl = WORKLOADS["qwen3_4b_64k_s128"]
+    _steady(wl, heads=[0], step=17, n_valid=17 * wl.chunk_len)
+
+
 def test_decode_steps():
     wl = WORKLOADS["decode"]
     st = state_from_synth(synth.prefilled_state(wl))
@@ -150,6 +161,39 @@ def test_partial_overflow_and_garbage_slots():
     r = oracle_step(st, ch.q_bits, ch.k_bits, ch.v_bits, ch.p0)
     compare(g, r, st, ch.k_bits, ch.v_bits, ch.p0, "overflow")
     assert set(range(144, 160)).issubset(set(g["evict_idx"][0, 0].tolist()))
+
+
+# name, B, Hq, Hkv, D, C, S, heavy cache slot, heavy chunk column
+WIDE = [
+    ("wide_row_tiles", 1, 4, 1, 128, 1024, 128, 700, 90),
+    ("wide_few_rows", 2, 8, 2, 128, 512, 1, 300, 0),
+]
+
+
+@pytest.mark.parametrize("name,B,Hq,Hkv,D,C,S,slot,col", WIDE)
+def test_wide_logit_spread(name, B, Hq, Hkv, D, C, S, slot, col):
+    """All-positive queries against one cache slot (and one chunk key) of
+    constant 8.0: their logits exceed every row's first-tile maximum by about
+    130 in base 2, so weights against that reference would overflow fp32 and
+    pass 1 has to redo the rows against their exact maxima."""
+    wl = synth.Workload(name, 130 + [w[0] for w in WIDE].index(name), B, Hq, Hkv, D, C, S,
+                        4 * S, 1, 1.0, 0.0, 1.0, False)
+    step = C // S + 1
+    st = state_from_synth(synth.steady_state(wl, 0, step))
+    ch = synth.gen_chunk(wl, 0, step)
+    q = synth.to_bf16(np.abs(synth.bf16_bits_to_f32(ch.q_bits)) + np.float32(0.25))[0]
+    big = synth.to_bf16(np.full(D, 8.0, np.float32))[0]
+    st.k_bits[:, :, slot, :] = big
+    kn = ch.k_bits.copy()
+    kn[:, :, col, :] = big
+    shape = shape_of(B, Hq, Hkv, D, C, S, st.n_valid)
+    log(f"[parity] {name} heavy slot {slot} chunk column {col}")
+    g = gpu_step(shape, st, q, kn, ch.v_bits, ch.p0)
+    r = oracle_step(st, q, kn, ch.v_bits, ch.p0)
+    s = compare(g, r, st, kn, ch.v_bits, ch.p0, name)
+    log(f"[parity] {name} stats {s}")
+    # the heavy keys take nearly all of the weight of the rows that see them
+    assert r["wsum"][0, 0, slot] > 0.25 * (Hq // Hkv) * S
 
 
 def test_exact_tie_trajectory():
