@@ -46,6 +46,10 @@ def parse():
                     help="print a summary of a rocprofv3 --stats csv run and exit")
     ap.add_argument("--summarize-pmc", metavar="DIR",
                     help="print per-kernel FETCH_SIZE/WRITE_SIZE of a rocprofv3 --pmc csv run")
+    ap.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="print the copy-calibrated HBM bytes per dispatch of every h2o "
+                         "kernel from a FETCH_SIZE and a WRITE_SIZE run (both with "
+                         "--calib-copy); the file format measured_traffic() reads")
     return ap.parse_args()
 
 
@@ -93,6 +97,44 @@ def summarize_pmc(d):
             avg = sum(per.values()) / len(per)
             print(f"{k[:60]:60s} {c:12s} dispatches {len(per):5d} avg_KiB {avg:14.1f}")
 
+
+
+def _pmc_kib(d, counter):
+    """{kernel: average KiB per dispatch} of one rocprofv3 --pmc csv run."""
+    import collections
+    import csv
+    import glob
+    path = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)[0]
+    per = collections.defaultdict(lambda: collections.defaultdict(float))
+    for r in csv.DictReader(open(path)):
+        if r["Counter_Name"] == counter:
+            per[_short(r["Kernel_Name"])][int(r["Dispatch_Id"])] += float(r["Counter_Value"])
+    return {k: (sum(v.values()) / len(v), len(v)) for k, v in per.items()}
+
+
+def traffic_summary(fetch_dir, write_dir):
+    """HBM bytes per dispatch of each h2o kernel: counter KiB x 1024, scaled by
+    (true bytes / counted bytes) of the 1 GiB calibration copy."""
+    import hashlib
+    fetch = _pmc_kib(fetch_dir, "FETCH_SIZE")
+    write = _pmc_kib(write_dir, "WRITE_SIZE")
+    copy = next(k for k in fetch if "copyBuffer" in k)
+    f_scale = CALIB_BYTES / (fetch[copy][0] * 1024.0)
+    w_scale = CALIB_BYTES / (write[copy][0] * 1024.0)
+    src = os.path.join(ROOT, "h2o_kv_cache_amd", "csrc", "attn.hip")
+    print(f"# calibration: the 1 GiB copy reads FETCH_SIZE {fetch[copy][0]:.1f} KiB, "
+          f"WRITE_SIZE {write[copy][0]:.1f} KiB")
+    print(f"fetch_scale {f_scale:.5f}")
+    print(f"write_scale {w_scale:.5f}")
+    print("# bytes = counter KiB x 1024 x scale, averaged over the dispatches")
+    print(f"source_sha1 {hashlib.sha1(open(src, 'rb').read()).hexdigest()}")
+    for k in fetch:
+        if k in write and "copyBuffer" not in k and not k.startswith("at::") \
+                and not k.startswith("elementwise"):
+            fb = fetch[k][0] * 1024.0 * f_scale
+            wb = write[k][0] * 1024.0 * w_scale
+            print(f"{k:28s} fetch_bytes {fb:14.0f} write_bytes {wb:14.0f}   "
+                  f"dispatches {fetch[k][1]}")
 
 
 def pairs_per_layer_step(B, Hq, C, S, n):
@@ -195,6 +237,9 @@ def main():
         return
     if args.summarize_pmc:
         summarize_pmc(args.summarize_pmc)
+        return
+    if args.traffic_summary:
+        traffic_summary(*args.traffic_summary)
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
