@@ -40,6 +40,11 @@ reading, listed here and implemented below:
       goes to the t-th of them;
   R10 positions are absolute token indices; -1 marks an empty slot.
 
+The backward of the attention with the slot layout fixed
+(``attention_chunk_backward``) follows [LtF-zh] abstract and §1: the paper's
+fine-tuning computes gradients through the sparse attention with the cache
+policy in place.
+
 Arithmetic is float64 by default.  ``dtype=np.float32`` runs the same code in
 float32 (the timed CPU baseline).  Inputs are the bf16-rounded values the
 device sees, passed in as float arrays.
@@ -99,6 +104,63 @@ def attention_chunk(q, k_cache, v_cache, k_new, v_new, n_valid, scale=None,
             wsum[b, h, :n] += col[:n]                             # R2
             wsum[b, h, C:] += col[n:]
     return out, lse, wsum
+
+
+def attention_chunk_backward(q, k_cache, v_cache, k_new, v_new, n_valid, dout, scale=None,
+                             dtype=np.float64):
+    """Gradients of ``out`` of :func:`attention_chunk` with respect to all of
+    its inputs, for a given upstream gradient ``dout`` [B, Hq, S, D].
+
+    The slot layout (which keys are visible) is fixed: the eviction decisions
+    that produced it are discrete and not differentiated.  This is the step a
+    fine-tuning loop calls to push gradients through the sparse attention with
+    the cache policy in place ([LtF-zh] abstract and §1: gradients for the
+    whole model are computed under any KV cache policy, with no approximation
+    beyond the sparse attention itself).
+
+    Written out from the chain rule of out = softmax(tau Q K^T) V over the
+    visible keys (R3-R5):  dp = dout V^T;  D_i = sum_j p_ij dp_ij;
+    ds = p * (dp - D);  dq = tau ds K;  dk = tau ds^T Q;  dv = p^T dout,
+    with the G query heads of a KV head summed into its key / value gradients.
+
+    Returns ``(dq, dk_cache, dv_cache, dk_new, dv_new)``; the cache gradients
+    are zero for empty slots (index >= n_valid).
+    """
+    B, Hq, S, D = q.shape
+    Hkv, C = k_cache.shape[1], k_cache.shape[2]
+    G = Hq // Hkv
+    n = int(n_valid)
+    tau = (1.0 / math.sqrt(D)) if (scale is None or scale <= 0) else float(scale)
+    dq = np.zeros((B, Hq, S, D), dtype)
+    dk_cache = np.zeros((B, Hkv, C, D), dtype)
+    dv_cache = np.zeros((B, Hkv, C, D), dtype)
+    dk_new = np.zeros((B, Hkv, S, D), dtype)
+    dv_new = np.zeros((B, Hkv, S, D), dtype)
+    visible = np.concatenate([np.ones((S, n), bool),
+                              np.tril(np.ones((S, S), bool))], axis=1)
+    for b in range(B):
+        for a in range(Hq):
+            h = a // G
+            keys = np.concatenate([k_cache[b, h, :n], k_new[b, h]]).astype(dtype)
+            vals = np.concatenate([v_cache[b, h, :n], v_new[b, h]]).astype(dtype)
+            qa = q[b, a].astype(dtype)
+            go = dout[b, a].astype(dtype)
+            s = dtype(tau) * (qa @ keys.T)
+            s = np.where(visible, s, dtype(-np.inf))
+            m = s.max(axis=1, keepdims=True)
+            p = np.exp(s - m)
+            p /= p.sum(axis=1, keepdims=True)                      # masked -> 0
+            dp = go @ vals.T
+            drow = (p * dp).sum(axis=1, keepdims=True)
+            ds = p * (dp - drow)
+            dq[b, a] = dtype(tau) * (ds @ keys)
+            dk = dtype(tau) * (ds.T @ qa)
+            dv = p.T @ go
+            dk_cache[b, h, :n] += dk[:n]
+            dv_cache[b, h, :n] += dv[:n]
+            dk_new[b, h] += dk[n:]
+            dv_new[b, h] += dv[n:]
+    return dq, dk_cache, dv_cache, dk_new, dv_new
 
 
 # ---------------------------------------------------------------------------
