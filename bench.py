@@ -46,6 +46,9 @@ def parse():
                     help="print a summary of a rocprofv3 --stats csv run and exit")
     ap.add_argument("--summarize-pmc", metavar="DIR",
                     help="print per-kernel FETCH_SIZE/WRITE_SIZE of a rocprofv3 --pmc csv run")
+    ap.add_argument("--backward", action="store_true",
+                    help="time the attention backward (dQ, dK, dV with the slot layout "
+                         "fixed) instead of the forward step")
     ap.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="print the copy-calibrated HBM bytes per dispatch of every h2o "
                          "kernel from a FETCH_SIZE and a WRITE_SIZE run (both with "
@@ -230,6 +233,99 @@ def cpu_baseline(wl, min_seconds=10.0, max_heads=24):
                        f"scaled x{wl.n_kv_heads * wl.batch} heads x{wl.layers} layers")}
 
 
+def run_backward(args, wl):
+    """Time h2o_attn_chunk_bwd over all layers of a steady step.  Each layer
+    keeps one chunk (its forward output and log-sum-exp computed once,
+    untimed): the backward has no value-dependent work, so the timed steps
+    repeat the same calls."""
+    import torch
+    import h2o_kv_cache_amd as h2o
+    B, Hq, Hkv, D, C, S, L = (wl.batch, wl.n_q_heads, wl.n_kv_heads, wl.head_dim,
+                              wl.cache_len, wl.chunk_len, wl.layers)
+    shape = h2o.Shape(B, Hq, Hkv, D, C, S, C)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(20261204)
+    layers = [make_layer_state(wl, gen) for _ in range(L)]
+    chunk = make_inputs(wl, 1, gen)[0]
+    ws_f = torch.empty(h2o.h2o_workspace_size(shape), dtype=torch.uint8, device="cuda")
+    ws_b = torch.empty(h2o.h2o_attn_bwd_workspace_size(shape), dtype=torch.uint8, device="cuda")
+    wsum = torch.empty((B, Hkv, C + S), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+    fw = []
+    for li, st in enumerate(layers):
+        q, kn, vn = chunk[li]
+        out = torch.empty((B, Hq, S, D), dtype=torch.float32, device="cuda")
+        lse = torch.empty((B, Hq, S), dtype=torch.float32, device="cuda")
+        h2o.h2o_attn_chunk(shape, q, st["k"], st["v"], kn, vn, out, lse, wsum, ws_f, stream)
+        dout = torch.randn((B, Hq, S, D), generator=gen, device="cuda").to(torch.bfloat16)
+        fw.append((out, lse, dout))
+    grads = dict(dq=torch.empty((B, Hq, S, D), device="cuda"),
+                 dkc=torch.empty((B, Hkv, C, D), device="cuda"),
+                 dvc=torch.empty((B, Hkv, C, D), device="cuda"),
+                 dkn=torch.empty((B, Hkv, S, D), device="cuda"),
+                 dvn=torch.empty((B, Hkv, S, D), device="cuda"))
+
+    def run_step():
+        for li, st in enumerate(layers):
+            q, kn, vn = chunk[li]
+            out, lse, dout = fw[li]
+            h2o.h2o_attn_chunk_bwd(shape, q, st["k"], st["v"], kn, vn, out, lse, dout,
+                                   grads["dq"], grads["dkc"], grads["dvc"], grads["dkn"],
+                                   grads["dvn"], ws_b, stream)
+
+    for _ in range(args.warmup):
+        run_step()
+    torch.cuda.synchronize()
+    h2o.h2o_timing_start(args.steps * L)
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_stop = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for _ in range(args.steps):
+        run_step()
+    t_stop.record(stream)
+    torch.cuda.synchronize()
+    kernel_ms, calls = h2o.h2o_timing_stop()
+    elapsed_ms = t_start.elapsed_time(t_stop)
+    ms_per_step = elapsed_ms / args.steps
+    pairs = pairs_per_layer_step(B, Hq, C, S, C)
+    names = ("bwd_prep", "bwd_dkdv", "bwd_dq")
+    per_layer = {n: kernel_ms[k] / calls for n, k in zip(names, h2o.ATTN_KERNELS)}
+    dkdv_ms = per_layer["bwd_dkdv"]
+    # algorithmic, 2*D flop per pair each: dP = dO V^T, dV = P^T dO and
+    # dK = dS^T Q (the key-major kernel), dQ = dS K (the query-major one).
+    # Executed: the key-major kernel also recomputes S (8*D per pair), the
+    # query-major one S and dP (6*D per pair)
+    dkdv_flop = 6.0 * D * pairs
+    roof = {"bound": "mfma", "achieved": dkdv_flop / (dkdv_ms * 1e-3) / 1e12,
+            "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "per_launch_flop": dkdv_flop}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    result = {
+        "metric": "H2O chunk-step attention backward tokens/s (dQ, dK, dV; slot layout fixed)",
+        "value": B * S * args.steps / (elapsed_ms / 1e3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": wl.name, "batch": B, "q_heads": Hq, "kv_heads": Hkv, "head_dim": D,
+            "cache_len": C, "chunk_len": S, "layers": L, "pass": "backward",
+            "ms_per_layer_step": per_layer,
+            "algorithmic_flop_per_layer_step": 8.0 * D * pairs,
+            "algorithmic_tflops_whole_step": 8.0 * D * pairs * L / (ms_per_step * 1e-3) / 1e12,
+        },
+        "roofline": dict(kernel="bwd_dkdv_kernel<%d> (dP, dV, dK)" % D, traffic=None,
+                         avg_launch_ms=dkdv_ms, launches=calls, **roof),
+    }
+    print(json.dumps(result), flush=True)
+
+
 def main():
     args = parse()
     if args.summarize_stats:
@@ -255,6 +351,9 @@ def main():
     wl = synth.WORKLOADS[args.workload]
     h2o.load_library()
     torch.cuda.set_device(0)
+    if args.backward:
+        run_backward(args, wl)
+        return
     B, Hq, Hkv, D, C, S, L = (wl.batch, wl.n_q_heads, wl.n_kv_heads, wl.head_dim,
                               wl.cache_len, wl.chunk_len, wl.layers)
     shape = h2o.Shape(B, Hq, Hkv, D, C, S, C)   # steady state: cache full

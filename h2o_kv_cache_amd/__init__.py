@@ -31,6 +31,7 @@ from ._lib import H2OShape
 
 __all__ = ["Shape", "H2OError", "h2o_workspace_size", "h2o_attn_chunk",
            "h2o_score_accumulate", "h2o_evict_select", "kv_scatter",
+           "h2o_attn_bwd_workspace_size", "h2o_attn_chunk_bwd",
            "h2o_timing_start", "h2o_timing_stop", "h2o_status_string", "H2OCache",
            "load_library", "ATTN_KERNELS"]
 
@@ -169,6 +170,43 @@ def kv_scatter(shape: Shape, k_cache, v_cache, scores, pos, k_new, v_new, new_sc
         _ptr(evict_idx, "evict_idx", (B, Hkv, S), (torch.int32,)),
         ctypes.c_int64(int(p0)), _stream(stream)),
         "kv_scatter")
+
+
+def h2o_attn_bwd_workspace_size(shape: Shape) -> int:
+    sh = shape.c()
+    return int(_lib.load().h2o_attn_bwd_workspace_size(ctypes.byref(sh)))
+
+
+def h2o_attn_chunk_bwd(shape: Shape, q, k_cache, v_cache, k_new, v_new, out, lse, dout,
+                       dq, dk_cache, dv_cache, dk_new, dv_new, ws, stream=None):
+    """Gradients of h2o_attn_chunk's output (slot layout fixed).  dout is
+    bf16; the gradients are fp32 and every element is written."""
+    s = shape
+    B, Hq, Hkv, D, C, S = (s.batch, s.n_q_heads, s.n_kv_heads, s.head_dim,
+                           s.cache_len, s.chunk_len)
+    args = [
+        _ptr(q, "q", (B, Hq, S, D), _BF16),
+        _ptr(k_cache, "k_cache", (B, Hkv, C, D), _BF16),
+        _ptr(v_cache, "v_cache", (B, Hkv, C, D), _BF16),
+        _ptr(k_new, "k_new", (B, Hkv, S, D), _BF16),
+        _ptr(v_new, "v_new", (B, Hkv, S, D), _BF16),
+        _ptr(out, "out", (B, Hq, S, D), _F32),
+        _ptr(lse, "lse", (B, Hq, S), _F32),
+        _ptr(dout, "dout", (B, Hq, S, D), _BF16),
+        _ptr(dq, "dq", (B, Hq, S, D), _F32),
+        _ptr(dk_cache, "dk_cache", (B, Hkv, C, D), _F32),
+        _ptr(dv_cache, "dv_cache", (B, Hkv, C, D), _F32),
+        _ptr(dk_new, "dk_new", (B, Hkv, S, D), _F32),
+        _ptr(dv_new, "dv_new", (B, Hkv, S, D), _F32),
+    ]
+    if ws.device.type != "cuda" or not ws.is_contiguous():
+        raise ValueError("ws must be a contiguous device tensor")
+    nbytes = ws.numel() * ws.element_size()
+    sh = s.c()
+    _check(_lib.load().h2o_attn_chunk_bwd(ctypes.byref(sh), *args,
+                                          ctypes.c_void_p(ws.data_ptr()),
+                                          ctypes.c_size_t(nbytes), _stream(stream)),
+           "h2o_attn_chunk_bwd")
 
 
 def h2o_timing_start(max_calls: int):

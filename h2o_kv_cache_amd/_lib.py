@@ -15,7 +15,8 @@ H2O_ERR_WORKSPACE = 3
 H2O_ERR_HIP = 4
 
 EXPORTED = ("h2o_workspace_size", "h2o_attn_chunk", "h2o_score_accumulate",
-            "h2o_evict_select", "kv_scatter", "h2o_timing_start", "h2o_timing_stop",
+            "h2o_evict_select", "kv_scatter", "h2o_attn_bwd_workspace_size",
+            "h2o_attn_chunk_bwd", "h2o_timing_start", "h2o_timing_stop",
             "h2o_status_string")
 
 
@@ -44,6 +45,10 @@ def _declare(lib):
     lib.h2o_evict_select.restype = ctypes.c_int
     lib.kv_scatter.argtypes = [S, P, P, P, P, P, P, P, P, ctypes.c_int64, P]
     lib.kv_scatter.restype = ctypes.c_int
+    lib.h2o_attn_bwd_workspace_size.argtypes = [S]
+    lib.h2o_attn_bwd_workspace_size.restype = ctypes.c_size_t
+    lib.h2o_attn_chunk_bwd.argtypes = [S] + [P] * 14 + [ctypes.c_size_t, P]
+    lib.h2o_attn_chunk_bwd.restype = ctypes.c_int
     lib.h2o_timing_start.argtypes = [ctypes.c_int32]
     lib.h2o_timing_start.restype = ctypes.c_int
     lib.h2o_timing_stop.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int32)]

@@ -4,8 +4,10 @@
 // set in the environment, which synchronises after every launch to pin a
 // fault to its kernel).
 #include "h2o.h"
+#include "h2o_device.h"
 #include "h2o_launch.h"
 
+#include <math.h>
 #include <stdlib.h>
 
 #include <vector>
@@ -139,13 +141,62 @@ h2o_status_t kv_scatter(const h2o_shape_t* s, uint16_t* k_cache, uint16_t* v_cac
     return from_hip(e);
 }
 
+}  // extern "C"
+
+namespace {
+
+h2o::BwdGeom bwd_geom(const h2o_shape_t* s) {
+    h2o::BwdGeom g;
+    g.B = s->batch;
+    g.Hq = s->n_q_heads;
+    g.Hkv = s->n_kv_heads;
+    g.G = g.Hq / g.Hkv;
+    g.D = s->head_dim;
+    g.C = s->cache_len;
+    g.S = s->chunk_len;
+    g.n = s->n_valid;
+    g.R = g.G * g.S;
+    g.tau = s->scale > 0.f ? s->scale : 1.0f / sqrtf((float)g.D);
+    g.c = g.tau * h2o::kLog2e;
+    return g;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t h2o_attn_bwd_workspace_size(const h2o_shape_t* s) {
+    if (check_shape(s) != H2O_OK) return 0;
+    return (h2o::bwd_workspace_bytes(bwd_geom(s)) + 255) & ~(size_t)255;
+}
+
+h2o_status_t h2o_attn_chunk_bwd(const h2o_shape_t* s, const uint16_t* q,
+                                const uint16_t* k_cache, const uint16_t* v_cache,
+                                const uint16_t* k_new, const uint16_t* v_new,
+                                const float* out, const float* lse, const uint16_t* dout,
+                                float* dq, float* dk_cache, float* dv_cache, float* dk_new,
+                                float* dv_new, void* ws, size_t ws_bytes, void* stream) {
+    h2o_status_t st = check_shape(s);
+    if (st != H2O_OK) return st;
+    const void* ptrs[] = {q, k_cache, v_cache, k_new, v_new, out, lse, dout,
+                          dq, dk_cache, dv_cache, dk_new, dv_new};
+    for (const void* p : ptrs)
+        if (!p || !aligned16(p)) return H2O_ERR_INVALID_ARG;
+    const h2o::BwdGeom g = bwd_geom(s);
+    const size_t need = (h2o::bwd_workspace_bytes(g) + 255) & ~(size_t)255;
+    if (!ws || ((uintptr_t)ws & 255u) || ws_bytes < need) return H2O_ERR_WORKSPACE;
+    return from_hip(h2o::launch_attention_bwd(g, q, k_cache, v_cache, k_new, v_new, out, lse,
+                                              dout, dq, dk_cache, dv_cache, dk_new, dv_new, ws,
+                                              (hipStream_t)stream, sync_debug(), timing_slot()));
+}
+
 h2o_status_t h2o_timing_start(int32_t max_calls) {
     if (max_calls < 1 || max_calls > (1 << 20) || g_timing.on) return H2O_ERR_INVALID_ARG;
     g_timing.ev.assign((size_t)5 * max_calls, nullptr);
     for (auto& e : g_timing.ev) {
         if (hipEventCreate(&e) != hipSuccess) {
             for (auto& x : g_timing.ev)
-                if (x) hipEventDestroy(x);
+                if (x) (void)hipEventDestroy(x);
             g_timing.ev.clear();
             return H2O_ERR_HIP;
         }
@@ -175,7 +226,7 @@ h2o_status_t h2o_timing_stop(double* ms, int32_t* calls) {
         }
     }
     *calls = g_timing.used;
-    for (auto& e : g_timing.ev) hipEventDestroy(e);
+    for (auto& e : g_timing.ev) (void)hipEventDestroy(e);
     g_timing.ev.clear();
     g_timing.on = false;
     g_timing.used = 0;

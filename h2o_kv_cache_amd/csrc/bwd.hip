@@ -1,0 +1,553 @@
+// Backward of the chunk attention with the slot layout fixed, for gfx950.
+//
+// Method: "Learning how to Forget: Fine-tuning for Long-Context Sparse
+// Attention" -- Chinese translation page, abstract and §1: the fine-tuning
+// computes gradients through the sparse attention with the KV cache policy in
+// place, with no approximation beyond the sparse attention.  The eviction
+// decisions that produced the slot layout are discrete and not
+// differentiated; gradients flow to Q, to the K/V rows of the valid cache
+// slots, and to the chunk's K/V.
+//
+// With P = 2^(S*c - L2) the forward's normalised weights (c = scale*log2 e,
+// L2 the row's base-2 log-sum-exp):
+//   dP = dO V^T,  D_i = sum_j P_ij dP_ij = dO_i . O_i,  dS = P * (dP - D),
+//   dQ = scale dS K,   dK = scale dS^T Q,   dV = P^T dO.
+// Three kernels:
+//   bwd_prep_kernel  per packed row: L2 and D.
+//   bwd_dkdv_kernel  key-major.  A wave owns one (D = 128) or two (D = 64)
+//                    32-key blocks of one KV head, keeps their K and V
+//                    fragments and its dK^T, dV^T
+//                    accumulators in registers, and walks the rows of the G
+//                    query heads in 32-row blocks: S = Q K^T and dP = dO V^T
+//                    (a lane owns a key and 16 rows), then dV^T += dO^T P and
+//                    dK^T += Q^T dS straight from those accumulators (the
+//                    contraction runs over rows, whose fragments are read
+//                    transposed from LDS).
+//   bwd_dq_kernel    row-major, shaped like the forward's pass 1:
+//                    S^T = K Q^T and dP^T = V dO^T (a lane owns a row), then
+//                    dQ^T += K^T dS^T.
+// Rows are packed as in the forward: row r of a (b, kv head h) is query r / G
+// of head h*G + r % G.  Every reduction has a fixed order.
+#include "h2o_device.h"
+#include "h2o_launch.h"
+#include "h2o_tiles.h"
+
+namespace h2o {
+namespace {
+
+// ---------------------------------------------------------------------------
+// prep: L2 = lse * log2(e) and D = dO . O per packed row
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256) void bwd_prep_kernel(const BwdGeom g,
+                                                      const float* __restrict__ out,
+                                                      const float* __restrict__ lse,
+                                                      const uint16_t* __restrict__ dout,
+                                                      float* __restrict__ l2,
+                                                      float* __restrict__ drow) {
+    constexpr int LPR = D / 8;   // lanes per row, 8 elements each (consecutive lanes)
+    const long row = ((long)blockIdx.x * 256 + threadIdx.x) / LPR;
+    const int part = threadIdx.x % LPR;
+    const long total = (long)g.B * g.Hkv * g.R;
+    const bool ok = row < total;
+    float acc = 0.f;
+    size_t head_row = 0;
+    if (ok) {
+        const int bh = (int)(row / g.R), r = (int)(row % g.R);
+        const int b = bh / g.Hkv, h = bh % g.Hkv;
+        head_row = ((size_t)b * g.Hq + (size_t)h * g.G + r % g.G) * g.S + r / g.G;
+        const float* o = out + head_row * D + part * 8;
+        const f32x4 o0 = *(const f32x4*)o, o1 = *(const f32x4*)(o + 4);
+        const bf16x8 d8 = as_bf16x8(*(const u32x4*)(dout + head_row * D + part * 8));
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc = fmaf((float)d8[e], o0[e], acc);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc = fmaf((float)d8[4 + e], o1[e], acc);
+    }
+#pragma unroll
+    for (int off = 1; off < LPR; off <<= 1) acc += __shfl_xor(acc, off, 64);
+    if (ok && part == 0) {
+        drow[row] = acc;
+        l2[row] = lse[head_row] * kLog2e;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// shared pieces of the two main kernels
+// ---------------------------------------------------------------------------
+constexpr int BR = 32;   // rows per row block / keys per key block
+
+// One 4-byte HBM -> LDS copy per lane (global_load_lds_dword): lane l writes
+// bytes [4*l, 4*l + 4) past the wave-uniform LDS address `lds`.  As with the
+// 16-byte copy, written as asm without register outputs; completion is
+// awaited with wait_tiles() before the barrier that publishes the data.
+__device__ __forceinline__ void dma4(const float* gptr, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, off"
+                 :
+                 : "s"(lds), "v"(gptr)
+                 : "memory", "m0");
+}
+
+// Copy packed rows r0 .. r0+ROWS-1 of q or dO (base = the tensor at head
+// h*G, query 0) into a ROWS x D LDS tile with swizzle VT.  The rows of one
+// tile come from G different heads, so every 16-byte chunk computes its own
+// source; rows past R re-read row R-1 (a valid row whose weights are masked).
+template <int D, bool VT, int NW, int ROWS>
+__device__ __forceinline__ void issue_rows(uint16_t* tile, const uint16_t* __restrict__ base,
+                                           int r0, int R, int G, int S, int wave, int lane) {
+    constexpr int CPR = D / 8;
+    constexpr int ITER = ROWS * CPR / (NW * 64);
+    static_assert(ITER * NW * 64 == ROWS * CPR, "tile must split into whole 1 KiB blocks");
+    const uint32_t tb = __builtin_amdgcn_readfirstlane(lds_addr(tile));
+#pragma unroll
+    for (int it = 0; it < ITER; ++it) {
+        const int blk = it * NW + wave;
+        const int p = blk * 64 + lane;
+        const int row = p / CPR;
+        const int chunk = (p % CPR) ^ tile_swz<D, VT>(row);
+        const int gr = min(r0 + row, R - 1);
+        dma16(base + ((size_t)(gr % G) * S + gr / G) * D + chunk * 8, tb + blk * 1024);
+    }
+}
+
+// K (or V) fragments of one key of this lane as the B operand of an MFMA
+// whose k-dimension is the head dimension: dims 16*ks + 8*half + [0, 8) of
+// `row` (zeros when the key does not exist).
+template <int D>
+__device__ __forceinline__ void load_key_frags(bf16x8 (&f)[D / 16], const uint16_t* row, bool ok,
+                                               int half) {
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) {
+        u32x4 v = {0u, 0u, 0u, 0u};
+        if (ok) v = *(const u32x4*)(row + ks * 16 + half * 8);
+        f[ks] = as_bf16x8(v);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// dK, dV: key-major
+// ---------------------------------------------------------------------------
+constexpr int KV_WAVES = 4;                 // one wave per SIMD (up to 512 registers)
+constexpr int KV_NT = KV_WAVES * 64;
+// 32-key blocks per wave: each Q / dO fragment read feeds KB MFMAs; at D = 128
+// the K, V fragments and dK, dV accumulators of two blocks exceed 512 registers
+template <int D>
+constexpr int kv_kb() { return D == 128 ? 1 : 2; }
+template <int D>
+constexpr int kv_keys() { return KV_WAVES * kv_kb<D>() * BR; }   // keys per workgroup
+
+template <int D>
+__global__ __launch_bounds__(KV_NT, 1) void bwd_dkdv_kernel(
+    const BwdGeom g, const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc,
+    const uint16_t* __restrict__ vc, const uint16_t* __restrict__ kn,
+    const uint16_t* __restrict__ vn, const uint16_t* __restrict__ dout,
+    const float* __restrict__ l2, const float* __restrict__ drow, float* __restrict__ dkc,
+    float* __restrict__ dvc, float* __restrict__ dkn, float* __restrict__ dvn) {
+    constexpr int TILE = BR * D;            // elements of one row-block tile
+    constexpr int KV_KB = kv_kb<D>();
+    constexpr int KV_KEYS = kv_keys<D>();
+    // per buffer: Q (row-fragment swizzle), Q (transposed-read swizzle),
+    // dO (both swizzles), then L2 and D of the 32 rows
+    __shared__ __attribute__((aligned(16))) uint16_t tiles[2][4][TILE];
+    __shared__ __attribute__((aligned(16))) float stats[2][2 * BR];
+
+    const int n_ct = (g.C + KV_KEYS - 1) / KV_KEYS;   // cache key tiles (all C slots)
+    const int n_kt = n_ct + (g.S + KV_KEYS - 1) / KV_KEYS;
+    const int bh = blockIdx.x / n_kt, kt = blockIdx.x % n_kt;
+    const int b = bh / g.Hkv, h = bh % g.Hkv;
+    const bool chunk = kt >= n_ct;
+    const int key0 = (chunk ? kt - n_ct : kt) * KV_KEYS;   // first key of the tile
+    const int lim = chunk ? g.S : g.n;                     // keys that exist
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int half = lane >> 5, l32 = lane & 31;
+
+    // this lane's keys: key0 + wave*64 + kb*32 + l32
+    bf16x8 kf[KV_KB][D / 16], vf[KV_KB][D / 16];
+    int key[KV_KB];
+    bool kok[KV_KB];
+#pragma unroll
+    for (int kb = 0; kb < KV_KB; ++kb) {
+        key[kb] = key0 + wave * (KV_KB * BR) + kb * BR + l32;
+        kok[kb] = key[kb] < lim;
+        const size_t krow = chunk ? ((size_t)bh * g.S + key[kb]) * D : ((size_t)bh * g.C + key[kb]) * D;
+        load_key_frags<D>(kf[kb], (chunk ? kn : kc) + krow, kok[kb], half);
+        load_key_frags<D>(vf[kb], (chunk ? vn : vc) + krow, kok[kb], half);
+    }
+    f32x16 dk_acc[KV_KB][D / 32], dv_acc[KV_KB][D / 32];
+#pragma unroll
+    for (int kb = 0; kb < KV_KB; ++kb)
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) dk_acc[kb][db][v] = dv_acc[kb][db][v] = 0.f;
+
+    // rows that can see a key of this tile: all for cache slots (if any slot
+    // of the tile is valid), rows with query >= key0 for chunk keys
+    const int nrb = (g.R + BR - 1) / BR;
+    int rb0 = chunk ? (key0 * g.G) / BR : 0;
+    if (key0 >= lim) rb0 = nrb;             // no valid key: gradients stay 0
+    const uint16_t* q_h = q + ((size_t)b * g.Hq + (size_t)h * g.G) * g.S * D;
+    const uint16_t* do_h = dout + ((size_t)b * g.Hq + (size_t)h * g.G) * g.S * D;
+    const float* l2_bh = l2 + (size_t)bh * g.R;
+    const float* dr_bh = drow + (size_t)bh * g.R;
+
+    auto issue = [&](int rb, int buf) {
+        const int r0 = rb * BR;
+        issue_rows<D, false, KV_WAVES, BR>(tiles[buf][0], q_h, r0, g.R, g.G, g.S, wave, lane);
+        issue_rows<D, true, KV_WAVES, BR>(tiles[buf][1], q_h, r0, g.R, g.G, g.S, wave, lane);
+        issue_rows<D, false, KV_WAVES, BR>(tiles[buf][2], do_h, r0, g.R, g.G, g.S, wave, lane);
+        issue_rows<D, true, KV_WAVES, BR>(tiles[buf][3], do_h, r0, g.R, g.G, g.S, wave, lane);
+        if (wave == 0) {   // lanes 0-31: L2 of rows r0.., lanes 32-63: D
+            const int gr = min(r0 + l32, g.R - 1);
+            dma4((half ? dr_bh : l2_bh) + gr,
+                 __builtin_amdgcn_readfirstlane(lds_addr(stats[buf])));
+        }
+    };
+
+    const LdsOffsets<D> off(lane);
+    const float c = g.c;
+    if (rb0 < nrb) issue(rb0, 0);
+    wait_tiles();
+    __syncthreads();
+    for (int rb = rb0; rb < nrb; ++rb) {
+        const int buf = (rb - rb0) & 1;
+        if (rb + 1 < nrb) issue(rb + 1, buf ^ 1);
+        const uint16_t* Qk = tiles[buf][0];
+        const uint16_t* Qv = tiles[buf][1];
+        const uint16_t* Ok = tiles[buf][2];
+        const uint16_t* Ov = tiles[buf][3];
+        const int r0 = rb * BR;
+
+        // S = Q K^T and dP = dO V^T for both key blocks: element v of a lane
+        // is row r0 + 8*(v/4) + 4*half + v%4 against the lane's key
+        f32x16 s[KV_KB], dp[KV_KB];
+#pragma unroll
+        for (int kb = 0; kb < KV_KB; ++kb)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) s[kb][v] = dp[kb][v] = 0.f;
+#pragma unroll
+        for (int ks = 0; ks < D / 16; ++ks) {
+            const bf16x8 qa = as_bf16x8(lds_read16(Qk, off.k[ks]));
+            const bf16x8 oa = as_bf16x8(lds_read16(Ok, off.k[ks]));
+#pragma unroll
+            for (int kb = 0; kb < KV_KB; ++kb) {
+                s[kb] = mfma32x32x16(qa, kf[kb][ks], s[kb]);
+                dp[kb] = mfma32x32x16(oa, vf[kb][ks], dp[kb]);
+            }
+        }
+
+        // P and dS (selects, so masked entries are exactly 0 whatever the
+        // arithmetic gives), in bf16 as the B operands of the row contraction
+        float l2v[16], drv[16];
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+            const f32x4 a = *(const f32x4*)&stats[buf][8 * g4 + 4 * half];
+            const f32x4 d = *(const f32x4*)&stats[buf][BR + 8 * g4 + 4 * half];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                l2v[4 * g4 + e] = a[e];
+                drv[4 * g4 + e] = d[e];
+            }
+        }
+        bf16x8 pf[KV_KB][2], sf[KV_KB][2];
+#pragma unroll
+        for (int kb = 0; kb < KV_KB; ++kb)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int row = r0 + acc_row(v, half);
+                const bool vis = kok[kb] && row < g.R && (!chunk || row / g.G >= key[kb]);
+                const float p = vis ? fast_exp2(fmaf(s[kb][v], c, -l2v[v])) : 0.f;
+                const float ds = vis ? p * (dp[kb][v] - drv[v]) : 0.f;
+                pf[kb][v >> 3][v & 7] = (__bf16)p;
+                sf[kb][v >> 3][v & 7] = (__bf16)ds;
+            }
+
+        // dV^T += dO^T P and dK^T += Q^T dS: k-step hs covers rows
+        // r0 + 16*hs + {4*half + [0,4), 8 + 4*half + [0,4)}, the rows the
+        // accumulator elements 8*hs .. 8*hs+7 hold
+#pragma unroll
+        for (int hs = 0; hs < 2; ++hs) {
+            const uint32_t row_b = (uint32_t)(16 * hs) * 2 * D;
+#pragma unroll
+            for (int db = 0; db < D / 32; ++db) {
+                const u32x2 olo = lds_read_tr(Ov, off.v[db] + row_b);
+                const u32x2 ohi = lds_read_tr(Ov, off.v[db] + row_b + 8 * 2 * D);
+                const u32x2 qlo = lds_read_tr(Qv, off.v[db] + row_b);
+                const u32x2 qhi = lds_read_tr(Qv, off.v[db] + row_b + 8 * 2 * D);
+                const bf16x8 ot = as_bf16x8(u32x4{olo[0], olo[1], ohi[0], ohi[1]});
+                const bf16x8 qt = as_bf16x8(u32x4{qlo[0], qlo[1], qhi[0], qhi[1]});
+#pragma unroll
+                for (int kb = 0; kb < KV_KB; ++kb) {
+                    dv_acc[kb][db] = mfma32x32x16(ot, pf[kb][hs], dv_acc[kb][db]);
+                    dk_acc[kb][db] = mfma32x32x16(qt, sf[kb][hs], dk_acc[kb][db]);
+                }
+            }
+        }
+        wait_tiles();
+        __syncthreads();
+    }
+
+    // dK = scale * (dK^T)^T, dV = (dV^T)^T: lane holds its key's dims
+    // 32*db + 8*gq + 4*half + [0, 4) in elements 4*gq .. 4*gq+3
+#pragma unroll
+    for (int kb = 0; kb < KV_KB; ++kb) {
+        if (key[kb] >= (chunk ? g.S : g.C)) continue;
+        const size_t row = chunk ? ((size_t)bh * g.S + key[kb]) * D : ((size_t)bh * g.C + key[kb]) * D;
+        float* dk = (chunk ? dkn : dkc) + row;
+        float* dv = (chunk ? dvn : dvc) + row;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+            for (int gq = 0; gq < 4; ++gq) {
+                const int d = db * 32 + 8 * gq + 4 * half;
+                *(f32x4*)(dk + d) = g.tau * f32x4{dk_acc[kb][db][4 * gq + 0], dk_acc[kb][db][4 * gq + 1],
+                                                  dk_acc[kb][db][4 * gq + 2], dk_acc[kb][db][4 * gq + 3]};
+                *(f32x4*)(dv + d) = f32x4{dv_acc[kb][db][4 * gq + 0], dv_acc[kb][db][4 * gq + 1],
+                                          dv_acc[kb][db][4 * gq + 2], dv_acc[kb][db][4 * gq + 3]};
+            }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// dQ: row-major
+// ---------------------------------------------------------------------------
+constexpr int Q_WAVES = 8;
+constexpr int Q_NT = Q_WAVES * 64;
+constexpr int Q_ROWS = Q_WAVES * BR;        // rows per workgroup
+constexpr int Q_KT = 64;                    // keys per tile
+
+template <int D>
+__global__ __launch_bounds__(Q_NT, 1) void bwd_dq_kernel(
+    const BwdGeom g, const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc,
+    const uint16_t* __restrict__ vc, const uint16_t* __restrict__ kn,
+    const uint16_t* __restrict__ vn, const uint16_t* __restrict__ dout,
+    const float* __restrict__ l2, const float* __restrict__ drow, const int nsplit,
+    float* __restrict__ dq, float* __restrict__ dq_part) {
+    constexpr int TILE = Q_KT * D;
+    // per buffer: K (row-fragment swizzle), K (transposed-read swizzle), V (row fragments)
+    __shared__ __attribute__((aligned(16))) uint16_t tiles[2][3][TILE];
+
+    const int n_rt = (g.R + Q_ROWS - 1) / Q_ROWS;
+    int rt, bh, split;
+    decode_block(n_rt, nsplit, rt, bh, split);
+    const int b = bh / g.Hkv, h = bh % g.Hkv;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int half = lane >> 5, l32 = lane & 31;
+    const int r = rt * Q_ROWS + wave * BR + l32;     // this lane's packed row
+    const bool rok = r < g.R;
+    const int rr = rok ? r : g.R - 1;
+    const int i = rr / g.G;                          // its query
+    const size_t head_row = ((size_t)b * g.Hq + (size_t)h * g.G + rr % g.G) * g.S + i;
+
+    // Q and dO fragments of the row: B operands of S^T = K Q^T and dP^T = V dO^T
+    bf16x8 qf[D / 16], of[D / 16];
+    load_key_frags<D>(qf, q + head_row * D, rok, half);
+    load_key_frags<D>(of, dout + head_row * D, rok, half);
+    const float l2r = l2[(size_t)bh * g.R + rr];
+    const float drr = drow[(size_t)bh * g.R + rr];
+
+    // key tiles: the n valid cache slots, then the chunk keys up to the last
+    // query of this row tile
+    const int n_ct = (g.n + Q_KT - 1) / Q_KT;
+    const int r_last = min((rt + 1) * Q_ROWS, g.R) - 1;
+    const int total = n_ct + (r_last / g.G) / Q_KT + 1;
+    const int t_begin = (int)((long)split * total / nsplit);
+    const int t_end = (int)((long)(split + 1) * total / nsplit);
+    const uint16_t* kc_bh = kc + (size_t)bh * g.C * D;
+    const uint16_t* vc_bh = vc + (size_t)bh * g.C * D;
+    const uint16_t* kn_bh = kn + (size_t)bh * g.S * D;
+    const uint16_t* vn_bh = vn + (size_t)bh * g.S * D;
+    auto issue = [&](int t, int buf) {
+        const bool ch = t >= n_ct;
+        const int k0 = ch ? (t - n_ct) * Q_KT : t * Q_KT;
+        const int lim = ch ? g.S : g.n;
+        issue_tile<D, false, Q_WAVES, Q_KT>(tiles[buf][0], ch ? kn_bh : kc_bh, k0, lim, wave, lane);
+        issue_tile<D, true, Q_WAVES, Q_KT>(tiles[buf][1], ch ? kn_bh : kc_bh, k0, lim, wave, lane);
+        issue_tile<D, false, Q_WAVES, Q_KT>(tiles[buf][2], ch ? vn_bh : vc_bh, k0, lim, wave, lane);
+    };
+
+    f32x16 acc[D / 32];
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[db][v] = 0.f;
+    const LdsOffsets<D> off(lane);
+    const float c = g.c;
+    if (t_begin < t_end) issue(t_begin, 0);
+    wait_tiles();
+    __syncthreads();
+    for (int t = t_begin; t < t_end; ++t) {
+        const int buf = (t - t_begin) & 1;
+        if (t + 1 < t_end) issue(t + 1, buf ^ 1);
+        const bool ch = t >= n_ct;
+        const int k0 = ch ? (t - n_ct) * Q_KT : t * Q_KT;
+        const int lim = ch ? g.S : g.n;
+        const uint16_t* Kk = tiles[buf][0];
+        const uint16_t* Kv = tiles[buf][1];
+        const uint16_t* Vk = tiles[buf][2];
+#pragma unroll
+        for (int kb = 0; kb < Q_KT / BR; ++kb) {
+            // S^T = K Q^T and dP^T = V dO^T: element v is key
+            // k0 + 32*kb + 8*(v/4) + 4*half + v%4 against this lane's row
+            f32x16 s, dp;
+#pragma unroll
+            for (int v = 0; v < 16; ++v) s[v] = dp[v] = 0.f;
+#pragma unroll
+            for (int ks = 0; ks < D / 16; ++ks) {
+                const bf16x8 ka = as_bf16x8(lds_read16(Kk, off.k[ks] + kb * BR * 2 * D));
+                const bf16x8 va = as_bf16x8(lds_read16(Vk, off.k[ks] + kb * BR * 2 * D));
+                s = mfma32x32x16(ka, qf[ks], s);
+                dp = mfma32x32x16(va, of[ks], dp);
+            }
+            bf16x8 sf[2];
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int kk = k0 + kb * BR + acc_row(v, half);
+                const bool vis = rok && kk < lim && (!ch || kk <= i);
+                const float p = vis ? fast_exp2(fmaf(s[v], c, -l2r)) : 0.f;
+                const float ds = vis ? p * (dp[v] - drr) : 0.f;
+                sf[v >> 3][v & 7] = (__bf16)ds;
+            }
+            // dQ^T += K^T dS^T
+#pragma unroll
+            for (int hs = 0; hs < 2; ++hs) {
+                const uint32_t row_b = (uint32_t)(kb * BR + 16 * hs) * 2 * D;
+#pragma unroll
+                for (int db = 0; db < D / 32; ++db) {
+                    const u32x2 lo = lds_read_tr(Kv, off.v[db] + row_b);
+                    const u32x2 hi = lds_read_tr(Kv, off.v[db] + row_b + 8 * 2 * D);
+                    acc[db] = mfma32x32x16(as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]}),
+                                           sf[hs], acc[db]);
+                }
+            }
+        }
+        wait_tiles();
+        __syncthreads();
+    }
+    if (!rok) return;
+    // one key split: dQ itself; several: this split's partial (scaled later)
+    const float sc = nsplit == 1 ? g.tau : 1.f;
+    float* dqr = (nsplit == 1 ? dq : dq_part + (size_t)split * g.B * g.Hq * g.S * D) + head_row * D;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int gq = 0; gq < 4; ++gq) {
+            const int d = db * 32 + 8 * gq + 4 * half;
+            *(f32x4*)(dqr + d) = sc * f32x4{acc[db][4 * gq + 0], acc[db][4 * gq + 1],
+                                            acc[db][4 * gq + 2], acc[db][4 * gq + 3]};
+        }
+}
+
+// dQ = scale * (sum of the key splits' partials, in split order)
+__global__ __launch_bounds__(256) void bwd_dq_reduce_kernel(const float* __restrict__ part,
+                                                           int nsplit, long n4, float tau,
+                                                           float* __restrict__ dq) {
+    for (long i = (long)blockIdx.x * 256 + threadIdx.x; i < n4; i += (long)gridDim.x * 256) {
+        f32x4 acc = ((const f32x4*)part)[i];
+        for (int sp = 1; sp < nsplit; ++sp) acc += ((const f32x4*)part)[sp * n4 + i];
+        ((f32x4*)dq)[i] = tau * acc;
+    }
+}
+
+// Key splits of the query-major kernel: enough workgroups for the 256 CUs,
+// at least 4 key tiles each; a function of the shape only (n = C assumed).
+int bwd_dq_splits(const BwdGeom& g) {
+    const int base = g.B * g.Hkv * ((g.R + Q_ROWS - 1) / Q_ROWS);
+    const int max_tiles = (g.C + Q_KT - 1) / Q_KT + (g.S + Q_KT - 1) / Q_KT;
+    int sp = (256 + base - 1) / base;
+    sp = sp > 4 ? 4 : sp;
+    const int cap = max_tiles / 4 < 1 ? 1 : max_tiles / 4;
+    return sp > cap ? cap : sp;
+}
+
+template <int D>
+hipError_t launch_bwd_d(const BwdGeom& g, const uint16_t* q, const uint16_t* kc,
+                        const uint16_t* vc, const uint16_t* kn, const uint16_t* vn,
+                        const float* out, const float* lse, const uint16_t* dout, float* dq,
+                        float* dkc, float* dvc, float* dkn, float* dvn, void* ws,
+                        hipStream_t stream, bool sync_debug, hipEvent_t* ev) {
+    const int BH = g.B * g.Hkv;
+    float* l2 = (float*)ws;
+    float* drow = l2 + bwd_rows_padded(g);
+    hipError_t err;
+#define H2O_CHECK()                                  \
+    do {                                             \
+        err = hipGetLastError();                     \
+        if (err != hipSuccess) return err;           \
+        if (sync_debug) {                            \
+            err = hipStreamSynchronize(stream);      \
+            if (err != hipSuccess) return err;       \
+        }                                            \
+    } while (0)
+#define H2O_EVENT(i)                                                               \
+    do {                                                                           \
+        if (ev && (err = hipEventRecord(ev[i], stream)) != hipSuccess) return err; \
+    } while (0)
+    H2O_EVENT(0);
+    {
+        const long threads = (long)BH * g.R * (D / 8);
+        hipLaunchKernelGGL(bwd_prep_kernel<D>, dim3((unsigned)((threads + 255) / 256)), dim3(256),
+                           0, stream, g, out, lse, dout, l2, drow);
+        H2O_CHECK();
+    }
+    H2O_EVENT(1);
+    {
+        constexpr int KV_KEYS = kv_keys<D>();
+        const int n_kt = (g.C + KV_KEYS - 1) / KV_KEYS + (g.S + KV_KEYS - 1) / KV_KEYS;
+        hipLaunchKernelGGL(bwd_dkdv_kernel<D>, dim3(BH * n_kt), dim3(KV_NT), 0, stream, g, q, kc,
+                           vc, kn, vn, dout, l2, drow, dkc, dvc, dkn, dvn);
+        H2O_CHECK();
+    }
+    H2O_EVENT(2);
+    {
+        const int n_rt = (g.R + Q_ROWS - 1) / Q_ROWS;
+        const int nsplit = bwd_dq_splits(g);
+        float* part = drow + bwd_rows_padded(g);
+        hipLaunchKernelGGL(bwd_dq_kernel<D>, dim3(BH * n_rt * nsplit), dim3(Q_NT), 0, stream, g,
+                           q, kc, vc, kn, vn, dout, l2, drow, nsplit, dq, part);
+        H2O_CHECK();
+        if (nsplit > 1) {
+            const long n4 = (long)g.B * g.Hq * g.S * D / 4;
+            long blocks = (n4 + 255) / 256;
+            if (blocks > 8192) blocks = 8192;
+            hipLaunchKernelGGL(bwd_dq_reduce_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
+                               part, nsplit, n4, g.tau, dq);
+            H2O_CHECK();
+        }
+    }
+    H2O_EVENT(3);
+    H2O_EVENT(4);
+#undef H2O_CHECK
+#undef H2O_EVENT
+    return hipSuccess;
+}
+
+}  // namespace
+
+size_t bwd_rows_padded(const BwdGeom& g) {
+    const size_t rows = (size_t)g.B * g.Hkv * g.R;
+    return (rows + 63) & ~(size_t)63;
+}
+
+size_t bwd_workspace_bytes(const BwdGeom& g) {
+    const int nsplit = bwd_dq_splits(g);
+    const size_t part = nsplit > 1 ? (size_t)nsplit * g.B * g.Hq * g.S * g.D : 0;
+    return (2 * bwd_rows_padded(g) + part) * sizeof(float);
+}
+
+hipError_t launch_attention_bwd(const BwdGeom& g, const uint16_t* q, const uint16_t* kc,
+                                const uint16_t* vc, const uint16_t* kn, const uint16_t* vn,
+                                const float* out, const float* lse, const uint16_t* dout,
+                                float* dq, float* dkc, float* dvc, float* dkn, float* dvn,
+                                void* ws, hipStream_t stream, bool sync_debug,
+                                hipEvent_t* ev5) {
+    if (g.D == 64)
+        return launch_bwd_d<64>(g, q, kc, vc, kn, vn, out, lse, dout, dq, dkc, dvc, dkn, dvn, ws,
+                                stream, sync_debug, ev5);
+    return launch_bwd_d<128>(g, q, kc, vc, kn, vn, out, lse, dout, dq, dkc, dvc, dkn, dvn, ws,
+                             stream, sync_debug, ev5);
+}
+
+}  // namespace h2o

@@ -41,6 +41,23 @@ hipError_t launch_attention(const AttnPlan& plan, const uint16_t* q,
                             hipStream_t stream, bool sync_debug,
                             hipEvent_t* ev5 /* nullable: 5 timing events */);
 
+// Backward of the attention (bwd.hip).
+struct BwdGeom {
+    int B, Hq, Hkv, G, D, C, S, n;
+    int R;          // G * S packed rows per (b, kv head)
+    float c;        // logit scale * log2(e)
+    float tau;      // logit scale
+};
+
+size_t bwd_rows_padded(const BwdGeom& g);
+size_t bwd_workspace_bytes(const BwdGeom& g);
+hipError_t launch_attention_bwd(const BwdGeom& g, const uint16_t* q, const uint16_t* kc,
+                                const uint16_t* vc, const uint16_t* kn, const uint16_t* vn,
+                                const float* out, const float* lse, const uint16_t* dout,
+                                float* dq, float* dkc, float* dvc, float* dkn, float* dvn,
+                                void* ws, hipStream_t stream, bool sync_debug,
+                                hipEvent_t* ev5 /* nullable: 5 timing events */);
+
 hipError_t launch_score_accumulate(int BH, int C, int S, int n, float* scores,
                                    float* new_scores, const float* wsum,
                                    hipStream_t stream);

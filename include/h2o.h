@@ -148,6 +148,37 @@ h2o_status_t kv_scatter(const h2o_shape_t* shape, uint16_t* k_cache,
                         const float* new_scores, const int32_t* evict_idx,
                         int64_t p0, void* stream);
 
+/* Backward of step 1 with the slot layout fixed: gradients of `out` of
+ * h2o_attn_chunk with respect to q and to the keys and values it attended to.
+ * ([LtF] Chinese page abstract and §1: the paper's fine-tuning computes
+ * gradients through the sparse attention with the KV cache policy in place;
+ * the eviction decisions that produced the slot layout are discrete and are
+ * not differentiated.)  With P the forward's normalised weights:
+ *   dP = dO V^T,  D = rowsum(dO * O),  dS = P * (dP - D),
+ *   dq = scale * dS K,  dk = scale * dS^T q,  dv = P^T dO,
+ * the G query heads of a KV head summed into its key and value gradients.
+ *   q, k_cache, v_cache, k_new, v_new   as for h2o_attn_chunk (same shape,
+ *                                 same n_valid: the forward's inputs)
+ *   out      [B, Hq, S, D]   fp32  the forward's output
+ *   lse      [B, Hq, S]      fp32  the forward's log-sum-exp (required here)
+ *   dout     [B, Hq, S, D]   bf16  upstream gradient of out
+ *   dq       [B, Hq, S, D]   fp32  written
+ *   dk_cache, dv_cache [B, Hkv, C, D] fp32  written; 0 for slots >= n_valid
+ *   dk_new,   dv_new   [B, Hkv, S, D] fp32  written
+ *   ws, ws_bytes                   device workspace of at least
+ *                                  h2o_attn_bwd_workspace_size(shape) bytes,
+ *                                  256-byte aligned; contents are scratch.
+ * Every output element is written.  Reductions run in a fixed order:
+ * repeated calls give bit-identical results. */
+size_t h2o_attn_bwd_workspace_size(const h2o_shape_t* shape);
+h2o_status_t h2o_attn_chunk_bwd(const h2o_shape_t* shape, const uint16_t* q,
+                                const uint16_t* k_cache, const uint16_t* v_cache,
+                                const uint16_t* k_new, const uint16_t* v_new,
+                                const float* out, const float* lse,
+                                const uint16_t* dout, float* dq, float* dk_cache,
+                                float* dv_cache, float* dk_new, float* dv_new,
+                                void* ws, size_t ws_bytes, void* stream);
+
 /* Diagnostics: per-kernel timing of h2o_attn_chunk with HIP events.
  * h2o_timing_start(max_calls) creates 5 * max_calls events (call it outside
  * any timed or captured region); until h2o_timing_stop, each h2o_attn_chunk
@@ -156,8 +187,10 @@ h2o_status_t kv_scatter(const h2o_shape_t* shape, uint16_t* k_cache,
  * summed-weight partials; partial reduction), for the first max_calls calls.
  * h2o_timing_stop(ms, calls) waits for the last recorded event, writes the
  * summed milliseconds of the four kernels to ms[0..3] and the number of timed
- * calls to *calls, and destroys the events.  Not thread-safe; meant for one
- * benchmarking thread. */
+ * calls to *calls, and destroys the events.  h2o_attn_chunk_bwd calls are
+ * timed the same way, with ms[0..2] its three kernels (row statistics; key,
+ * value gradients; query gradients) and ms[3] = 0.  Not thread-safe; meant
+ * for one benchmarking thread. */
 h2o_status_t h2o_timing_start(int32_t max_calls);
 h2o_status_t h2o_timing_stop(double* ms, int32_t* calls);
 

@@ -125,3 +125,30 @@ def test_workspace_checks(lib):
     assert lib.h2o_attn_chunk(ctypes.byref(sh), *([A] * 8), A, need - 1, None) == _lib.H2O_ERR_WORKSPACE
     assert lib.h2o_attn_chunk(ctypes.byref(sh), *([A] * 8), ctypes.c_void_p(4096 + 16), need,
                               None) == _lib.H2O_ERR_WORKSPACE
+
+
+def test_backward_argument_checks(lib):
+    sh = _shape()
+    A = ctypes.c_void_p(4096)
+    M = ctypes.c_void_p(4098)
+    N = ctypes.c_void_p(None)
+    need = lib.h2o_attn_bwd_workspace_size(ctypes.byref(sh))
+    assert need > 0 and need % 256 == 0
+    assert need == lib.h2o_attn_bwd_workspace_size(ctypes.byref(_shape(n_valid=0)))
+    # every tensor pointer is required and must be 16-byte aligned
+    for k in range(13):
+        for bad in (N, M):
+            args = [A] * 13
+            args[k] = bad
+            st = lib.h2o_attn_chunk_bwd(ctypes.byref(sh), *args, A, need, None)
+            assert st == _lib.H2O_ERR_INVALID_ARG, (k, bad)
+    assert lib.h2o_attn_chunk_bwd(ctypes.byref(sh), *([A] * 13), None, need,
+                                  None) == _lib.H2O_ERR_WORKSPACE
+    assert lib.h2o_attn_chunk_bwd(ctypes.byref(sh), *([A] * 13), A, need - 1,
+                                  None) == _lib.H2O_ERR_WORKSPACE
+    bad = _shape(head_dim=96)
+    assert lib.h2o_attn_bwd_workspace_size(ctypes.byref(bad)) == 0
+    assert lib.h2o_attn_chunk_bwd(ctypes.byref(bad), *([A] * 13), A, need,
+                                  None) == _lib.H2O_ERR_UNSUPPORTED
+    assert lib.h2o_attn_chunk_bwd(ctypes.byref(_shape(n_q_heads=12)), *([A] * 13), A, need,
+                                  None) == _lib.H2O_ERR_INVALID_ARG
