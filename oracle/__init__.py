@@ -4,7 +4,8 @@ Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
 ``bench.py`` may import this package.  The HIP library never does.
 """
 from .h2o_oracle import (attention_chunk, attention_chunk_backward, score_accumulate,
-                         evict_select, kv_scatter, h2o_step)
+                         evict_select, kv_scatter, h2o_step, snapkv_keep,
+                         snapkv_compact)
 
 __all__ = ["attention_chunk", "attention_chunk_backward", "score_accumulate",
-           "evict_select", "kv_scatter", "h2o_step"]
+           "evict_select", "kv_scatter", "h2o_step", "snapkv_keep", "snapkv_compact"]

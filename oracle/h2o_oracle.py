@@ -40,6 +40,11 @@ reading, listed here and implemented below:
       goes to the t-th of them;
   R10 positions are absolute token indices; -1 marks an empty slot.
 
+  R17 SnapKV-style one-shot choice: made once, from the summed weights of
+      one observation chunk (the window) over the cache slots; the lowest
+      (weight, slot) slots beyond the budget are dropped in R8's order, the
+      kept slots are compacted in slot order and the window is appended.
+
 The backward of the attention with the slot layout fixed
 (``attention_chunk_backward``) follows [LtF-zh] abstract and §1: the paper's
 fine-tuning computes gradients through the sparse attention with the cache
@@ -231,6 +236,66 @@ def kv_scatter(k_cache, v_cache, scores, pos, k_new, v_new, new_scores,
                 v_cache[b, h, j] = v_new[b, h, t]
                 scores[b, h, j] = new_scores[b, h, t]
                 pos[b, h, j] = p0 + t
+
+
+# ---------------------------------------------------------------------------
+# SnapKV-style one-shot choice from the same summed weights
+# ---------------------------------------------------------------------------
+def snapkv_keep(wsum, n_valid, budget):
+    """The `budget` cache slots each (batch, KV head) keeps when the choice is
+    made once, from one observation chunk's summed weights.
+
+    [LtF-zh] §2: SnapKV ranks cache entries by H2O-like summed attention
+    weights but decides only at one point of the generation.  Reading (R17):
+    the weights are the summed weights ``attention_chunk`` returns for the
+    window chunk, columns j < n_valid; the n_valid - budget slots with the
+    lowest (weight, slot) pairs are dropped -- the order of R8: equal weights
+    drop the lower slot first, -0.0 equals +0.0, NaN ranks last -- and the
+    rest are kept, listed in increasing slot order.
+    wsum [B, Hkv, C + S]; returns [B, Hkv, budget] int64.
+    """
+    B, Hkv, _ = wsum.shape
+    n = int(n_valid)
+    budget = int(budget)
+    drop = n - budget
+    out = np.empty((B, Hkv, budget), np.int64)
+    for b in range(B):
+        for h in range(Hkv):
+            # stable sort: equal weights keep slot order; NaN sorts last
+            order = np.argsort(wsum[b, h, :n], kind="stable")
+            out[b, h] = np.sort(order[drop:])
+    return out
+
+
+def snapkv_compact(k_cache, v_cache, pos, k_new, v_new, wsum, keep_idx, out_len, p0):
+    """The cache after a SnapKV choice, in a new cache of out_len slots (R17):
+    slot i < budget holds kept slot keep_idx[i] (its K, V, position and
+    summed weight), slot budget + t holds window token t (position p0 + t,
+    score = its own column, as R6), later slots are empty (position -1,
+    zeros).  Returns (k_out, v_out, pos_out, scores_out).
+    [LtF-zh] §1 (fixed slots) and §2 (SnapKV keeps the entries it chose).
+    """
+    B, Hkv, C, D = k_cache.shape
+    S = k_new.shape[2]
+    budget = keep_idx.shape[2]
+    k_out = np.zeros((B, Hkv, out_len, D), k_cache.dtype)
+    v_out = np.zeros((B, Hkv, out_len, D), v_cache.dtype)
+    pos_out = np.full((B, Hkv, out_len), -1, np.int64)
+    scores_out = np.zeros((B, Hkv, out_len), wsum.dtype)
+    for b in range(B):
+        for h in range(Hkv):
+            for i in range(budget):
+                j = int(keep_idx[b, h, i])
+                k_out[b, h, i] = k_cache[b, h, j]
+                v_out[b, h, i] = v_cache[b, h, j]
+                pos_out[b, h, i] = pos[b, h, j]
+                scores_out[b, h, i] = wsum[b, h, j]
+            for t in range(S):
+                k_out[b, h, budget + t] = k_new[b, h, t]
+                v_out[b, h, budget + t] = v_new[b, h, t]
+                pos_out[b, h, budget + t] = p0 + t
+                scores_out[b, h, budget + t] = wsum[b, h, C + t]
+    return k_out, v_out, pos_out, scores_out
 
 
 # ---------------------------------------------------------------------------
