@@ -326,6 +326,155 @@ def run_backward(args, wl):
     print(json.dumps(result), flush=True)
 
 
+def cpu_baseline_snapkv(wl):
+    """The oracle (float64) on one KV head of one layer of the SnapKV-style
+    one-shot choice (window attention over the prompt cache, keep choice,
+    compaction), scaled to window tokens/s of the whole workload."""
+    import numpy as np
+    import oracle
+    import synth
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = len(os.sched_getaffinity(0))
+    G = wl.group
+    sub = wl.with_(n_kv_heads=1, n_q_heads=G, batch=1)
+    st = synth.prefilled_state(sub)
+    ch = synth.gen_chunk(sub, 0, 0)
+    k, v = st.k, st.v
+    t0 = time.perf_counter()
+    _, _, wsum = oracle.attention_chunk(ch.q, k, v, ch.k, ch.v, st.n_valid)
+    keep = oracle.snapkv_keep(wsum, st.n_valid, wl.keep_budget)
+    oracle.snapkv_compact(k, v, st.pos, ch.k, ch.v, wsum, keep,
+                          wl.keep_budget + wl.chunk_len, ch.p0)
+    spent = time.perf_counter() - t0
+    total = spent * wl.n_kv_heads * wl.batch * wl.layers
+    return {"value": wl.chunk_len * wl.batch / total, "unit": "tokens/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": (f"one KV head ({G} query heads) of one layer: window attention over "
+                       f"{wl.cache_len} slots, keep choice, compaction; float64, {spent:.1f} s; "
+                       f"scaled x{wl.n_kv_heads * wl.batch} heads x{wl.layers} layers")}
+
+
+def run_snapkv(args, wl):
+    """Time the SnapKV-style one-shot choice at the end of a prompt, over all
+    layers: per layer the window chunk's attention over the prompt cache
+    (h2o_attn_chunk, unchanged), the keep choice and the compaction into a
+    cache of budget + S slots.  The input caches are not modified, so every
+    timed step repeats the same work."""
+    import torch
+    import h2o_kv_cache_amd as h2o
+    B, Hq, Hkv, D, C, S, L = (wl.batch, wl.n_q_heads, wl.n_kv_heads, wl.head_dim,
+                              wl.cache_len, wl.chunk_len, wl.layers)
+    budget = wl.keep_budget
+    out_len = budget + S
+    shape = h2o.Shape(B, Hq, Hkv, D, C, S, C)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(20261205)
+    layers = [make_layer_state(wl, gen) for _ in range(L)]
+    chunk = make_inputs(wl, 1, gen)[0]
+    out = torch.empty((B, Hq, S, D), dtype=torch.float32, device="cuda")
+    lse = torch.empty((B, Hq, S), dtype=torch.float32, device="cuda")
+    wsum = torch.empty((B, Hkv, C + S), dtype=torch.float32, device="cuda")
+    keep = torch.empty((B, Hkv, budget), dtype=torch.int32, device="cuda")
+    ws = torch.empty(h2o.h2o_workspace_size(shape), dtype=torch.uint8, device="cuda")
+    outs = [dict(k=torch.empty((B, Hkv, out_len, D), dtype=torch.bfloat16, device="cuda"),
+                 v=torch.empty((B, Hkv, out_len, D), dtype=torch.bfloat16, device="cuda"),
+                 pos=torch.empty((B, Hkv, out_len), dtype=torch.int64, device="cuda"),
+                 scores=torch.empty((B, Hkv, out_len), dtype=torch.float32, device="cuda"))
+            for _ in range(L)]
+    stream = torch.cuda.current_stream()
+    p0 = C
+
+    def attn(li):
+        q, kn, vn = chunk[li]
+        st = layers[li]
+        h2o.h2o_attn_chunk(shape, q, st["k"], st["v"], kn, vn, out, lse, wsum, ws, stream)
+
+    def select(li):
+        h2o.h2o_snapkv_select(shape, wsum, budget, keep, stream)
+
+    def compact(li):
+        q, kn, vn = chunk[li]
+        st, o = layers[li], outs[li]
+        h2o.h2o_snapkv_compact(shape, st["k"], st["v"], st["pos"], kn, vn, wsum, keep, budget,
+                               out_len, p0, o["k"], o["v"], o["pos"], o["scores"], stream)
+
+    def run_step():
+        for li in range(L):
+            attn(li)
+            select(li)
+            compact(li)
+
+    for _ in range(args.warmup):
+        run_step()
+    torch.cuda.synchronize()
+    h2o.h2o_timing_start(args.steps * L)
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_stop = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for _ in range(args.steps):
+        run_step()
+    t_stop.record(stream)
+    torch.cuda.synchronize()
+    kernel_ms, calls = h2o.h2o_timing_stop()
+    elapsed_ms = t_start.elapsed_time(t_stop)
+    ms_per_step = elapsed_ms / args.steps
+
+    # per-call times of the choice and the compaction (one untimed pass each,
+    # bracketed by events on the same stream; the wsum of the last layer)
+    part_ms = {}
+    for name, fn in (("snapkv_select", select), ("snapkv_compact", compact)):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for li in range(L):
+            fn(li)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        part_ms[name] = e0.elapsed_time(e1) / L
+
+    pairs = pairs_per_layer_step(B, Hq, C, S, C)
+    per_layer = {k: v / calls for k, v in kernel_ms.items()}
+    per_layer.update(part_ms)
+    fwd_ms = per_layer["attn_fwd"]
+    fwd_flop = 4.0 * D * pairs
+    roof = {"bound": "mfma", "achieved": fwd_flop / (fwd_ms * 1e-3) / 1e12,
+            "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "per_launch_flop": fwd_flop}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    # compaction moves budget + S rows of K and V per KV head (read + write)
+    cp_bytes = 2.0 * 2 * B * Hkv * out_len * D * 2
+    result = {
+        "metric": ("SnapKV-style one-shot choice at the end of a 128k prompt: window tokens/s "
+                   "(window attention + keep choice + compaction, all layers)"),
+        "value": B * S * args.steps / (elapsed_ms / 1e3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": wl.name, "batch": B, "q_heads": Hq, "kv_heads": Hkv, "head_dim": D,
+            "prompt_len": wl.seq_len, "cache_len": C, "window": S, "keep_budget": budget,
+            "out_len": out_len, "layers": L,
+            "ms_per_layer": per_layer,
+            "compact_gbs": cp_bytes / (part_ms["snapkv_compact"] * 1e-3) / 1e9,
+        },
+        "roofline": dict(kernel="attn_fwd_kernel<%d> (pass 1: QK^T, online softmax, PV)" % D,
+                         traffic=None, avg_launch_ms=fwd_ms, launches=calls, **roof),
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline_snapkv(wl)
+    print(json.dumps(result), flush=True)
+
+
 def main():
     args = parse()
     if args.summarize_stats:
@@ -353,6 +502,9 @@ def main():
     torch.cuda.set_device(0)
     if args.backward:
         run_backward(args, wl)
+        return
+    if wl.keep_budget > 0:
+        run_snapkv(args, wl)
         return
     B, Hq, Hkv, D, C, S, L = (wl.batch, wl.n_q_heads, wl.n_kv_heads, wl.head_dim,
                               wl.cache_len, wl.chunk_len, wl.layers)

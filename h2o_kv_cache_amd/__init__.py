@@ -31,7 +31,7 @@ from ._lib import H2OShape
 
 __all__ = ["Shape", "H2OError", "h2o_workspace_size", "h2o_attn_chunk",
            "h2o_score_accumulate", "h2o_evict_select", "kv_scatter",
-           "h2o_attn_bwd_workspace_size", "h2o_attn_chunk_bwd",
+           "h2o_snapkv_select", "h2o_snapkv_compact", "h2o_attn_bwd_workspace_size", "h2o_attn_chunk_bwd",
            "h2o_timing_start", "h2o_timing_stop", "h2o_status_string", "H2OCache",
            "load_library", "ATTN_KERNELS"]
 
@@ -170,6 +170,44 @@ def kv_scatter(shape: Shape, k_cache, v_cache, scores, pos, k_new, v_new, new_sc
         _ptr(evict_idx, "evict_idx", (B, Hkv, S), (torch.int32,)),
         ctypes.c_int64(int(p0)), _stream(stream)),
         "kv_scatter")
+
+
+def h2o_snapkv_select(shape: Shape, wsum, budget: int, keep_idx, stream=None):
+    s = shape
+    B, Hkv, C, S = s.batch, s.n_kv_heads, s.cache_len, s.chunk_len
+    sh = s.c()
+    keep = (ctypes.c_void_p(None) if keep_idx is None
+            else _ptr(keep_idx, "keep_idx", (B, Hkv, int(budget)), (torch.int32,)))
+    _check(_lib.load().h2o_snapkv_select(
+        ctypes.byref(sh), _ptr(wsum, "wsum", (B, Hkv, C + S), _F32),
+        ctypes.c_int32(int(budget)), keep, _stream(stream)),
+        "h2o_snapkv_select")
+
+
+def h2o_snapkv_compact(shape: Shape, k_cache, v_cache, pos, k_new, v_new, wsum, keep_idx,
+                       budget: int, out_len: int, p0: int, k_out, v_out, pos_out=None,
+                       scores_out=None, stream=None):
+    s = shape
+    B, Hkv, D, C, S = s.batch, s.n_kv_heads, s.head_dim, s.cache_len, s.chunk_len
+    L = int(out_len)
+    sh = s.c()
+    none = ctypes.c_void_p(None)
+    _check(_lib.load().h2o_snapkv_compact(
+        ctypes.byref(sh), _ptr(k_cache, "k_cache", (B, Hkv, C, D), _BF16),
+        _ptr(v_cache, "v_cache", (B, Hkv, C, D), _BF16),
+        none if pos is None else _ptr(pos, "pos", (B, Hkv, C), (torch.int64,)),
+        _ptr(k_new, "k_new", (B, Hkv, S, D), _BF16),
+        _ptr(v_new, "v_new", (B, Hkv, S, D), _BF16),
+        _ptr(wsum, "wsum", (B, Hkv, C + S), _F32),
+        none if keep_idx is None else _ptr(keep_idx, "keep_idx", (B, Hkv, int(budget)),
+                                           (torch.int32,)),
+        ctypes.c_int32(int(budget)), ctypes.c_int32(L), ctypes.c_int64(int(p0)),
+        _ptr(k_out, "k_out", (B, Hkv, L, D), _BF16),
+        _ptr(v_out, "v_out", (B, Hkv, L, D), _BF16),
+        none if pos_out is None else _ptr(pos_out, "pos_out", (B, Hkv, L), (torch.int64,)),
+        none if scores_out is None else _ptr(scores_out, "scores_out", (B, Hkv, L), _F32),
+        _stream(stream)),
+        "h2o_snapkv_compact")
 
 
 def h2o_attn_bwd_workspace_size(shape: Shape) -> int:

@@ -35,7 +35,7 @@ h2o_status_t check_shape(const h2o_shape_t* s) {
     if (s->n_valid < 0 || s->n_valid > s->cache_len) return H2O_ERR_INVALID_ARG;
     if (!(s->scale == s->scale)) return H2O_ERR_INVALID_ARG;   // NaN scale
     if (s->head_dim != 64 && s->head_dim != 128) return H2O_ERR_UNSUPPORTED;
-    if (s->cache_len > 65536) return H2O_ERR_UNSUPPORTED;   // slot choice holds keys in registers
+    if (s->cache_len > (1 << 20)) return H2O_ERR_UNSUPPORTED;   // in-head indices stay 32-bit
     // 32-bit index limits used inside the kernels
     const long long BH = (long long)s->batch * s->n_kv_heads;
     const long long W = (long long)s->cache_len + s->chunk_len;
@@ -46,6 +46,11 @@ h2o_status_t check_shape(const h2o_shape_t* s) {
 }
 
 h2o_status_t from_hip(hipError_t e) { return e == hipSuccess ? H2O_OK : H2O_ERR_HIP; }
+
+bool overlaps(const void* a, size_t a_bytes, const void* b, size_t b_bytes) {
+    const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+    return x < y + b_bytes && y < x + a_bytes;
+}
 
 // Event timing of the attention kernels (diagnostics, one thread).
 struct Timing {
@@ -136,6 +141,57 @@ h2o_status_t kv_scatter(const h2o_shape_t* s, uint16_t* k_cache, uint16_t* v_cac
     hipError_t e = h2o::launch_kv_scatter(s->batch * s->n_kv_heads, s->head_dim, s->cache_len,
                                           s->chunk_len, k_cache, v_cache, scores, pos, k_new,
                                           v_new, new_scores, evict_idx, p0,
+                                          (hipStream_t)stream);
+    if (e == hipSuccess && sync_debug()) e = hipStreamSynchronize((hipStream_t)stream);
+    return from_hip(e);
+}
+
+h2o_status_t h2o_snapkv_select(const h2o_shape_t* s, const float* wsum, int32_t budget,
+                               int32_t* keep_idx, void* stream) {
+    h2o_status_t st = check_shape(s);
+    if (st != H2O_OK) return st;
+    if (budget < 0 || budget > s->n_valid) return H2O_ERR_INVALID_ARG;
+    if (!wsum || (budget > 0 && !keep_idx)) return H2O_ERR_INVALID_ARG;
+    if (!aligned16(wsum) || (keep_idx && !aligned16(keep_idx))) return H2O_ERR_INVALID_ARG;
+    hipError_t e = h2o::launch_snapkv_select(s->batch * s->n_kv_heads, s->cache_len,
+                                             s->chunk_len, s->n_valid, budget, wsum, keep_idx,
+                                             (hipStream_t)stream);
+    if (e == hipSuccess && sync_debug()) e = hipStreamSynchronize((hipStream_t)stream);
+    return from_hip(e);
+}
+
+h2o_status_t h2o_snapkv_compact(const h2o_shape_t* s, const uint16_t* k_cache,
+                                const uint16_t* v_cache, const int64_t* pos,
+                                const uint16_t* k_new, const uint16_t* v_new, const float* wsum,
+                                const int32_t* keep_idx, int32_t budget, int32_t out_len,
+                                int64_t p0, uint16_t* k_out, uint16_t* v_out, int64_t* pos_out,
+                                float* scores_out, void* stream) {
+    h2o_status_t st = check_shape(s);
+    if (st != H2O_OK) return st;
+    if (budget < 0 || budget > s->n_valid) return H2O_ERR_INVALID_ARG;
+    if (out_len < 1 || out_len > (1 << 20) || (long long)budget + s->chunk_len > out_len)
+        return H2O_ERR_INVALID_ARG;
+    if (!k_cache || !v_cache || !k_new || !v_new || !wsum || !k_out || !v_out ||
+        (budget > 0 && !keep_idx) || (pos_out && !pos))
+        return H2O_ERR_INVALID_ARG;
+    if (p0 < 0) return H2O_ERR_INVALID_ARG;
+    if (!aligned16(k_cache) || !aligned16(v_cache) || !aligned16(k_new) || !aligned16(v_new) ||
+        !aligned16(k_out) || !aligned16(v_out) || !aligned16(wsum) ||
+        (keep_idx && !aligned16(keep_idx)) || (pos && !aligned16(pos)) ||
+        (pos_out && !aligned16(pos_out)) || (scores_out && !aligned16(scores_out)))
+        return H2O_ERR_INVALID_ARG;
+    const size_t BH = (size_t)s->batch * s->n_kv_heads, D = s->head_dim;
+    const size_t out_b = BH * out_len * D * 2, cache_b = BH * s->cache_len * D * 2,
+                 new_b = BH * s->chunk_len * D * 2;
+    const void* srcs[4] = {k_cache, v_cache, k_new, v_new};
+    const size_t src_b[4] = {cache_b, cache_b, new_b, new_b};
+    for (int i = 0; i < 4; ++i)
+        if (overlaps(k_out, out_b, srcs[i], src_b[i]) || overlaps(v_out, out_b, srcs[i], src_b[i]))
+            return H2O_ERR_INVALID_ARG;
+    if (overlaps(k_out, out_b, v_out, out_b)) return H2O_ERR_INVALID_ARG;
+    hipError_t e = h2o::launch_kv_compact((int)BH, s->head_dim, s->cache_len, s->chunk_len,
+                                          budget, out_len, k_cache, v_cache, pos, k_new, v_new,
+                                          wsum, keep_idx, p0, k_out, v_out, pos_out, scores_out,
                                           (hipStream_t)stream);
     if (e == hipSuccess && sync_debug()) e = hipStreamSynchronize((hipStream_t)stream);
     return from_hip(e);

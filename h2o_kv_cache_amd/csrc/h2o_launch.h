@@ -72,4 +72,16 @@ hipError_t launch_kv_scatter(int BH, int D, int C, int S, uint16_t* kc,
                              const float* new_scores, const int32_t* evict_idx,
                              int64_t p0, hipStream_t stream);
 
+// SnapKV one-shot choice: keep_idx[bh][0..budget) = the budget valid slots
+// (of n) that are not among the n - budget lowest (wsum, slot), ascending.
+// wsum rows are C + S floats.
+hipError_t launch_snapkv_select(int BH, int C, int S, int n, int budget, const float* wsum,
+                                int32_t* keep_idx, hipStream_t stream);
+
+hipError_t launch_kv_compact(int BH, int D, int C, int S, int budget, int out_len,
+                             const uint16_t* kc, const uint16_t* vc, const int64_t* pos,
+                             const uint16_t* kn, const uint16_t* vn, const float* wsum,
+                             const int32_t* keep_idx, int64_t p0, uint16_t* ko, uint16_t* vo,
+                             int64_t* pos_out, float* scores_out, hipStream_t stream);
+
 }  // namespace h2o

@@ -92,6 +92,36 @@ __device__ __forceinline__ void hist_add(uint32_t* hist, uint32_t bin, bool acti
     if (active && !same) atomicAdd(&hist[bin], 1u);
 }
 
+// Run by one wave (lanes 0-63): the bin of a 256-bin histogram that holds
+// rank k (1-based, counting from bin 0), and the rank inside that bin.
+__device__ __forceinline__ void find_bin(const uint32_t* hist, uint32_t k, uint32_t* sh_digit,
+                                         uint32_t* sh_k) {
+    const int lane = threadIdx.x & 63;
+    uint32_t h4[4], s4 = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        h4[e] = hist[lane * 4 + e];
+        s4 += h4[e];
+    }
+    uint32_t inc = s4;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const uint32_t y = __shfl_up(inc, off, 64);
+        if (lane >= off) inc += y;
+    }
+    uint32_t before = inc - s4;
+    if (before < k && k <= inc) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            if (before < k && k <= before + h4[e]) {
+                *sh_digit = (uint32_t)(lane * 4 + e);
+                *sh_k = k - before;
+            }
+            before += h4[e];
+        }
+    }
+}
+
 // One workgroup per (b, kv head).  Each thread holds the keys of a
 // contiguous run of KPT slots in registers.  Radix select (4 passes of 8
 // bits) finds the key T of the S-th smallest (key, slot) pair and how many
@@ -152,28 +182,7 @@ __global__ __launch_bounds__(SEL_T) void evict_select_kernel(
         for (int e = 0; e < KPT; ++e)
             hist_add(hist, (key[e] >> shift) & 255u, e < cnt && (key[e] & mask) == prefix);
         __syncthreads();
-        if (tid < 64) {   // one wave finds the bucket holding rank k
-            uint32_t h4[4], s4 = 0;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) { h4[e] = hist[tid * 4 + e]; s4 += h4[e]; }
-            uint32_t inc = s4;
-#pragma unroll
-            for (int off = 1; off < 64; off <<= 1) {
-                const uint32_t y = __shfl_up(inc, off, 64);
-                if (tid >= off) inc += y;
-            }
-            uint32_t before = inc - s4;
-            if (before < k && k <= inc) {
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    if (before < k && k <= before + h4[e]) {
-                        sh_digit = (uint32_t)(tid * 4 + e);
-                        sh_k = k - before;
-                    }
-                    before += h4[e];
-                }
-            }
-        }
+        if (tid < 64) find_bin(hist, k, &sh_digit, &sh_k);
         __syncthreads();
         prefix |= sh_digit << shift;
         mask |= 255u << shift;
@@ -203,6 +212,173 @@ __global__ __launch_bounds__(SEL_T) void evict_select_kernel(
         if (take) {
             if (o < (uint32_t)S) out[o] = j0 + e;   // never past the row, whatever the counts
             ++o;
+        }
+    }
+}
+
+// The same choice with the keys left in memory, for rows too long to hold in
+// registers (more than SEL_T * 64 slots) and for the SnapKV keep list.  Wave w
+// owns the contiguous slots [w*seg, (w+1)*seg) and walks them 64 at a time
+// with coalesced loads, re-reading the keys (from L2) in every pass.  Slot
+// order inside a 64-slot step comes from ballots, across steps from a running
+// count, across waves from a scan of the 16 wave totals.
+//   KEEP = false: out[0..k) = the k chosen slots (rows of `stride` floats,
+//                 n valid; the fill phase appends as above)
+//   KEEP = true : out[0..C-k) = the C - k slots not chosen (all C valid)
+// Both lists are in increasing slot order.
+constexpr int SEL_W = SEL_T / 64;
+
+template <bool KEEP>
+__global__ __launch_bounds__(SEL_T) void select_stream_kernel(
+    int C, int k, int n, const float* __restrict__ scores, long stride,
+    int32_t* __restrict__ out, long out_stride) {
+    __shared__ uint32_t hist[256];
+    __shared__ uint32_t sh_lt[SEL_W], sh_eq[SEL_W];
+    __shared__ uint32_t sh_digit, sh_k;
+
+    const int bh = blockIdx.x, tid = threadIdx.x, lane = tid & 63;
+    const int wave = tid >> 6;
+    const float* sc = scores + (size_t)bh * stride;
+    int32_t* o = out + (size_t)bh * out_stride;
+    const int n_out = KEEP ? C - k : k;
+
+    if (!KEEP && n + k <= C) {   // fill phase: append
+        for (int t = tid; t < k; t += SEL_T) o[t] = n + t;
+        return;
+    }
+    if (k == 0) {   // KEEP only: every slot stays
+        for (int j = tid; j < C; j += SEL_T) o[j] = j;
+        return;
+    }
+    const int seg = (C + SEL_T - 1) / SEL_T * 64;
+    const int s0 = min(C, wave * seg), s1 = min(C, s0 + seg);
+    const unsigned long long below = (1ull << lane) - 1ull;
+
+    uint32_t prefix = 0u, mask = 0u, kk = (uint32_t)k;
+    for (int pass = 0; pass < 4; ++pass) {
+        const int shift = 24 - 8 * pass;
+        for (int i = tid; i < 256; i += SEL_T) hist[i] = 0u;
+        __syncthreads();
+        for (int base = s0; base < s1; base += 256) {
+            uint32_t key[4];
+            bool in[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int j = base + 64 * u + lane;
+                in[u] = j < s1;
+                key[u] = in[u] ? slot_key(sc, j, n) : 0u;
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+                hist_add(hist, (key[u] >> shift) & 255u, in[u] && (key[u] & mask) == prefix);
+        }
+        __syncthreads();
+        if (tid < 64) find_bin(hist, kk, &sh_digit, &sh_k);
+        __syncthreads();
+        prefix |= sh_digit << shift;
+        mask |= 255u << shift;
+        kk = sh_k;
+        __syncthreads();
+    }
+    const uint32_t T = prefix;   // key of the k-th smallest; kk of its ties are taken
+
+    // per-wave counts below / at T, then the wave's share of the ties
+    uint32_t n_lt = 0, n_eq = 0;
+    for (int base = s0; base < s1; base += 64) {
+        const int j = base + lane;
+        const uint32_t key = j < s1 ? slot_key(sc, j, n) : 0u;
+        n_lt += (uint32_t)__popcll(__ballot(j < s1 && key < T));
+        n_eq += (uint32_t)__popcll(__ballot(j < s1 && key == T));
+    }
+    if (lane == 0) {
+        sh_lt[wave] = n_lt;
+        sh_eq[wave] = n_eq;
+    }
+    __syncthreads();
+    uint32_t eq_before = 0, taken = 0;
+    for (int w = 0; w < wave; ++w) {
+        const uint32_t e = sh_eq[w];
+        const uint32_t take_w = kk > eq_before ? min(kk - eq_before, e) : 0u;
+        taken += sh_lt[w] + take_w;
+        eq_before += e;
+    }
+    const uint32_t eq_take = kk > eq_before ? min(kk - eq_before, n_eq) : 0u;
+
+    uint32_t eq_seen = 0;
+    for (int base = s0; base < s1; base += 64) {
+        const int j = base + lane;
+        const bool in = j < s1;
+        const uint32_t key = in ? slot_key(sc, j, n) : 0u;
+        const unsigned long long eqm = __ballot(in && key == T);
+        const uint32_t eq_rank = eq_seen + (uint32_t)__popcll(eqm & below);
+        const bool take = in && (key < T || (key == T && eq_rank < eq_take));
+        const unsigned long long tm = __ballot(take);
+        const uint32_t t_below = taken + (uint32_t)__popcll(tm & below);
+        if (KEEP) {
+            const uint32_t idx = (uint32_t)j - t_below;   // slots before j not taken
+            if (in && !take && idx < (uint32_t)n_out) o[idx] = j;
+        } else {
+            if (take && t_below < (uint32_t)n_out) o[t_below] = j;
+        }
+        taken += (uint32_t)__popcll(tm);
+        eq_seen += (uint32_t)__popcll(eqm);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// SnapKV compaction: output slot i < budget <- kept input slot keep[i];
+// output slot budget + t <- chunk token t
+// ---------------------------------------------------------------------------
+// Each thread moves one 16-byte piece of a K or V row; a workgroup moves
+// CP_ROWS rows, CP_UNROLL pieces per thread in flight.
+constexpr int CP_UNROLL = 4;
+
+template <int D>
+__global__ __launch_bounds__(256) void kv_compact_kernel(
+    int C, int S, int budget, int out_len, const uint16_t* __restrict__ kc,
+    const uint16_t* __restrict__ vc, const int64_t* __restrict__ pos,
+    const uint16_t* __restrict__ kn, const uint16_t* __restrict__ vn,
+    const float* __restrict__ wsum, const int32_t* __restrict__ keep, int64_t p0,
+    uint16_t* __restrict__ ko, uint16_t* __restrict__ vo, int64_t* __restrict__ pos_out,
+    float* __restrict__ scores_out) {
+    constexpr int TPR = D / 8;                 // 16-byte pieces per row
+    constexpr int RPI = 256 / (2 * TPR);       // rows per unrolled step
+    constexpr int CP_ROWS = RPI * CP_UNROLL;   // rows per workgroup
+    const int bh = blockIdx.y, tid = threadIdx.x;
+    const int which = (tid / TPR) & 1, c = tid % TPR, r_in = tid / (2 * TPR);
+    const int total = budget + S;
+    u32x4 v[CP_UNROLL];
+    int dst[CP_UNROLL];
+#pragma unroll
+    for (int u = 0; u < CP_UNROLL; ++u) {
+        const int i = blockIdx.x * CP_ROWS + u * RPI + r_in;
+        dst[u] = -1;
+        if (i >= total) continue;
+        const uint16_t* src;
+        if (i < budget) {
+            const int slot = keep[(size_t)bh * budget + i];
+            if (slot < 0 || slot >= C) continue;   // out-of-range index: nothing written
+            src = (which ? vc : kc) + ((size_t)bh * C + slot) * D;
+        } else {
+            src = (which ? vn : kn) + ((size_t)bh * S + (i - budget)) * D;
+        }
+        v[u] = *(const u32x4*)(src + c * 8);
+        dst[u] = i;
+    }
+#pragma unroll
+    for (int u = 0; u < CP_UNROLL; ++u) {
+        if (dst[u] < 0) continue;
+        const int i = dst[u];
+        *(u32x4*)((which ? vo : ko) + ((size_t)bh * out_len + i) * D + c * 8) = v[u];
+        if (which == 0 && c == 0) {
+            const bool kept = i < budget;
+            const int slot = kept ? keep[(size_t)bh * budget + i] : 0;
+            if (pos_out)
+                pos_out[(size_t)bh * out_len + i] =
+                    kept ? pos[(size_t)bh * C + slot] : p0 + (i - budget);
+            if (scores_out)
+                scores_out[(size_t)bh * out_len + i] =
+                    wsum[(size_t)bh * (C + S) + (kept ? slot : C + (i - budget))];
         }
     }
 }
@@ -251,7 +427,10 @@ hipError_t launch_evict_select(int BH, int C, int S, int n, const float* scores,
                                int32_t* evict_idx, hipStream_t stream) {
     // keys per thread: the smallest supported run that covers C
     const int kpt = (C + SEL_T - 1) / SEL_T;
-    if (kpt <= 4)
+    if (kpt > 64)
+        hipLaunchKernelGGL(select_stream_kernel<false>, dim3(BH), dim3(SEL_T), 0, stream, C, S,
+                           n, scores, (long)C, evict_idx, (long)S);
+    else if (kpt <= 4)
         hipLaunchKernelGGL(evict_select_kernel<4>, dim3(BH), dim3(SEL_T), 0, stream, C, S, n,
                            scores, evict_idx);
     else if (kpt <= 16)
@@ -260,8 +439,34 @@ hipError_t launch_evict_select(int BH, int C, int S, int n, const float* scores,
     else if (kpt <= 64)
         hipLaunchKernelGGL(evict_select_kernel<64>, dim3(BH), dim3(SEL_T), 0, stream, C, S, n,
                            scores, evict_idx);
-    else
-        return hipErrorInvalidValue;   // rejected earlier by the shape check
+    return hipGetLastError();
+}
+
+hipError_t launch_snapkv_select(int BH, int C, int S, int n, int budget, const float* wsum,
+                                int32_t* keep_idx, hipStream_t stream) {
+    if (budget == 0) return hipSuccess;   // nothing is kept
+    hipLaunchKernelGGL(select_stream_kernel<true>, dim3(BH), dim3(SEL_T), 0, stream, n,
+                       n - budget, n, wsum, (long)C + S, keep_idx, (long)budget);
+    return hipGetLastError();
+}
+
+hipError_t launch_kv_compact(int BH, int D, int C, int S, int budget, int out_len,
+                             const uint16_t* kc, const uint16_t* vc, const int64_t* pos,
+                             const uint16_t* kn, const uint16_t* vn, const float* wsum,
+                             const int32_t* keep_idx, int64_t p0, uint16_t* ko, uint16_t* vo,
+                             int64_t* pos_out, float* scores_out, hipStream_t stream) {
+    const int total = budget + S;
+    if (D == 64) {
+        constexpr int ROWS = 256 / (2 * (64 / 8)) * CP_UNROLL;
+        hipLaunchKernelGGL(kv_compact_kernel<64>, dim3((total + ROWS - 1) / ROWS, BH), dim3(256),
+                           0, stream, C, S, budget, out_len, kc, vc, pos, kn, vn, wsum, keep_idx,
+                           p0, ko, vo, pos_out, scores_out);
+    } else {
+        constexpr int ROWS = 256 / (2 * (128 / 8)) * CP_UNROLL;
+        hipLaunchKernelGGL(kv_compact_kernel<128>, dim3((total + ROWS - 1) / ROWS, BH),
+                           dim3(256), 0, stream, C, S, budget, out_len, kc, vc, pos, kn, vn,
+                           wsum, keep_idx, p0, ko, vo, pos_out, scores_out);
+    }
     return hipGetLastError();
 }
 

@@ -40,7 +40,7 @@
  *     call then returns a non-zero status and touches no buffer.
  *     H2O_ERR_HIP means a launch failed (hipGetLastError after the launch).
  *     Faults inside kernels surface at the caller's next synchronisation.
- *   - Supported: head_dim in {64, 128}; 1 <= chunk_len <= cache_len <= 65536;
+ *   - Supported: head_dim in {64, 128}; 1 <= chunk_len <= cache_len <= 2^20;
  *     0 <= n_valid <= cache_len; n_q_heads a multiple of n_kv_heads.
  *   - Calls are asynchronous and stream-ordered; two calls that share buffers
  *     must be ordered by the caller (same stream or events).
@@ -147,6 +147,51 @@ h2o_status_t kv_scatter(const h2o_shape_t* shape, uint16_t* k_cache,
                         const uint16_t* k_new, const uint16_t* v_new,
                         const float* new_scores, const int32_t* evict_idx,
                         int64_t p0, void* stream);
+
+/* SnapKV-style one-shot choice ([LtF] Chinese page §2: SnapKV scores cache
+ * entries with H2O-like summed attention weights but makes the choice at a
+ * single point of the generation).  Reading used here: the choice is made
+ * once, from the summed weights that h2o_attn_chunk returns for one chunk --
+ * the observation window, typically the prompt's last S tokens -- over the
+ * n_valid cache slots holding the rest of the prompt.  Of those slots, the
+ * n_valid - budget with the lowest (weight, slot) pairs are dropped, in the
+ * same order as h2o_evict_select (equal weights drop the lower slot first,
+ * -0.0 equals +0.0, NaN ranks above +inf), and the rest are kept.
+ *   wsum     [B, Hkv, C + S] fp32  in: from h2o_attn_chunk with this shape
+ *   budget   0 <= budget <= n_valid
+ *   keep_idx [B, Hkv, budget] int32 out: the kept slots in increasing order
+ *            (may be NULL when budget == 0)
+ * Any cache_len allowed by the shape; rows are read from memory once per
+ * radix pass (no register limit on their length). */
+h2o_status_t h2o_snapkv_select(const h2o_shape_t* shape, const float* wsum,
+                               int32_t budget, int32_t* keep_idx, void* stream);
+
+/* The cache after a SnapKV choice, written to a separate output cache of
+ * out_len slots (out_len >= budget + S):
+ *   slot i < budget        <- input slot keep_idx[i]: K, V row, position
+ *                             pos[keep_idx[i]], score wsum[keep_idx[i]]
+ *   slot budget + t (t < S) <- chunk token t: k_new/v_new row, position
+ *                             p0 + t, score wsum[C + t] (its own column)
+ *   slots >= budget + S     not written.
+ * The caller continues with n_valid = budget + S on the output cache.
+ *   k_cache, v_cache [B, Hkv, C, D]       bf16  in (not modified)
+ *   pos              [B, Hkv, C]          int64 in (NULL only if pos_out is)
+ *   k_new, v_new     [B, Hkv, S, D]       bf16  the observation window
+ *   wsum             [B, Hkv, C + S]      fp32  the window's summed weights
+ *   keep_idx         [B, Hkv, budget]     int32 from h2o_snapkv_select; an
+ *                                         index outside [0, C) leaves its
+ *                                         output row unwritten
+ *   k_out, v_out     [B, Hkv, out_len, D] bf16  out; must not overlap any
+ *                                         input cache or chunk (checked)
+ *   pos_out          [B, Hkv, out_len]    int64 out, may be NULL
+ *   scores_out       [B, Hkv, out_len]    fp32  out, may be NULL */
+h2o_status_t h2o_snapkv_compact(const h2o_shape_t* shape, const uint16_t* k_cache,
+                                const uint16_t* v_cache, const int64_t* pos,
+                                const uint16_t* k_new, const uint16_t* v_new,
+                                const float* wsum, const int32_t* keep_idx,
+                                int32_t budget, int32_t out_len, int64_t p0,
+                                uint16_t* k_out, uint16_t* v_out, int64_t* pos_out,
+                                float* scores_out, void* stream);
 
 /* Backward of step 1 with the slot layout fixed: gradients of `out` of
  * h2o_attn_chunk with respect to q and to the keys and values it attended to.

@@ -51,6 +51,7 @@ class Workload:
     heavy_frac: float     # fraction of K rows scaled by heavy_scale
     heavy_scale: float
     prefilled: bool       # cache starts full (decode-shaped runs)
+    keep_budget: int = 0  # SnapKV-style one-shot runs: cache slots kept
 
     @property
     def group(self) -> int:
@@ -86,6 +87,12 @@ WORKLOADS = {
     # small chunks at 64k: C=8192, S=128 (the pages' 128-token setting), 36 layers
     "qwen3_4b_64k_s128": Workload("qwen3_4b_64k_s128", 5, 1, 32, 8, 128, 8192, 128,
                                   65536, 36, 1.0, 0.05, 4.0, False),
+    # SnapKV-style one-shot choice at the end of a 131072-token prompt: the
+    # cache holds the first 130048 prompt tokens (positions 0..130047), the
+    # last 1024 form the observation window (the chunk); 15360 slots are
+    # kept, so the compacted cache holds 16384 tokens like the 128k runs
+    "qwen3_4b_128k_snapkv": Workload("qwen3_4b_128k_snapkv", 6, 1, 32, 8, 128, 130048, 1024,
+                                     131072, 36, 1.0, 0.05, 4.0, True, 15360),
     # decode: 16 sequences, cache pre-filled, one token per step, 4096 steps
     "decode": Workload("decode", 4, 16, 32, 8, 128, 16384, 1, 4096, 1,
                        1.0, 0.05, 4.0, True),

@@ -74,7 +74,7 @@ def test_invalid_shapes_rejected(lib, bad):
     assert lib.kv_scatter(ctypes.byref(sh), P, P, P, P, P, P, P, P, 0, None) == _lib.H2O_ERR_INVALID_ARG
 
 
-@pytest.mark.parametrize("bad", [dict(head_dim=96), dict(cache_len=65537, n_valid=0)])
+@pytest.mark.parametrize("bad", [dict(head_dim=96), dict(cache_len=(1 << 20) + 1, n_valid=0)])
 def test_unsupported_shapes(lib, bad):
     sh = _shape(**bad)
     assert lib.h2o_workspace_size(ctypes.byref(sh)) == 0
@@ -152,3 +152,43 @@ def test_backward_argument_checks(lib):
                                   None) == _lib.H2O_ERR_UNSUPPORTED
     assert lib.h2o_attn_chunk_bwd(ctypes.byref(_shape(n_q_heads=12)), *([A] * 13), A, need,
                                   None) == _lib.H2O_ERR_INVALID_ARG
+
+
+def test_snapkv_argument_checks(lib):
+    sh = _shape(cache_len=8192, n_valid=8000, chunk_len=1024)
+    D, C, S, BH = 128, 8192, 1024, 8
+    A = ctypes.c_void_p(1 << 32)                       # input caches / chunk
+    O = ctypes.c_void_p((1 << 32) + (1 << 30))         # output cache, disjoint
+    O2 = ctypes.c_void_p((1 << 32) + (1 << 31))
+    M = ctypes.c_void_p((1 << 32) + 2)
+    N = ctypes.c_void_p(None)
+    I = _lib.H2O_ERR_INVALID_ARG
+    sel = lambda budget, w=A, k=A: lib.h2o_snapkv_select(ctypes.byref(sh), w, budget, k, None)
+    for budget in (-1, 8001):
+        assert sel(budget) == I
+    assert sel(10, w=N) == I and sel(10, w=M) == I
+    assert sel(10, k=N) == I and sel(10, k=M) == I
+    # budget 0 needs no keep list; a bad shape is rejected before anything else
+    assert lib.h2o_snapkv_select(ctypes.byref(_shape(head_dim=96)), A, 0, N,
+                                 None) == _lib.H2O_ERR_UNSUPPORTED
+
+    def comp(budget=4000, out_len=5024, k_out=O, v_out=O2, pos=A, pos_out=A, p0=8000,
+             ins=None):
+        ins = ins or [A] * 7   # k_cache, v_cache, pos, k_new, v_new, wsum, keep_idx
+        ins = list(ins)
+        ins[2] = pos
+        return lib.h2o_snapkv_compact(ctypes.byref(sh), *ins, budget, out_len, p0, k_out, v_out,
+                                      pos_out, N, None)
+    assert comp(out_len=5023) == I          # budget + S > out_len
+    assert comp(budget=8001) == I
+    assert comp(p0=-1) == I
+    assert comp(pos=N, pos_out=A) == I      # positions out need positions in
+    for k in (0, 1, 3, 4, 5, 6):
+        for bad in (N, M):
+            ins = [A] * 7
+            ins[k] = bad
+            assert comp(ins=ins) == I, (k, bad)
+    assert comp(k_out=N) == I and comp(v_out=M) == I
+    # the output cache may not overlap an input (k_out placed on the chunk rows)
+    assert comp(k_out=A) == I
+    assert comp(k_out=O, v_out=ctypes.c_void_p((1 << 32) + (1 << 30) + 4096)) == I
