@@ -40,6 +40,11 @@ reading, listed here and implemented below:
       goes to the t-th of them;
   R10 positions are absolute token indices; -1 marks an empty slot.
 
+  R18 8-bit cache (Q-Hitter-like): cached K and V rows are stored as int8
+      codes with one float32 scale per (token, KV head) row, amax / 127,
+      codes = round-half-even(x / scale); attention reads the dequantised
+      rows, the chunk's own K/V are used unquantised in their step and
+      quantised when written; scores and the choice are unchanged.
   R17 SnapKV-style one-shot choice: made once, from the summed weights of
       one observation chunk (the window) over the cache slots; the lowest
       (weight, slot) slots beyond the budget are dropped in R8's order, the
@@ -239,6 +244,67 @@ def kv_scatter(k_cache, v_cache, scores, pos, k_new, v_new, new_scores,
 
 
 # ---------------------------------------------------------------------------
+# Quantised (8-bit) KV cache: Q-Hitter-like H2O over int8 cache rows
+# ---------------------------------------------------------------------------
+def quantize_rows_int8(x):
+    """Symmetric 8-bit quantisation of K or V rows, one scale per row (R18).
+
+    [LtF-zh] §2: cache buffers can be quantised to 8 bits (or fewer), and
+    Q-Hitter combines H2O with such quantisation.  Reading: every stored
+    (token, KV head) row gets scale = amax / 127 (amax = the row's largest
+    |x|) and codes = round-half-even(x / scale), both computed in float32, the
+    precision the device takes the same decision in; a row of zeros gets
+    scale 0 and codes 0.  Rows must be finite.
+    x [..., D] (float32 values, here bf16-representable); returns
+    (codes int8 [..., D], scale float32 [...]).
+    """
+    x = np.asarray(x, np.float32)
+    amax = np.abs(x).max(axis=-1)
+    scale = (amax / np.float32(127.0)).astype(np.float32)
+    safe = np.where(scale > 0, scale, np.float32(1.0)).astype(np.float32)
+    q = np.rint(x / safe[..., None])                      # float32 division
+    q = np.clip(q, -127, 127)
+    q = np.where(scale[..., None] > 0, q, 0)
+    return q.astype(np.int8), scale
+
+
+def dequantize_rows_int8(codes, scale, dtype=np.float64):
+    """codes * scale, exactly (float64)."""
+    return codes.astype(dtype) * np.asarray(scale, dtype)[..., None]
+
+
+def attention_chunk_q8(q, kq, k_scale, vq, v_scale, k_new, v_new, n_valid, scale=None,
+                       dtype=np.float64):
+    """a1 + a2 with the cache slots stored as int8 rows (R18): the cache keys
+    and values are the dequantised rows; the chunk's own keys and values are
+    used as given (they are quantised only when written into the cache).
+    Returns (out, lse, wsum) as :func:`attention_chunk`."""
+    return attention_chunk(q, dequantize_rows_int8(kq, k_scale, dtype),
+                           dequantize_rows_int8(vq, v_scale, dtype), k_new, v_new,
+                           n_valid, scale, dtype)
+
+
+def kv_scatter_q8(kq, k_scale, vq, v_scale, scores, pos, k_new, v_new, new_scores,
+                  evict_idx, p0):
+    """a5 into an int8 cache (R18), in place: chunk token t is quantised and
+    written to slot evict_idx[..., t] (codes and scale), with its score and
+    position as :func:`kv_scatter`."""
+    ck, sk = quantize_rows_int8(k_new)
+    cv, sv = quantize_rows_int8(v_new)
+    B, Hkv, S = evict_idx.shape
+    for b in range(B):
+        for h in range(Hkv):
+            for t in range(S):
+                j = int(evict_idx[b, h, t])
+                kq[b, h, j] = ck[b, h, t]
+                vq[b, h, j] = cv[b, h, t]
+                k_scale[b, h, j] = sk[b, h, t]
+                v_scale[b, h, j] = sv[b, h, t]
+                scores[b, h, j] = new_scores[b, h, t]
+                pos[b, h, j] = p0 + t
+
+
+# ---------------------------------------------------------------------------
 # SnapKV-style one-shot choice from the same summed weights
 # ---------------------------------------------------------------------------
 def snapkv_keep(wsum, n_valid, budget):
@@ -325,3 +391,25 @@ def h2o_step(k_cache, v_cache, scores, pos, n_valid, q, k_new, v_new, p0,
                 new_scores=new_scores, evict_idx=evict, k_cache=kc,
                 v_cache=vc, scores=sc, pos=ps,
                 n_valid=min(C, int(n_valid) + S))
+
+
+def h2o_step_q8(kq, k_scale, vq, v_scale, scores, pos, n_valid, q, k_new, v_new, p0,
+                scale=None, dtype=np.float64):
+    """One chunk step over an int8 cache (R18): attend to the dequantised
+    cache, accumulate, choose (unchanged), scatter the quantised chunk.
+    The cache arrays are not modified; updated copies are returned in a dict
+    like :func:`h2o_step` (keys kq, k_scale, vq, v_scale instead of
+    k_cache, v_cache)."""
+    C = kq.shape[2]
+    S = q.shape[2]
+    out, lse, wsum = attention_chunk_q8(q, kq, k_scale, vq, v_scale, k_new, v_new, n_valid,
+                                        scale, dtype)
+    acc, new_scores = score_accumulate(scores, wsum, n_valid)
+    evict = evict_select(acc, n_valid, S)
+    kq2, ks2, vq2, vs2 = kq.copy(), k_scale.copy(), vq.copy(), v_scale.copy()
+    sc = acc.copy()
+    ps = pos.copy()
+    kv_scatter_q8(kq2, ks2, vq2, vs2, sc, ps, k_new, v_new, new_scores, evict, p0)
+    return dict(out=out, lse=lse, wsum=wsum, scores_acc=acc, new_scores=new_scores,
+                evict_idx=evict, kq=kq2, k_scale=ks2, vq=vq2, v_scale=vs2, scores=sc,
+                pos=ps, n_valid=min(C, int(n_valid) + S))

@@ -1,0 +1,98 @@
+"""Pins of the oracle's 8-bit cache (quantisation, attention over int8 rows,
+quantising scatter) against facts other than its own code: exact codes for
+rows whose scale is a power of two, round-half-even on ties, the half-step
+error bound, and attention over exactly representable rows equal to the
+unquantised attention.  CPU only."""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+
+
+def test_power_of_two_scales_give_exact_codes():
+    # amax = 127 * 2^e makes the float32 scale exactly 2^e, so x / scale is
+    # exact and the codes are the integers themselves
+    ints = np.array([127, -63, 1, 0, -127, 5, 64, -1], np.float32)
+    for e in (-20, -3, 0, 4, 30):
+        x = (ints * np.float32(2.0 ** e)).reshape(1, -1)
+        codes, sc = oracle.quantize_rows_int8(x)
+        assert sc[0] == np.float32(2.0 ** e)
+        assert codes[0].tolist() == ints.astype(int).tolist()
+
+
+def test_ties_round_to_even():
+    codes, sc = oracle.quantize_rows_int8(np.array([[127, 0.5, 1.5, 2.5, -0.5, -1.5, 126.5]],
+                                                    np.float32))
+    assert sc[0] == 1.0
+    assert codes[0].tolist() == [127, 0, 2, 2, 0, -2, 126]
+
+
+def test_zero_row_and_sign_of_the_largest():
+    codes, sc = oracle.quantize_rows_int8(np.zeros((2, 3, 8), np.float32))
+    assert (codes == 0).all() and (sc == 0).all()
+    codes, sc = oracle.quantize_rows_int8(np.array([[-3.0, 1.0, 2.0]], np.float32))
+    assert codes[0, 0] == -127 and sc[0] == np.float32(3.0) / np.float32(127.0)
+
+
+def test_half_step_error_bound():
+    # round to nearest: |x - code * scale| <= scale / 2 (plus float32 slack),
+    # and the row's largest |x| maps to +-127
+    rng = np.random.default_rng(21)
+    x = (rng.standard_normal((50, 128)) * rng.uniform(0.01, 100, (50, 1))).astype(np.float32)
+    codes, sc = oracle.quantize_rows_int8(x)
+    err = np.abs(x.astype(np.float64) - oracle.dequantize_rows_int8(codes, sc))
+    assert (err <= sc[:, None].astype(np.float64) * (0.5 + 1e-5)).all()
+    assert (np.abs(codes).max(axis=1) == 127).all()
+    assert np.abs(codes.astype(int)).max() <= 127
+
+
+def test_attention_over_representable_rows_equals_unquantised():
+    # rows = integer vectors (amax 127) times 2^e with e per row and per
+    # tensor: quantisation is exact, so the int8 attention must equal the
+    # attention on the original values; a scale applied to the wrong row or
+    # tensor breaks the equality
+    rng = np.random.default_rng(22)
+    B, Hq, Hkv, D, C, S, n = 1, 4, 2, 16, 24, 5, 19
+    def rows(shape):
+        ints = rng.integers(-127, 128, size=shape).astype(np.float32)
+        ints[..., 0] = 127
+        e = rng.integers(-8, 3, size=shape[:-1]).astype(np.float32)
+        return ints * np.float32(2.0) ** e[..., None]
+    kc, vc = rows((B, Hkv, C, D)), rows((B, Hkv, C, D))
+    kq, ks = oracle.quantize_rows_int8(kc)
+    vq, vs = oracle.quantize_rows_int8(vc)
+    q = rng.standard_normal((B, Hq, S, D)) * 0.05
+    kn, vn = rng.standard_normal((B, Hkv, S, D)), rng.standard_normal((B, Hkv, S, D))
+    want = oracle.attention_chunk(q, kc, vc, kn, vn, n)
+    got = oracle.attention_chunk_q8(q, kq, ks, vq, vs, kn, vn, n)
+    for w, g in zip(want, got):
+        np.testing.assert_allclose(g, w, rtol=1e-13, atol=1e-13)
+    # swapping the two scale arrays changes the result
+    bad = oracle.attention_chunk_q8(q, kq, vs, vq, ks, kn, vn, n)
+    assert np.abs(bad[0] - want[0]).max() > 1e-3
+
+
+def test_scatter_writes_the_quantised_chunk():
+    rng = np.random.default_rng(23)
+    B, Hkv, C, D, S = 1, 2, 10, 8, 3
+    kq = np.zeros((B, Hkv, C, D), np.int8)
+    vq = np.zeros((B, Hkv, C, D), np.int8)
+    ks = np.zeros((B, Hkv, C), np.float32)
+    vs = np.zeros((B, Hkv, C), np.float32)
+    sc = np.zeros((B, Hkv, C))
+    pos = np.full((B, Hkv, C), -1, np.int64)
+    kn = rng.standard_normal((B, Hkv, S, D)).astype(np.float32)
+    vn = rng.standard_normal((B, Hkv, S, D)).astype(np.float32)
+    ev = np.array([[[1, 4, 9], [0, 2, 3]]])
+    oracle.kv_scatter_q8(kq, ks, vq, vs, sc, pos, kn, vn, np.ones((B, Hkv, S)), ev, p0=40)
+    for h in range(Hkv):
+        for t in range(S):
+            j = ev[0, h, t]
+            x = kn[0, h, t]
+            assert ks[0, h, j] == np.float32(np.abs(x).max()) / np.float32(127)
+            assert np.abs(x - kq[0, h, j] * np.float64(ks[0, h, j])).max() <= ks[0, h, j] * 0.50001
+            assert pos[0, h, j] == 40 + t
+        untouched = [j for j in range(C) if j not in ev[0, h]]
+        assert (kq[0, h, untouched] == 0).all() and (pos[0, h, untouched] == -1).all()
