@@ -46,6 +46,9 @@ def parse():
                     help="print a summary of a rocprofv3 --stats csv run and exit")
     ap.add_argument("--summarize-pmc", metavar="DIR",
                     help="print per-kernel FETCH_SIZE/WRITE_SIZE of a rocprofv3 --pmc csv run")
+    ap.add_argument("--kv8", action="store_true",
+                    help="8-bit KV cache (int8 codes + one fp32 scale per row): attention "
+                         "over the int8 cache and the quantising scatter")
     ap.add_argument("--backward", action="store_true",
                     help="time the attention backward (dQ, dK, dV with the slot layout "
                          "fixed) instead of the forward step")
@@ -201,10 +204,10 @@ def measured_traffic(workload, kernel):
             "source": os.path.relpath(path, ROOT)}
 
 
-def cpu_baseline(wl, min_seconds=10.0, max_heads=24):
+def cpu_baseline(wl, min_seconds=10.0, max_heads=24, q8=False):
     """The oracle (float64, as it stands) on single-KV-head slices of steady
     layer-steps, repeated until about ``min_seconds`` of CPU work; scaled to
-    tokens/s of the whole workload."""
+    tokens/s of the whole workload.  q8: the 8-bit cache step."""
     import numpy as np
     import oracle
     import synth
@@ -217,11 +220,17 @@ def cpu_baseline(wl, min_seconds=10.0, max_heads=24):
     sub = wl.with_(n_kv_heads=1, n_q_heads=G, batch=1)
     st = synth.steady_state(sub)
     k, v, sc = st.k, st.v, st.scores.astype(np.float64)
+    if q8:
+        kq, ks = oracle.quantize_rows_int8(k)
+        vq, vs = oracle.quantize_rows_int8(v)
     spent, heads = 0.0, 0
     while heads < max_heads and (spent < min_seconds or heads == 0):
         ch = synth.gen_chunk(sub, 0, sub.fill_steps + 2 + heads)
         t0 = time.perf_counter()
-        oracle.h2o_step(k, v, sc, st.pos, st.n_valid, ch.q, ch.k, ch.v, ch.p0)
+        if q8:
+            oracle.h2o_step_q8(kq, ks, vq, vs, sc, st.pos, st.n_valid, ch.q, ch.k, ch.v, ch.p0)
+        else:
+            oracle.h2o_step(k, v, sc, st.pos, st.n_valid, ch.q, ch.k, ch.v, ch.p0)
         spent += time.perf_counter() - t0
         heads += 1
     per_head = spent / heads
@@ -513,6 +522,15 @@ def main():
     gen = torch.Generator(device="cuda")
     gen.manual_seed(20261203)
     layers = [make_layer_state(wl, gen) for _ in range(L)]
+    if args.kv8:   # the same caches, quantised on the device
+        for st in layers:
+            for name in ("k", "v"):
+                codes = torch.empty((B, Hkv, C, D), dtype=torch.int8, device="cuda")
+                scales = torch.empty((B, Hkv, C), dtype=torch.float32, device="cuda")
+                h2o.h2o_quantize_rows_q8(st[name], codes, scales)
+                st[name + "q"], st[name + "s"] = codes, scales
+                del st[name]
+        torch.cuda.synchronize()
     inputs = make_inputs(wl, args.warmup + args.steps, gen)
     out = torch.empty((B, Hq, S, D), dtype=torch.float32, device="cuda")
     lse = torch.empty((B, Hq, S), dtype=torch.float32, device="cuda")
@@ -527,11 +545,20 @@ def main():
         p0 = p0_base + i * S
         for li, st in enumerate(layers):
             q, kn, vn = inputs[i][li]
-            h2o.h2o_attn_chunk(shape, q, st["k"], st["v"], kn, vn, out, lse, wsum, ws, stream)
+            if args.kv8:
+                h2o.h2o_attn_chunk_q8(shape, q, st["kq"], st["ks"], st["vq"], st["vs"], kn, vn,
+                                      out, lse, wsum, ws, stream)
+            else:
+                h2o.h2o_attn_chunk(shape, q, st["k"], st["v"], kn, vn, out, lse, wsum, ws,
+                                   stream)
             h2o.h2o_score_accumulate(shape, st["scores"], new_scores, wsum, stream)
             h2o.h2o_evict_select(shape, st["scores"], evict, stream)
-            h2o.kv_scatter(shape, st["k"], st["v"], st["scores"], st["pos"], kn, vn,
-                           new_scores, evict, p0, stream)
+            if args.kv8:
+                h2o.kv_scatter_q8(shape, st["kq"], st["ks"], st["vq"], st["vs"], st["scores"],
+                                  st["pos"], kn, vn, new_scores, evict, p0, stream)
+            else:
+                h2o.kv_scatter(shape, st["k"], st["v"], st["scores"], st["pos"], kn, vn,
+                               new_scores, evict, p0, stream)
 
     if args.calib_copy:   # a copy of known size, to scale the HBM byte counters
         src = torch.empty(CALIB_BYTES // 4, dtype=torch.float32, device="cuda").fill_(1.0)
@@ -562,7 +589,8 @@ def main():
     fwd_ms = kernel_ms["attn_fwd"] / calls
     per_layer = {k: v / calls for k, v in kernel_ms.items()}
     # pass 1 reads every cached K/V row once plus the chunk's Q/K/V
-    fwd_bytes = 2.0 * (B * Hkv * (C + S) * D * 2) + B * Hq * S * D * 2
+    cache_row_bytes = (D + 4) if args.kv8 else 2 * D   # int8 codes + scale, or bf16
+    fwd_bytes = (2.0 * B * Hkv * (C * cache_row_bytes + S * D * 2)) + B * Hq * S * D * 2
     fwd_flop = 4.0 * D * pairs                   # QK^T + PV, 2 flop per MAC
     if fwd_flop / fwd_bytes >= PEAK_BF16_TFLOPS / PEAK_HBM_GBS * 1e3:   # above the ridge
         roof = {"bound": "mfma", "achieved": fwd_flop / (fwd_ms * 1e-3) / 1e12,
@@ -571,8 +599,11 @@ def main():
         roof = {"bound": "hbm", "achieved": fwd_bytes / (fwd_ms * 1e-3) / 1e9,
                 "peak": PEAK_HBM_GBS, "unit": "GB/s", "per_launch_bytes": fwd_bytes}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    fwd_kernel = "attn_fwd_small_kernel<128>" if Hq // Hkv * S <= 32 else "attn_fwd_kernel<128>"
-    traffic = measured_traffic(wl.name, fwd_kernel)
+    small = Hq // Hkv * S <= 32
+    fwd_kernel = (("attn_fwd_small_q8_kernel<%d>" if small else "attn_fwd_q8_kernel<%d>") % D
+                  if args.kv8 else
+                  ("attn_fwd_small_kernel<%d>" if small else "attn_fwd_kernel<%d>") % D)
+    traffic = None if args.kv8 else measured_traffic(wl.name, fwd_kernel)
     per_layer["policy_and_gaps"] = ms_per_step / L - sum(per_layer.values())
     total_flop_exec = 6.0 * D * pairs
     step_tflops = total_flop_exec * L / (ms_per_step * 1e-3) / 1e12
@@ -588,11 +619,12 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "bf16" + (" (int8 KV cache)" if args.kv8 else ""),
         "data": "synthetic",
         "config": {
             "workload": wl.name, "batch": B, "q_heads": Hq, "kv_heads": Hkv, "head_dim": D,
             "cache_len": C, "chunk_len": S, "layers": L, "context": wl.seq_len,
+            "kv_cache": "int8 codes + fp32 row scales" if args.kv8 else "bf16",
             "phase": "steady state: cache full, S slots evicted per KV head per layer",
             "ms_per_layer_step": per_layer,
             "executed_mfma_tflops_whole_step": step_tflops,
@@ -604,7 +636,7 @@ def main():
             avg_launch_ms=fwd_ms, launches=calls, **roof),
     }
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(wl)
+        result["cpu_baseline"] = cpu_baseline(wl, q8=args.kv8)
     print(json.dumps(result), flush=True)
 
 

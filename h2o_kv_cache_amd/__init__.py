@@ -31,6 +31,7 @@ from ._lib import H2OShape
 
 __all__ = ["Shape", "H2OError", "h2o_workspace_size", "h2o_attn_chunk",
            "h2o_score_accumulate", "h2o_evict_select", "kv_scatter",
+           "h2o_attn_chunk_q8", "kv_scatter_q8", "h2o_quantize_rows_q8",
            "h2o_snapkv_select", "h2o_snapkv_compact", "h2o_attn_bwd_workspace_size", "h2o_attn_chunk_bwd",
            "h2o_timing_start", "h2o_timing_stop", "h2o_status_string", "H2OCache",
            "load_library", "ATTN_KERNELS"]
@@ -170,6 +171,62 @@ def kv_scatter(shape: Shape, k_cache, v_cache, scores, pos, k_new, v_new, new_sc
         _ptr(evict_idx, "evict_idx", (B, Hkv, S), (torch.int32,)),
         ctypes.c_int64(int(p0)), _stream(stream)),
         "kv_scatter")
+
+
+_I8 = (torch.int8,)
+
+
+def h2o_attn_chunk_q8(shape: Shape, q, k_cache, k_scale, v_cache, v_scale, k_new, v_new, out,
+                      lse, wsum, ws, stream=None):
+    s = shape
+    B, Hq, Hkv, D, C, S = (s.batch, s.n_q_heads, s.n_kv_heads, s.head_dim, s.cache_len,
+                           s.chunk_len)
+    sh = s.c()
+    nbytes = ws.numel() * ws.element_size()
+    _check(_lib.load().h2o_attn_chunk_q8(
+        ctypes.byref(sh), _ptr(q, "q", (B, Hq, S, D), _BF16),
+        _ptr(k_cache, "k_cache", (B, Hkv, C, D), _I8),
+        _ptr(k_scale, "k_scale", (B, Hkv, C), _F32),
+        _ptr(v_cache, "v_cache", (B, Hkv, C, D), _I8),
+        _ptr(v_scale, "v_scale", (B, Hkv, C), _F32),
+        _ptr(k_new, "k_new", (B, Hkv, S, D), _BF16),
+        _ptr(v_new, "v_new", (B, Hkv, S, D), _BF16),
+        _ptr(out, "out", (B, Hq, S, D), _F32),
+        ctypes.c_void_p(None) if lse is None else _ptr(lse, "lse", (B, Hq, S), _F32),
+        _ptr(wsum, "wsum", (B, Hkv, C + S), _F32),
+        ctypes.c_void_p(ws.data_ptr()), ctypes.c_size_t(nbytes), _stream(stream)),
+        "h2o_attn_chunk_q8")
+
+
+def kv_scatter_q8(shape: Shape, k_cache, k_scale, v_cache, v_scale, scores, pos, k_new, v_new,
+                  new_scores, evict_idx, p0: int, stream=None):
+    s = shape
+    B, Hkv, D, C, S = s.batch, s.n_kv_heads, s.head_dim, s.cache_len, s.chunk_len
+    sh = s.c()
+    _check(_lib.load().kv_scatter_q8(
+        ctypes.byref(sh), _ptr(k_cache, "k_cache", (B, Hkv, C, D), _I8),
+        _ptr(k_scale, "k_scale", (B, Hkv, C), _F32),
+        _ptr(v_cache, "v_cache", (B, Hkv, C, D), _I8),
+        _ptr(v_scale, "v_scale", (B, Hkv, C), _F32),
+        _ptr(scores, "scores", (B, Hkv, C), _F32),
+        ctypes.c_void_p(None) if pos is None else _ptr(pos, "pos", (B, Hkv, C), (torch.int64,)),
+        _ptr(k_new, "k_new", (B, Hkv, S, D), _BF16),
+        _ptr(v_new, "v_new", (B, Hkv, S, D), _BF16),
+        _ptr(new_scores, "new_scores", (B, Hkv, S), _F32),
+        _ptr(evict_idx, "evict_idx", (B, Hkv, S), (torch.int32,)),
+        ctypes.c_int64(int(p0)), _stream(stream)),
+        "kv_scatter_q8")
+
+
+def h2o_quantize_rows_q8(x, codes, scales, stream=None):
+    """x [..., D] bf16 -> codes [..., D] int8, scales [...] fp32 (contiguous)."""
+    D = x.shape[-1]
+    rows = x.numel() // D
+    _check(_lib.load().h2o_quantize_rows_q8(
+        _ptr(x, "x", tuple(x.shape), _BF16), ctypes.c_int64(rows), ctypes.c_int32(D),
+        _ptr(codes, "codes", tuple(x.shape), _I8),
+        _ptr(scales, "scales", tuple(x.shape[:-1]), _F32), _stream(stream)),
+        "h2o_quantize_rows_q8")
 
 
 def h2o_snapkv_select(shape: Shape, wsum, budget: int, keep_idx, stream=None):

@@ -15,7 +15,8 @@ H2O_ERR_WORKSPACE = 3
 H2O_ERR_HIP = 4
 
 EXPORTED = ("h2o_workspace_size", "h2o_attn_chunk", "h2o_score_accumulate",
-            "h2o_evict_select", "kv_scatter", "h2o_snapkv_select", "h2o_snapkv_compact",
+            "h2o_evict_select", "kv_scatter", "h2o_attn_chunk_q8", "kv_scatter_q8",
+            "h2o_quantize_rows_q8", "h2o_snapkv_select", "h2o_snapkv_compact",
             "h2o_attn_bwd_workspace_size",
             "h2o_attn_chunk_bwd", "h2o_timing_start", "h2o_timing_stop",
             "h2o_status_string")
@@ -46,6 +47,12 @@ def _declare(lib):
     lib.h2o_evict_select.restype = ctypes.c_int
     lib.kv_scatter.argtypes = [S, P, P, P, P, P, P, P, P, ctypes.c_int64, P]
     lib.kv_scatter.restype = ctypes.c_int
+    lib.h2o_attn_chunk_q8.argtypes = [S] + [P] * 11 + [ctypes.c_size_t, P]
+    lib.h2o_attn_chunk_q8.restype = ctypes.c_int
+    lib.kv_scatter_q8.argtypes = [S] + [P] * 10 + [ctypes.c_int64, P]
+    lib.kv_scatter_q8.restype = ctypes.c_int
+    lib.h2o_quantize_rows_q8.argtypes = [P, ctypes.c_int64, ctypes.c_int32, P, P, P]
+    lib.h2o_quantize_rows_q8.restype = ctypes.c_int
     lib.h2o_snapkv_select.argtypes = [S, P, ctypes.c_int32, P, P]
     lib.h2o_snapkv_select.restype = ctypes.c_int
     lib.h2o_snapkv_compact.argtypes = ([S] + [P] * 7 + [ctypes.c_int32, ctypes.c_int32,

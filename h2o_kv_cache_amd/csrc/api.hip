@@ -146,6 +146,64 @@ h2o_status_t kv_scatter(const h2o_shape_t* s, uint16_t* k_cache, uint16_t* v_cac
     return from_hip(e);
 }
 
+h2o_status_t h2o_attn_chunk_q8(const h2o_shape_t* s, const uint16_t* q, const int8_t* k_cache,
+                               const float* k_scale, const int8_t* v_cache,
+                               const float* v_scale, const uint16_t* k_new,
+                               const uint16_t* v_new, float* out, float* lse, float* wsum,
+                               void* ws, size_t ws_bytes, void* stream) {
+    h2o_status_t st = check_shape(s);
+    if (st != H2O_OK) return st;
+    if (!q || !k_cache || !k_scale || !v_cache || !v_scale || !k_new || !v_new || !out || !wsum)
+        return H2O_ERR_INVALID_ARG;
+    if (!aligned16(q) || !aligned16(k_cache) || !aligned16(k_scale) || !aligned16(v_cache) ||
+        !aligned16(v_scale) || !aligned16(k_new) || !aligned16(v_new) || !aligned16(out) ||
+        !aligned16(wsum) || (lse && !aligned16(lse)))
+        return H2O_ERR_INVALID_ARG;
+    h2o::AttnPlan pl;
+    h2o::make_attn_plan(s->batch, s->n_q_heads, s->n_kv_heads, s->head_dim, s->cache_len,
+                        s->chunk_len, s->n_valid, s->scale, &pl);
+    if (!ws || ((uintptr_t)ws & 255u) || ws_bytes < pl.bytes) return H2O_ERR_WORKSPACE;
+    return from_hip(h2o::launch_attention_q8(pl, q, k_cache, k_scale, v_cache, v_scale, k_new,
+                                             v_new, out, lse, wsum, ws, (hipStream_t)stream,
+                                             sync_debug(), timing_slot()));
+}
+
+h2o_status_t kv_scatter_q8(const h2o_shape_t* s, int8_t* k_cache, float* k_scale,
+                           int8_t* v_cache, float* v_scale, float* scores, int64_t* pos,
+                           const uint16_t* k_new, const uint16_t* v_new,
+                           const float* new_scores, const int32_t* evict_idx, int64_t p0,
+                           void* stream) {
+    h2o_status_t st = check_shape(s);
+    if (st != H2O_OK) return st;
+    if (!k_cache || !k_scale || !v_cache || !v_scale || !scores || !k_new || !v_new ||
+        !new_scores || !evict_idx)
+        return H2O_ERR_INVALID_ARG;
+    if (!aligned16(k_cache) || !aligned16(k_scale) || !aligned16(v_cache) ||
+        !aligned16(v_scale) || !aligned16(scores) || !aligned16(k_new) || !aligned16(v_new) ||
+        !aligned16(new_scores) || !aligned16(evict_idx) || (pos && !aligned16(pos)))
+        return H2O_ERR_INVALID_ARG;
+    if (p0 < 0) return H2O_ERR_INVALID_ARG;
+    hipError_t e = h2o::launch_kv_scatter_q8(s->batch * s->n_kv_heads, s->head_dim,
+                                             s->cache_len, s->chunk_len, k_cache, k_scale,
+                                             v_cache, v_scale, scores, pos, k_new, v_new,
+                                             new_scores, evict_idx, p0, (hipStream_t)stream);
+    if (e == hipSuccess && sync_debug()) e = hipStreamSynchronize((hipStream_t)stream);
+    return from_hip(e);
+}
+
+h2o_status_t h2o_quantize_rows_q8(const uint16_t* x, int64_t n_rows, int32_t head_dim,
+                                  int8_t* codes, float* scales, void* stream) {
+    if (head_dim != 64 && head_dim != 128) return H2O_ERR_UNSUPPORTED;
+    if (n_rows < 0 || n_rows >= (1ll << 31) / 16) return H2O_ERR_INVALID_ARG;
+    if (!x || !codes || !scales || !aligned16(x) || !aligned16(codes) || !aligned16(scales))
+        return H2O_ERR_INVALID_ARG;
+    if (n_rows == 0) return H2O_OK;
+    hipError_t e = h2o::launch_quantize_rows(x, (long)n_rows, head_dim, codes, scales,
+                                             (hipStream_t)stream);
+    if (e == hipSuccess && sync_debug()) e = hipStreamSynchronize((hipStream_t)stream);
+    return from_hip(e);
+}
+
 h2o_status_t h2o_snapkv_select(const h2o_shape_t* s, const float* wsum, int32_t budget,
                                int32_t* keep_idx, void* stream) {
     h2o_status_t st = check_shape(s);

@@ -89,8 +89,10 @@ constexpr bf16x2 kOnes2 = {(__bf16)1.0f, (__bf16)1.0f};
 // S^T = K Q^T, online softmax in base 2, O^T += V^T P^T.  MASKED handles the
 // last partial cache tile and the causal chunk tiles.  With a non-null
 // `lg_row` the base-2 logits of this lane's row are also stored, at logits
-// columns col0 + (key - key0).
-template <int D, bool MASKED>
+// columns col0 + (key - key0).  The block's rows sit at block lkb of the LDS
+// tiles (lkb = kb except for per-wave tiles).  KSC: the K tile holds int8
+// codes, and logit j is multiplied by the key's scale ksc[lkb*32 + j].
+template <int D, bool MASKED, bool KSC = false, bool K8 = false>
 __device__ __forceinline__ void fwd_block(const uint16_t* Ks, const uint16_t* Vs,
                                           const LdsOffsets<D>& off,
                                           const bf16x8 (&qf)[RB][D / 16],
@@ -98,7 +100,9 @@ __device__ __forceinline__ void fwd_block(const uint16_t* Ks, const uint16_t* Vs
                                           float (&m_seen)[RB], bool& overflow,
                                           float (&l_acc)[RB], float (&lt_acc)[RB], float c,
                                           int kb, int key0, int lim, bool chunk, int G,
-                                          int rbase, int lane, float* lg_row, int col0) {
+                                          int rbase, int lane, float* lg_row, int col0,
+                                          int lkb, const float* ksc = nullptr,
+                                          const uint8_t* k8 = nullptr) {
     const int l32 = lane & 31, half = lane >> 5;
     {
         f32x16 s[RB];
@@ -106,11 +110,29 @@ __device__ __forceinline__ void fwd_block(const uint16_t* Ks, const uint16_t* Vs
         for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
             for (int v = 0; v < 16; ++v) s[rb][v] = 0.f;
+        // K8: the K fragments come straight from a swizzled int8 tile (row
+        // lkb*32 + l32, dims 16*ks + 8*half + [0, 8)), converted exactly
+        const int krow = lkb * 32 + l32;
+        const uint8_t* k8row = K8 ? k8 + krow * D + 8 * half : nullptr;
 #pragma unroll
         for (int ks = 0; ks < D / 16; ++ks) {
-            const bf16x8 kf = as_bf16x8(lds_read16(Ks, off.k[ks] + kb * 64 * D));
+            bf16x8 kf;
+            if constexpr (K8)
+                kf = i8x8_to_bf16(*(const uint2*)(k8row + 16 * (ks ^ i8_swz<D>(krow))));
+            else
+                kf = as_bf16x8(lds_read16(Ks, off.k[ks] + lkb * 64 * D));
 #pragma unroll
             for (int rb = 0; rb < RB; ++rb) s[rb] = mfma32x32x16(kf, qf[rb][ks], s[rb]);
+        }
+        if (KSC) {   // element v is key lkb*32 + 8*(v/4) + 4*half + v%4 of the tile
+#pragma unroll
+            for (int g4 = 0; g4 < 4; ++g4) {
+                const f32x4 k4 = *(const f32x4*)(ksc + lkb * 32 + 8 * g4 + 4 * half);
+#pragma unroll
+                for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) s[rb][4 * g4 + e] *= k4[e];
+            }
         }
 
         // mask (last partial cache tile, chunk tiles), then row max over raw
@@ -185,7 +207,7 @@ __device__ __forceinline__ void fwd_block(const uint16_t* Ks, const uint16_t* Vs
 #pragma unroll
         for (int hs = 0; hs < 2; ++hs) {
             // keys kb*32 + 16*hs + 8*gg + 4*half + [0, 4): rows (kb*32 + 16*hs + 8*gg) below
-            const uint32_t row_b = (uint32_t)(kb * 32 + 16 * hs) * 2 * D;
+            const uint32_t row_b = (uint32_t)(lkb * 32 + 16 * hs) * 2 * D;
 #pragma unroll
             for (int db = 0; db < D / 32; ++db) {
                 const u32x2 lo = lds_read_tr(Vs, off.v[db] + row_b);
@@ -200,7 +222,7 @@ __device__ __forceinline__ void fwd_block(const uint16_t* Ks, const uint16_t* Vs
 }
 
 // One KT-key tile of pass 1 for one wave: its 32-key blocks in order.
-template <int D, bool MASKED>
+template <int D, bool MASKED, bool KSC = false>
 __device__ __forceinline__ void fwd_tile(const uint16_t* Ks, const uint16_t* Vs,
                                          const LdsOffsets<D>& off,
                                          const bf16x8 (&qf)[RB][D / 16],
@@ -208,11 +230,12 @@ __device__ __forceinline__ void fwd_tile(const uint16_t* Ks, const uint16_t* Vs,
                                          float (&m_seen)[RB], bool& overflow,
                                          float (&l_acc)[RB], float (&lt_acc)[RB], float c,
                                          int key0, int lim, bool chunk, int G, int rbase,
-                                         int lane) {
+                                         int lane, const float* ksc = nullptr) {
 #pragma unroll
     for (int kb = 0; kb < KT / 32; ++kb)
-        fwd_block<D, MASKED>(Ks, Vs, off, qf, o_acc, m_ref, m_seen, overflow, l_acc, lt_acc, c,
-                             kb, key0, lim, chunk, G, rbase, lane, nullptr, 0);
+        fwd_block<D, MASKED, KSC>(Ks, Vs, off, qf, o_acc, m_ref, m_seen, overflow, l_acc,
+                                  lt_acc, c, kb, key0, lim, chunk, G, rbase, lane, nullptr, 0,
+                                  kb, ksc);
 }
 
 // ---------------------------------------------------------------------------
@@ -418,11 +441,11 @@ __global__ __launch_bounds__(NT_S, 1) void attn_fwd_small_kernel(
             if (!chunk && key0 + KT <= g.n)
                 fwd_block<D, false>(Ks[buf], Vs[buf], off, qf, o_acc, m_ref, m_seen, overflow,
                                     l_acc, lt_acc, g.c, wave, key0, lim, false, 0, 0, lane,
-                                    sweep == 0 ? lg_row : nullptr, col0);
+                                    sweep == 0 ? lg_row : nullptr, col0, wave);
             else
                 fwd_block<D, true>(Ks[buf], Vs[buf], off, qf, o_acc, m_ref, m_seen, overflow,
                                    l_acc, lt_acc, g.c, wave, key0, lim, chunk, g.G, 0, lane,
-                                   sweep == 0 ? lg_row : nullptr, col0);
+                                   sweep == 0 ? lg_row : nullptr, col0, wave);
             // tile t+1 must have landed; tiles issued after it may stay in flight
             // (loads complete in issue order)
             const int later = min(STAGES_S - 2, t_end - 1 - (t + 1));
@@ -557,12 +580,13 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(
 // the column sums of P = 2^(S*c - L2) over this wave's rows into colp.
 // MASKED handles the last partial cache tile (G == 0) and chunk tiles (G > 0:
 // row r sees chunk key t iff t*G <= r).
-template <int D, bool MASKED>
+template <int D, bool MASKED, bool KSC = false>
 __device__ __forceinline__ void colsum_tile(const uint16_t* Ks, const LdsOffsets<D>& off,
                                             float* colp,
                                             const bf16x8 (&qf)[RB][D / 16],
                                             const float (&l2v)[RB][16], float c, int key0,
-                                            int lim, int G, int rbase, int l32, int half) {
+                                            int lim, int G, int rbase, int l32, int half,
+                                            const float* ksc = nullptr) {
     float col[KT / 32];
 #pragma unroll
     for (int kb = 0; kb < KT / 32; ++kb) {
@@ -579,11 +603,13 @@ __device__ __forceinline__ void colsum_tile(const uint16_t* Ks, const LdsOffsets
         }
         float cs = 0.f;
         const int key = key0 + kb * 32 + l32;
+        // KSC: the lane's key scale folds into the logit scale
+        const float ck = KSC ? c * ksc[kb * 32 + l32] : c;
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
-                const float p = fast_exp2(fmaf(s[rb][v], c, -l2v[rb][v]));
+                const float p = fast_exp2(fmaf(s[rb][v], ck, -l2v[rb][v]));
                 if (MASKED) {
                     const int r = rbase + rb * 32 + acc_row(v, half);
                     cs += (key < lim && key * G <= r) ? p : 0.f;
@@ -691,6 +717,521 @@ __global__ __launch_bounds__(NT, 2) void attn_colsum_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// 8-bit cache: the cache tiles arrive as int8 codes plus one float scale per
+// row and are converted in LDS into the bf16 tiles the blocks above read --
+// K codes exactly (integers of at most 7 bits; the K scale multiplies the
+// logit), V codes times their scale, rounded to bf16.  Chunk tiles are bf16
+// already and are only copied.  Conversion of tile t+1 runs after the MFMA
+// work of tile t, so a tile costs one barrier, as in the bf16 kernels.
+// ---------------------------------------------------------------------------
+struct Q8Cache {
+    const int8_t* kc;
+    const float* ks;
+    const int8_t* vc;
+    const float* vs;
+};
+
+// Staging area of one tile: K then V, each KT rows of D bf16 (chunk tiles,
+// already swizzled for the MFMA reads) or of D int8 codes (cache tiles).
+template <int D>
+constexpr int stage_bytes() { return 2 * KT * D * 2; }
+
+// Copy (chunk tile) or convert (cache tile) one staged tile into the bf16
+// tiles kt / vt, and its K scales into kscale (1 for chunk tiles).  Called by
+// all NT_ threads of the workgroup.
+template <int D, int NT_>
+__device__ __forceinline__ void convert_stage(const uint8_t* stg, const float* sks,
+                                              const float* svs, uint16_t* kt, uint16_t* vt,
+                                              float* kscale, bool chunk, int tid) {
+    if (chunk) {
+        constexpr int U = KT * D / 8;   // 16-byte pieces per tensor, layout kept
+#pragma unroll
+        for (int u0 = 0; u0 < 2 * U; u0 += NT_) {
+            const int u = u0 + tid;
+            if (u < 2 * U) {
+                const bool isv = u >= U;
+                const int uu = isv ? u - U : u;
+                const u32x4 x = *(const u32x4*)(stg + (isv ? KT * D * 2 : 0) + uu * 16);
+                *(u32x4*)((isv ? vt : kt) + uu * 8) = x;
+            }
+        }
+        if (tid < KT) kscale[tid] = 1.f;
+    } else {
+        constexpr int CPR = D / 16;     // 16 codes per piece
+        constexpr int U = KT * CPR;
+#pragma unroll
+        for (int u0 = 0; u0 < 2 * U; u0 += NT_) {
+            const int u = u0 + tid;
+            if (u < 2 * U) {
+                const bool isv = u >= U;
+                const int uu = isv ? u - U : u;
+                const int key = uu / CPR, c = uu % CPR;
+                const u32x4 x = *(const u32x4*)(stg + (isv ? KT * D : 0) + key * D + c * 16);
+                u32x4 lo, hi;
+                if (isv) {
+                    i8x16_to_bf16_scaled(x, svs[key], lo, hi);
+                    *(u32x4*)(vt + tile_off<D, true>(key, 2 * c)) = lo;
+                    *(u32x4*)(vt + tile_off<D, true>(key, 2 * c + 1)) = hi;
+                } else {
+                    i8x16_to_bf16(x, lo, hi);
+                    *(u32x4*)(kt + tile_off<D, false>(key, 2 * c)) = lo;
+                    *(u32x4*)(kt + tile_off<D, false>(key, 2 * c + 1)) = hi;
+                }
+            }
+        }
+        if (tid < KT) kscale[tid] = sks[tid];
+    }
+}
+
+// DMA of one tile into a staging area: int8 rows + scales for cache tiles,
+// swizzled bf16 rows for chunk tiles.
+template <int D, int NW>
+__device__ __forceinline__ void issue_stage(uint8_t* stg, float* sks, float* svs,
+                                            const Q8Cache& qc, const uint16_t* kn_bh,
+                                            const uint16_t* vn_bh, size_t cache_row0,
+                                            bool chunk, int key0, int lim, int wave, int lane) {
+    if (chunk) {
+        issue_tile<D, false, NW>((uint16_t*)stg, kn_bh, key0, lim, wave, lane);
+        issue_tile<D, true, NW>((uint16_t*)(stg + KT * D * 2), vn_bh, key0, lim, wave, lane);
+    } else {
+        issue_tile_i8<D, NW>(stg, qc.kc + cache_row0 * D, key0, lim, wave, lane);
+        issue_tile_i8<D, NW>(stg + KT * D, qc.vc + cache_row0 * D, key0, lim, wave, lane);
+        issue_scales<0, NW - 1>(sks, svs, qc.ks + cache_row0, qc.vs + cache_row0, key0, lim,
+                                wave, lane);
+    }
+}
+
+// pass 1 over an 8-bit cache
+template <int D>
+__global__ __launch_bounds__(NT, 1) void attn_fwd_q8_kernel(
+    const AttnGeom g, const int nsplit, const uint16_t* __restrict__ q, const Q8Cache qc,
+    const uint16_t* __restrict__ kn, const uint16_t* __restrict__ vn,
+    float* __restrict__ o_part, float* __restrict__ ml_part) {
+    __shared__ __attribute__((aligned(16))) uint16_t Ks[2][KT * D];
+    __shared__ __attribute__((aligned(16))) uint16_t Vs[2][KT * D];
+    __shared__ __attribute__((aligned(16))) uint8_t stg[2][stage_bytes<D>()];
+    __shared__ __attribute__((aligned(16))) float ssc[2][2][KT];
+    __shared__ __attribute__((aligned(16))) float ksc[2][KT];
+
+    int qt, bh, split;
+    decode_block(g.n_qt, nsplit, qt, bh, split);
+    const int BH = g.B * g.Hkv;
+    const int b = bh / g.Hkv, h = bh % g.Hkv;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int half = lane >> 5, l32 = lane & 31;
+    const int rbase = qt * kRowsPerBlock + wave * kRowsPerWave;
+    const int live = min(RB, max(0, (g.R - rbase + 31) / 32));
+
+    bf16x8 qf[RB][D / 16];
+    load_q<D>(qf, q, g, b, h, rbase, l32, half);
+    const LdsOffsets<D> off(lane);
+
+    const TileRange tr = tile_range(g, qt);
+    const int t_begin = (int)((long)split * tr.total / nsplit);
+    const int t_end = (int)((long)(split + 1) * tr.total / nsplit);
+    const uint16_t* kn_bh = kn + (size_t)bh * g.S * D;
+    const uint16_t* vn_bh = vn + (size_t)bh * g.S * D;
+
+    float m_ref[RB], m_seen[RB], l_acc[RB], lt_acc[RB];
+    f32x16 o_acc[RB][D / 32];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) m_seen[rb] = -INFINITY;
+
+    auto issue = [&](int t, int sb) {
+        const bool chunk = t >= tr.n_ct;
+        const int key0 = chunk ? (t - tr.n_ct) * KT : t * KT;
+        issue_stage<D, kWaves>(stg[sb], ssc[sb][0], ssc[sb][1], qc, kn_bh, vn_bh,
+                               (size_t)bh * g.C, chunk, key0, chunk ? g.S : g.n, wave, lane);
+    };
+    auto convert = [&](int t, int sb) {
+        convert_stage<D, NT>(stg[sb], ssc[sb][0], ssc[sb][1], Ks[sb], Vs[sb], ksc[sb],
+                             t >= tr.n_ct, tid);
+    };
+
+    for (int sweep = 0; sweep < 2; ++sweep) {
+        bool overflow = false;
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+            m_ref[rb] = (sweep == 0) ? -INFINITY : m_seen[rb];
+            l_acc[rb] = 0.f;
+            lt_acc[rb] = 0.f;
+#pragma unroll
+            for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) o_acc[rb][db][v] = 0.f;
+        }
+        // prologue: tile t_begin converted, tile t_begin+1 staged
+        if (t_begin < t_end) {
+            issue(t_begin, 0);
+            wait_tiles();
+            __syncthreads();
+            convert(t_begin, 0);
+        }
+        if (t_begin + 1 < t_end) issue(t_begin + 1, 1);
+        wait_tiles();
+        __syncthreads();
+
+        const int n_full = g.n / KT;
+        const int t_mid = max(t_begin, min(t_end, n_full));
+        // buffer b holds tile t (converted) and, until this iteration's
+        // issue, the staging of tile t that was converted last iteration
+        for (int t = t_begin; t < t_mid; ++t) {
+            const int bb = (t - t_begin) & 1;
+            if (t + 2 < t_end) issue(t + 2, bb);
+            if (live > 0)
+                fwd_tile<D, false, true>(Ks[bb], Vs[bb], off, qf, o_acc, m_ref, m_seen, overflow,
+                                         l_acc, lt_acc, g.c, 0, 0, false, 0, rbase, lane,
+                                         ksc[bb]);
+            if (t + 1 < t_end) convert(t + 1, bb ^ 1);
+            wait_tiles();
+            __syncthreads();
+        }
+        for (int t = t_mid; t < t_end; ++t) {
+            const int bb = (t - t_begin) & 1;
+            const bool chunk = t >= tr.n_ct;
+            const int key0 = chunk ? (t - tr.n_ct) * KT : t * KT;
+            const int lim = chunk ? g.S : g.n;
+            if (t + 2 < t_end) issue(t + 2, bb);
+            if (live > 0)
+                fwd_tile<D, true, true>(Ks[bb], Vs[bb], off, qf, o_acc, m_ref, m_seen, overflow,
+                                        l_acc, lt_acc, g.c, key0, lim, chunk, g.G, rbase, lane,
+                                        ksc[bb]);
+            if (t + 1 < t_end) convert(t + 1, bb ^ 1);
+            wait_tiles();
+            __syncthreads();
+        }
+        if (!__syncthreads_or(overflow)) break;
+    }
+
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+        const float l = l_acc[rb] + xor32(l_acc[rb]);
+        const float lt = lt_acc[rb] + xor32(lt_acc[rb]);
+        const int r = rbase + rb * 32 + l32;
+        if (r >= g.R) continue;
+        const size_t prow = ((size_t)split * BH + bh) * g.rows_pad + r;
+        if (half == 0) *(f32x4*)(ml_part + prow * 4) = f32x4{m_ref[rb], l, lt, 0.f};
+        float* orow = o_part + prow * D;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+            for (int gq = 0; gq < 4; ++gq) {
+                const f32x4 v4 = {o_acc[rb][db][4 * gq + 0], o_acc[rb][db][4 * gq + 1],
+                                  o_acc[rb][db][4 * gq + 2], o_acc[rb][db][4 * gq + 3]};
+                *(f32x4*)(orow + db * 32 + 8 * gq + 4 * half) = v4;
+            }
+    }
+}
+
+// pass 2 over an 8-bit cache (K only)
+template <int D>
+__global__ __launch_bounds__(NT, 2) void attn_colsum_q8_kernel(
+    const AttnGeom g, const int nsplit, const uint16_t* __restrict__ q, const Q8Cache qc,
+    const uint16_t* __restrict__ kn, const float* __restrict__ l2, float* __restrict__ wpart) {
+    __shared__ __attribute__((aligned(16))) uint16_t Ks[2][KT * D];
+    __shared__ __attribute__((aligned(16))) uint8_t stg[2][KT * D * 2];
+    __shared__ __attribute__((aligned(16))) float ssc[2][KT];
+    __shared__ __attribute__((aligned(16))) float ksc[2][KT];
+    __shared__ float colp[2][kWaves][KT];
+
+    int qt, bh, split;
+    decode_block(g.n_qt, nsplit, qt, bh, split);
+    const int BH = g.B * g.Hkv;
+    const int b = bh / g.Hkv, h = bh % g.Hkv;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int half = lane >> 5, l32 = lane & 31;
+    const int W = g.C + g.S;
+    const int rbase = qt * kRowsPerBlock + wave * kRowsPerWave;
+    const int live = min(RB, max(0, (g.R - rbase + 31) / 32));
+
+    bf16x8 qf[RB][D / 16];
+    load_q<D>(qf, q, g, b, h, rbase, l32, half);
+    const LdsOffsets<D> off(lane);
+    float l2v[RB][16];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+        for (int v = 0; v < 16; ++v)
+            l2v[rb][v] = l2[(size_t)bh * g.rows_pad + rbase + rb * 32 + acc_row(v, half)];
+
+    const TileRange tr = tile_range(g, qt);
+    const int t_begin = (int)((long)split * tr.total / nsplit);
+    const int t_end = (int)((long)(split + 1) * tr.total / nsplit);
+    const uint16_t* kn_bh = kn + (size_t)bh * g.S * D;
+    const size_t row0 = (size_t)bh * g.C;
+    float* wrow = wpart + ((size_t)qt * BH + bh) * W;
+
+    auto flush = [&](int t, int buf) {
+        if (tid < KT) {
+            const bool chunk = t >= tr.n_ct;
+            const int key = (chunk ? (t - tr.n_ct) * KT : t * KT) + tid;
+            if (key < (chunk ? g.S : g.n)) {
+                float tot = colp[buf][0][tid];
+#pragma unroll
+                for (int w = 1; w < kWaves; ++w) tot += colp[buf][w][tid];
+                wrow[chunk ? g.C + key : key] = tot;
+            }
+        }
+    };
+    auto issue = [&](int t, int sb) {
+        const bool chunk = t >= tr.n_ct;
+        const int key0 = chunk ? (t - tr.n_ct) * KT : t * KT;
+        if (chunk) {
+            issue_tile<D, false>((uint16_t*)stg[sb], kn_bh, key0, g.S, wave, lane);
+        } else {
+            issue_tile_i8<D, kWaves>(stg[sb], qc.kc + row0 * D, key0, g.n, wave, lane);
+            issue_scales<0, -1>(ssc[sb], nullptr, qc.ks + row0, nullptr, key0, g.n, wave, lane);
+        }
+    };
+    // K only: the V half of convert_stage is skipped by converting a
+    // K-sized "tile pair" whose V part is never read
+    auto convert = [&](int t, int sb) {
+        const bool chunk = t >= tr.n_ct;
+        if (chunk) {
+            constexpr int U = KT * D / 8;
+#pragma unroll
+            for (int u0 = 0; u0 < U; u0 += NT) {
+                const int u = u0 + tid;
+                if (u < U) *(u32x4*)(Ks[sb] + u * 8) = *(const u32x4*)(stg[sb] + u * 16);
+            }
+            if (tid < KT) ksc[sb][tid] = 1.f;
+        } else {
+            constexpr int CPR = D / 16;
+            constexpr int U = KT * CPR;
+#pragma unroll
+            for (int u0 = 0; u0 < U; u0 += NT) {
+                const int u = u0 + tid;
+                if (u < U) {
+                    const int key = u / CPR, c = u % CPR;
+                    u32x4 lo, hi;
+                    i8x16_to_bf16(*(const u32x4*)(stg[sb] + key * D + c * 16), lo, hi);
+                    *(u32x4*)(Ks[sb] + tile_off<D, false>(key, 2 * c)) = lo;
+                    *(u32x4*)(Ks[sb] + tile_off<D, false>(key, 2 * c + 1)) = hi;
+                }
+            }
+            if (tid < KT) ksc[sb][tid] = ssc[sb][tid];
+        }
+    };
+
+    if (t_begin < t_end) {
+        issue(t_begin, 0);
+        wait_tiles();
+        __syncthreads();
+        convert(t_begin, 0);
+    }
+    if (t_begin + 1 < t_end) issue(t_begin + 1, 1);
+    wait_tiles();
+    __syncthreads();
+
+    for (int t = t_begin; t < t_end; ++t) {
+        const int bb = (t - t_begin) & 1;
+        const bool chunk = t >= tr.n_ct;
+        const int key0 = chunk ? (t - tr.n_ct) * KT : t * KT;
+        const int lim = chunk ? g.S : g.n;
+        if (t + 2 < t_end) issue(t + 2, bb);
+        if (t > t_begin) flush(t - 1, bb ^ 1);
+        if (live == 0) {
+            if (half == 0) {
+                colp[bb][wave][l32] = 0.f;
+                colp[bb][wave][32 + l32] = 0.f;
+            }
+        } else if (!chunk && key0 + KT <= g.n) {
+            colsum_tile<D, false, true>(Ks[bb], off, colp[bb][wave], qf, l2v, g.c, 0, 0, 0,
+                                        rbase, l32, half, ksc[bb]);
+        } else {
+            colsum_tile<D, true, true>(Ks[bb], off, colp[bb][wave], qf, l2v, g.c, key0, lim,
+                                       chunk ? g.G : 0, rbase, l32, half, ksc[bb]);
+        }
+        if (t + 1 < t_end) convert(t + 1, bb ^ 1);
+        wait_tiles();
+        __syncthreads();
+    }
+    if (t_begin < t_end) flush(t_end - 1, (t_end - 1 - t_begin) & 1);
+}
+
+// few-row pass 1 over an 8-bit cache.  The waves take different 32-key
+// blocks of each tile.  K fragments are read straight from the staged int8
+// tile (swizzled) and converted in registers; each wave converts only its
+// own block of V into a bf16 block of its own, which the transposed reads
+// need.  Three staging buffers keep the workgroup small enough for two per
+// CU.  Every block runs the masked variant, so no branch separates
+// accumulator updates.
+constexpr int STQ = 3;                 // staging buffers: 2 cache tiles in flight
+
+template <int PT>
+__device__ __forceinline__ void wait_later(int later) {
+    if (later >= 1)
+        wait_vm<PT>();
+    else
+        wait_tiles();
+}
+
+template <int D>
+__global__ __launch_bounds__(NT_S, 2) void attn_fwd_small_q8_kernel(
+    const AttnGeom g, const int nsplit, const uint16_t* __restrict__ q, const Q8Cache qc,
+    const uint16_t* __restrict__ kn, const uint16_t* __restrict__ vn,
+    float* __restrict__ o_part, float* __restrict__ ml_part, float* __restrict__ logits) {
+    __shared__ __attribute__((aligned(16))) uint8_t stg[STQ][2 * KT * D];
+    __shared__ __attribute__((aligned(16))) float ssc[STQ][2][KT];
+    __shared__ __attribute__((aligned(16))) uint16_t wv[NW_S][32 * D];
+    __shared__ __attribute__((aligned(16))) float wks[NW_S][32];
+    // this wave's copy instructions per cache tile: K and V codes, one scale row
+    constexpr int PER_TILE = 2 * (KT * D / 1024) / NW_S + 1;
+    static_assert(STQ - 2 <= 1, "wait_later covers one later tile");
+
+    int qt, bh, split;
+    decode_block(1, nsplit, qt, bh, split);
+    const int BH = g.B * g.Hkv;
+    const int b = bh / g.Hkv, h = bh % g.Hkv;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l32 = lane & 31, half = lane >> 5;
+    const int W = g.C + g.S;
+
+    bf16x8 qf[RB][D / 16];
+    load_q<D>(qf, q, g, b, h, 0, l32, half);
+    const LdsOffsets<D> off(lane);
+    float* lg_row = (l32 < g.R) ? logits + ((size_t)bh * g.R + l32) * W : nullptr;
+
+    const TileRange tr = tile_range(g, 0);
+    const int t_begin = (int)((long)split * tr.total / nsplit);
+    const int t_end = (int)((long)(split + 1) * tr.total / nsplit);
+    const int c_end = min(t_end, tr.n_ct);       // cache tiles of this split: [t_begin, c_end)
+    const size_t row0 = (size_t)bh * g.C;
+    const uint16_t* kn_bh = kn + (size_t)bh * g.S * D;
+    const uint16_t* vn_bh = vn + (size_t)bh * g.S * D;
+    uint16_t* mv = wv[wave];
+    float* mks = wks[wave];
+
+    float m_ref[RB], m_seen[RB], l_acc[RB], lt_acc[RB];
+    f32x16 o_acc[RB][D / 32];
+    m_seen[0] = -INFINITY;
+    auto issue = [&](int t, int sb) {
+        issue_tile_i8<D, NW_S, KT, true>(stg[sb], qc.kc + row0 * D, t * KT, g.n, wave, lane);
+        issue_tile_i8<D, NW_S, KT, true>(stg[sb] + KT * D, qc.vc + row0 * D, t * KT, g.n, wave,
+                                         lane);
+        issue_scales<0, 1>(ssc[sb][0], ssc[sb][1], qc.ks + row0, qc.vs + row0, t * KT, g.n,
+                           wave, lane);
+    };
+    // V rows wave*32 .. +31 of a staged cache tile -> this wave's bf16 block
+    auto convert_mine = [&](int sb) {
+        constexpr int CPR = D / 16;
+#pragma unroll
+        for (int u0 = 0; u0 < 32 * CPR; u0 += 64) {
+            const int u = u0 + lane;
+            const int r = u / CPR, c = u % CPR;
+            const int key = wave * 32 + r;
+            u32x4 lo, hi;
+            i8x16_to_bf16_scaled(
+                *(const u32x4*)(stg[sb] + KT * D + key * D + 16 * (c ^ i8_swz<D>(key))),
+                ssc[sb][1][key], lo, hi);
+            *(u32x4*)(mv + tile_off<D, true>(r, 2 * c)) = lo;
+            *(u32x4*)(mv + tile_off<D, true>(r, 2 * c + 1)) = hi;
+        }
+        if (lane < 32) mks[lane] = ssc[sb][0][wave * 32 + lane];
+    };
+
+    for (int sweep = 0; sweep < 2; ++sweep) {
+        bool overflow = false;
+        m_ref[0] = (sweep == 0) ? -INFINITY : m_seen[0];
+        l_acc[0] = 0.f;
+        lt_acc[0] = 0.f;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) o_acc[0][db][v] = 0.f;
+        for (int i = 0; i < STQ - 1 && t_begin + i < c_end; ++i) issue(t_begin + i, i);
+        wait_tiles();
+        __syncthreads();
+        for (int t = t_begin; t < c_end; ++t) {
+            const int sb = (t - t_begin) % STQ;
+            const int key0 = t * KT;
+            // the staging buffer of tile t+2 was last read by tile t-1, which
+            // every wave finished before the barrier that ended it
+            if (t + STQ - 1 < c_end) issue(t + STQ - 1, (sb + STQ - 1) % STQ);
+            convert_mine(sb);
+            fwd_block<D, true, true, true>(nullptr, mv, off, qf, o_acc, m_ref, m_seen, overflow,
+                                           l_acc, lt_acc, g.c, wave, key0, g.n, false, g.G, 0,
+                                           lane, sweep == 0 ? lg_row : nullptr, key0, 0, mks,
+                                           stg[sb] + (size_t)wave * 32 * D);
+            // tile t+1 must have landed; a tile issued after it may stay in flight
+            wait_later<PER_TILE>(min(STQ - 2, c_end - 1 - (t + 1)));
+            __syncthreads();
+        }
+        if (t_end > tr.n_ct) {   // the chunk tile (S <= 32 here: a single tile)
+            const int key0 = (t_end - 1 - tr.n_ct) * KT;
+            // this wave's 32 rows straight from the bf16 chunk: V into its
+            // bf16 block, K into a bf16 block of its own in the (now idle)
+            // staging buffer 0
+            uint16_t* mk = (uint16_t*)(stg[0]) + (size_t)wave * 32 * D;
+            constexpr int CPR = D / 8;
+#pragma unroll
+            for (int u0 = 0; u0 < 32 * CPR; u0 += 64) {
+                const int u = u0 + lane;
+                const int r = u / CPR, cc = u % CPR;
+                const int key = min(key0 + wave * 32 + r, g.S - 1);
+                *(u32x4*)(mk + tile_off<D, false>(r, cc)) =
+                    *(const u32x4*)(kn_bh + (size_t)key * D + cc * 8);
+                *(u32x4*)(mv + tile_off<D, true>(r, cc)) =
+                    *(const u32x4*)(vn_bh + (size_t)key * D + cc * 8);
+            }
+            if (lane < 32) mks[lane] = 1.f;
+            fwd_block<D, true, true>(mk, mv, off, qf, o_acc, m_ref, m_seen, overflow, l_acc,
+                                     lt_acc, g.c, wave, key0, g.S, true, g.G, 0, lane,
+                                     sweep == 0 ? lg_row : nullptr, g.C + key0, 0, mks);
+        }
+        if (!__syncthreads_or(overflow)) break;
+    }
+
+    // merge the waves' (m, l, lt, O) through LDS (the staging buffers are free)
+    const float l = l_acc[0] + xor32(l_acc[0]);
+    const float lt = lt_acc[0] + xor32(lt_acc[0]);
+    constexpr int XS = D / 2 + 4;
+    static_assert(NW_S * 64 * XS * 4 <= (int)sizeof(stg), "merge area exceeds the staging");
+    float* xch = (float*)&stg[0][0];
+    float* mine = xch + ((size_t)wave * 64 + lane) * XS;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) mine[db * 16 + v] = o_acc[0][db][v];
+    mine[D / 2 + 0] = m_ref[0];
+    mine[D / 2 + 1] = l;
+    mine[D / 2 + 2] = lt;
+    __syncthreads();
+    if (wave != 0) return;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < NW_S; ++w) M = fmaxf(M, xch[((size_t)w * 64 + lane) * XS + D / 2]);
+    float wt[NW_S], L = 0.f, Lt = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW_S; ++w) {
+        const float* o = xch + ((size_t)w * 64 + lane) * XS;
+        wt[w] = (M == -INFINITY) ? 0.f : fast_exp2(o[D / 2] - M);
+        L += wt[w] * o[D / 2 + 1];
+        Lt += wt[w] * o[D / 2 + 2];
+    }
+    const int r = l32;
+    if (r >= g.R) return;
+    const size_t prow = ((size_t)split * BH + bh) * g.rows_pad + r;
+    if (half == 0) *(f32x4*)(ml_part + prow * 4) = f32x4{M, L, Lt, 0.f};
+    float* orow = o_part + prow * D;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int gq = 0; gq < 4; ++gq) {
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int w = 0; w < NW_S; ++w) {
+                const float* o = xch + ((size_t)w * 64 + lane) * XS + db * 16 + 4 * gq;
+                acc += wt[w] * f32x4{o[0], o[1], o[2], o[3]};
+            }
+            *(f32x4*)(orow + db * 32 + 8 * gq + 4 * half) = acc;
+        }
+}
+
+// ---------------------------------------------------------------------------
 // sum the row-tile partials in tile order
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void wsum_reduce_kernel(
@@ -722,9 +1263,11 @@ int pick_split(int base_blocks, int max_tiles, int target) {
     return want < 1 ? 1 : want;
 }
 
-template <int D>
+
+// Q8: the cache is int8 codes + scales (qc); otherwise bf16 (kc, vc).
+template <int D, bool Q8>
 hipError_t launch_attention_d(const AttnPlan& pl, const uint16_t* q,
-                              const uint16_t* kc, const uint16_t* vc,
+                              const uint16_t* kc, const uint16_t* vc, const Q8Cache& qc,
                               const uint16_t* kn, const uint16_t* vn, float* out,
                               float* lse, float* wsum, void* ws,
                               hipStream_t stream, bool sync_debug, hipEvent_t* ev) {
@@ -751,12 +1294,21 @@ hipError_t launch_attention_d(const AttnPlan& pl, const uint16_t* q,
     } while (0)
 
     H2O_EVENT(0);
-    if (pl.small)
-        hipLaunchKernelGGL(attn_fwd_small_kernel<D>, dim3(BH * pl.split1), dim3(NT_S), 0,
-                           stream, g, pl.split1, q, kc, vc, kn, vn, o_part, ml_part, wpart);
-    else
-        hipLaunchKernelGGL(attn_fwd_kernel<D>, dim3(g.n_qt * BH * pl.split1), dim3(NT), 0,
-                           stream, g, pl.split1, q, kc, vc, kn, vn, o_part, ml_part);
+    if constexpr (Q8) {
+        if (pl.small)
+            hipLaunchKernelGGL(attn_fwd_small_q8_kernel<D>, dim3(BH * pl.split1), dim3(NT_S), 0,
+                               stream, g, pl.split1, q, qc, kn, vn, o_part, ml_part, wpart);
+        else
+            hipLaunchKernelGGL(attn_fwd_q8_kernel<D>, dim3(g.n_qt * BH * pl.split1), dim3(NT),
+                               0, stream, g, pl.split1, q, qc, kn, vn, o_part, ml_part);
+    } else {
+        if (pl.small)
+            hipLaunchKernelGGL(attn_fwd_small_kernel<D>, dim3(BH * pl.split1), dim3(NT_S), 0,
+                               stream, g, pl.split1, q, kc, vc, kn, vn, o_part, ml_part, wpart);
+        else
+            hipLaunchKernelGGL(attn_fwd_kernel<D>, dim3(g.n_qt * BH * pl.split1), dim3(NT), 0,
+                               stream, g, pl.split1, q, kc, vc, kn, vn, o_part, ml_part);
+    }
     H2O_CHECK();
     H2O_EVENT(1);
     {
@@ -774,8 +1326,12 @@ hipError_t launch_attention_d(const AttnPlan& pl, const uint16_t* q,
         H2O_CHECK();
         H2O_EVENT(3);
     } else {
-        hipLaunchKernelGGL(attn_colsum_kernel<D>, dim3(g.n_qt * BH * pl.split2), dim3(NT), 0,
-                           stream, g, pl.split2, q, kc, kn, l2, wpart);
+        if constexpr (Q8)
+            hipLaunchKernelGGL(attn_colsum_q8_kernel<D>, dim3(g.n_qt * BH * pl.split2), dim3(NT),
+                               0, stream, g, pl.split2, q, qc, kn, l2, wpart);
+        else
+            hipLaunchKernelGGL(attn_colsum_kernel<D>, dim3(g.n_qt * BH * pl.split2), dim3(NT),
+                               0, stream, g, pl.split2, q, kc, kn, l2, wpart);
         H2O_CHECK();
         H2O_EVENT(3);
         hipLaunchKernelGGL(wsum_reduce_kernel, dim3((unsigned)((wtotal + 255) / 256)),
@@ -824,11 +1380,25 @@ hipError_t launch_attention(const AttnPlan& plan, const uint16_t* q, const uint1
                             const uint16_t* vc, const uint16_t* kn, const uint16_t* vn,
                             float* out, float* lse, float* wsum, void* ws,
                             hipStream_t stream, bool sync_debug, hipEvent_t* ev5) {
+    const Q8Cache none{nullptr, nullptr, nullptr, nullptr};
     if (plan.g.D == 64)
-        return launch_attention_d<64>(plan, q, kc, vc, kn, vn, out, lse, wsum, ws, stream,
-                                      sync_debug, ev5);
-    return launch_attention_d<128>(plan, q, kc, vc, kn, vn, out, lse, wsum, ws, stream,
-                                   sync_debug, ev5);
+        return launch_attention_d<64, false>(plan, q, kc, vc, none, kn, vn, out, lse, wsum, ws,
+                                             stream, sync_debug, ev5);
+    return launch_attention_d<128, false>(plan, q, kc, vc, none, kn, vn, out, lse, wsum, ws,
+                                          stream, sync_debug, ev5);
+}
+
+hipError_t launch_attention_q8(const AttnPlan& plan, const uint16_t* q, const int8_t* kc,
+                               const float* ks, const int8_t* vc, const float* vs,
+                               const uint16_t* kn, const uint16_t* vn, float* out, float* lse,
+                               float* wsum, void* ws, hipStream_t stream, bool sync_debug,
+                               hipEvent_t* ev5) {
+    const Q8Cache qc{kc, ks, vc, vs};
+    if (plan.g.D == 64)
+        return launch_attention_d<64, true>(plan, q, nullptr, nullptr, qc, kn, vn, out, lse,
+                                            wsum, ws, stream, sync_debug, ev5);
+    return launch_attention_d<128, true>(plan, q, nullptr, nullptr, qc, kn, vn, out, lse, wsum,
+                                         ws, stream, sync_debug, ev5);
 }
 
 }  // namespace h2o

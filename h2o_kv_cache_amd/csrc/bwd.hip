@@ -77,17 +77,6 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const BwdGeom g,
 // ---------------------------------------------------------------------------
 constexpr int BR = 32;   // rows per row block / keys per key block
 
-// One 4-byte HBM -> LDS copy per lane (global_load_lds_dword): lane l writes
-// bytes [4*l, 4*l + 4) past the wave-uniform LDS address `lds`.  As with the
-// 16-byte copy, written as asm without register outputs; completion is
-// awaited with wait_tiles() before the barrier that publishes the data.
-__device__ __forceinline__ void dma4(const float* gptr, uint32_t lds) {
-    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, off"
-                 :
-                 : "s"(lds), "v"(gptr)
-                 : "memory", "m0");
-}
-
 // Copy packed rows r0 .. r0+ROWS-1 of q or dO (base = the tensor at head
 // h*G, query 0) into a ROWS x D LDS tile with swizzle VT.  The rows of one
 // tile come from G different heads, so every 16-byte chunk computes its own

@@ -41,6 +41,14 @@ hipError_t launch_attention(const AttnPlan& plan, const uint16_t* q,
                             hipStream_t stream, bool sync_debug,
                             hipEvent_t* ev5 /* nullable: 5 timing events */);
 
+// The same attention over an 8-bit cache: int8 codes [B, Hkv, C, D] and one
+// float scale per row [B, Hkv, C] for K and V; same plan and workspace.
+hipError_t launch_attention_q8(const AttnPlan& plan, const uint16_t* q, const int8_t* kc,
+                               const float* ks, const int8_t* vc, const float* vs,
+                               const uint16_t* kn, const uint16_t* vn, float* out, float* lse,
+                               float* wsum, void* ws, hipStream_t stream, bool sync_debug,
+                               hipEvent_t* ev5 /* nullable: 5 timing events */);
+
 // Backward of the attention (bwd.hip).
 struct BwdGeom {
     int B, Hq, Hkv, G, D, C, S, n;
@@ -71,6 +79,15 @@ hipError_t launch_kv_scatter(int BH, int D, int C, int S, uint16_t* kc,
                              const uint16_t* kn, const uint16_t* vn,
                              const float* new_scores, const int32_t* evict_idx,
                              int64_t p0, hipStream_t stream);
+
+// 8-bit cache rows (one scale per row) from bf16 rows, and the scatter of a
+// chunk into an 8-bit cache.
+hipError_t launch_quantize_rows(const uint16_t* x, long rows, int D, int8_t* codes,
+                                float* scales, hipStream_t stream);
+hipError_t launch_kv_scatter_q8(int BH, int D, int C, int S, int8_t* kc, float* ks, int8_t* vc,
+                                float* vs, float* scores, int64_t* pos, const uint16_t* kn,
+                                const uint16_t* vn, const float* new_scores,
+                                const int32_t* evict_idx, int64_t p0, hipStream_t stream);
 
 // SnapKV one-shot choice: keep_idx[bh][0..budget) = the budget valid slots
 // (of n) that are not among the n - budget lowest (wsum, slot), ascending.

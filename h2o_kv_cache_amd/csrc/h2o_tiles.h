@@ -62,6 +62,16 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
     return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
 
+// One 4-byte HBM -> LDS copy per lane (global_load_lds_dword): lane l writes
+// bytes [4*l, 4*l + 4) past the wave-uniform LDS address `lds`.  Same
+// contract as dma16.
+__device__ __forceinline__ void dma4(const float* gptr, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, off"
+                 :
+                 : "s"(lds), "v"(gptr)
+                 : "memory", "m0");
+}
+
 // Issue the HBM -> LDS copy of one ROWS x D tile: each wave instruction fills
 // 1 KiB of LDS, and each lane fetches the global chunk that belongs at its
 // LDS slot.  Rows past `lim` re-read row lim-1, a valid row whose weight is
@@ -82,6 +92,87 @@ __device__ __forceinline__ void issue_tile(uint16_t* tile, const uint16_t* __res
         const int gkey = min(key0 + key, lim - 1);
         dma16(src + (size_t)gkey * D + chunk * 8, base + blk * 1024);
     }
+}
+
+// 8-bit cache tiles: ROWS x D int8 codes, row-major and unswizzled (they are
+// converted to bf16 tiles, not read as MFMA operands), copied by waves
+// 0..NW-1 in 1 KiB blocks; rows past `lim` re-read row lim-1.  The per-row
+// scales of the same rows go to `ksc` / `vsc` (ROWS floats each) with one
+// 4-byte copy per lane: wave SW_K copies the K scales, wave SW_V the V
+// scales (ROWS == 64).
+//   SWZ: chunk c of row `key` is stored at chunk position c ^ (key mod CPR),
+//   so that 32 lanes reading the same chunk of 32 rows spread over the banks.
+template <int D>
+__device__ __forceinline__ int i8_swz(int key) { return key & (D / 16 - 1); }
+
+template <int D, int NW, int ROWS = kKeyTile, bool SWZ = false>
+__device__ __forceinline__ void issue_tile_i8(uint8_t* tile, const int8_t* __restrict__ src,
+                                              int key0, int lim, int wave, int lane) {
+    constexpr int CPR = D / 16;                  // 16-byte chunks per row
+    constexpr int NBLK = ROWS * CPR / 64;        // 1 KiB blocks per tile
+    const uint32_t base = __builtin_amdgcn_readfirstlane(lds_addr(tile));
+#pragma unroll
+    for (int blk0 = 0; blk0 < NBLK; blk0 += NW) {
+        const int blk = blk0 + wave;
+        if (blk < NBLK) {
+            const int p = blk * 64 + lane;
+            const int key = p / CPR, c = (p % CPR) ^ (SWZ ? i8_swz<D>(p / CPR) : 0);
+            const int gkey = min(key0 + key, lim - 1);
+            dma16((const uint16_t*)(src + (size_t)gkey * D + c * 16), base + blk * 1024);
+        }
+    }
+}
+
+template <int SW_K, int SW_V>
+__device__ __forceinline__ void issue_scales(float* ksc, float* vsc, const float* __restrict__ ks,
+                                             const float* __restrict__ vs, int key0, int lim,
+                                             int wave, int lane) {
+    const int gkey = min(key0 + lane, lim - 1);
+    if (wave == SW_K) dma4(ks + gkey, __builtin_amdgcn_readfirstlane(lds_addr(ksc)));
+    if (wave == SW_V) dma4(vs + gkey, __builtin_amdgcn_readfirstlane(lds_addr(vsc)));
+}
+
+// 16 int8 codes (4 dwords) -> two 8-element bf16 chunks: exact (codes are
+// integers of at most 7 bits), or times `s` rounded to nearest even.
+__device__ __forceinline__ float i8_at(uint32_t w, int k) {
+    return (float)(int)(int8_t)(w >> (8 * k));
+}
+
+__device__ __forceinline__ void i8x16_to_bf16(const u32x4 in, u32x4& lo, u32x4& hi) {
+    uint32_t out[8];
+#pragma unroll
+    for (int p = 0; p < 8; ++p) {
+        const uint32_t w = in[p >> 1];
+        const int k = 2 * (p & 1);
+        // an integer of at most 8 significant bits: its bf16 is the high half
+        out[p] = pack_hi(__float_as_uint(i8_at(w, k)), __float_as_uint(i8_at(w, k + 1)));
+    }
+    lo = u32x4{out[0], out[1], out[2], out[3]};
+    hi = u32x4{out[4], out[5], out[6], out[7]};
+}
+
+// 8 int8 codes (2 dwords) -> one exact bf16 chunk
+__device__ __forceinline__ bf16x8 i8x8_to_bf16(const uint2 in) {
+    uint32_t out[4];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+        const uint32_t w = (p < 2) ? in.x : in.y;
+        const int k = 2 * (p & 1);
+        out[p] = pack_hi(__float_as_uint(i8_at(w, k)), __float_as_uint(i8_at(w, k + 1)));
+    }
+    return as_bf16x8(u32x4{out[0], out[1], out[2], out[3]});
+}
+
+__device__ __forceinline__ void i8x16_to_bf16_scaled(const u32x4 in, float s, u32x4& lo,
+                                                     u32x4& hi) {
+    bf16x8 a, b;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        a[e] = (__bf16)(i8_at(in[e >> 2], e & 3) * s);
+        b[e] = (__bf16)(i8_at(in[2 + (e >> 2)], e & 3) * s);
+    }
+    lo = __builtin_bit_cast(u32x4, a);
+    hi = __builtin_bit_cast(u32x4, b);
 }
 
 // All of this wave's outstanding tile copies (and other memory ops) done.

@@ -410,7 +410,120 @@ __global__ __launch_bounds__(256) void kv_scatter_kernel(
     }
 }
 
+// ---------------------------------------------------------------------------
+// 8-bit cache rows: scale = amax / 127 and code = round-half-even(x / scale),
+// both as correctly rounded fp32 divisions (so the codes are a function of
+// the row alone); |code| <= 127; a row of zeros gets scale 0 and codes 0.
+// D / 8 consecutive lanes hold one row, 8 values each.
+// ---------------------------------------------------------------------------
+template <int D>
+__device__ __forceinline__ void quantize_piece(const u32x4 x, bool ok, uint2& codes,
+                                               float& scale) {
+    constexpr int LPR = D / 8;
+    float f[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const uint32_t w = x[e >> 1];
+        f[e] = __uint_as_float((e & 1) ? (w & 0xFFFF0000u) : (w << 16));
+    }
+    float amax = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(f[e]));
+    if (!ok) amax = 0.f;
+#pragma unroll
+    for (int off = 1; off < LPR; off <<= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 64));
+    scale = amax / 127.f;
+    uint32_t b[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        float c = (scale > 0.f) ? rintf(f[e] / scale) : 0.f;
+        c = fminf(fmaxf(c, -127.f), 127.f);
+        b[e] = (uint32_t)(int)c & 0xFFu;
+    }
+    codes.x = b[0] | (b[1] << 8) | (b[2] << 16) | (b[3] << 24);
+    codes.y = b[4] | (b[5] << 8) | (b[6] << 16) | (b[7] << 24);
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void quantize_rows_kernel(const uint16_t* __restrict__ x,
+                                                            long rows, int8_t* __restrict__ codes,
+                                                            float* __restrict__ scales) {
+    constexpr int LPR = D / 8;
+    const long row = ((long)blockIdx.x * 256 + threadIdx.x) / LPR;
+    const int part = threadIdx.x % LPR;
+    const bool ok = row < rows;
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (ok) v = *(const u32x4*)(x + row * D + part * 8);
+    uint2 c;
+    float sc;
+    quantize_piece<D>(v, ok, c, sc);
+    if (!ok) return;
+    *(uint2*)(codes + row * D + part * 8) = c;
+    if (part == 0) scales[row] = sc;
+}
+
+// scatter into an 8-bit cache: chunk token t -> slot evict[t], quantised
+template <int D>
+__global__ __launch_bounds__(256) void kv_scatter_q8_kernel(
+    int C, int S, int8_t* __restrict__ kc, float* __restrict__ ks, int8_t* __restrict__ vc,
+    float* __restrict__ vs, float* __restrict__ scores, int64_t* __restrict__ pos,
+    const uint16_t* __restrict__ kn, const uint16_t* __restrict__ vn,
+    const float* __restrict__ new_scores, const int32_t* __restrict__ evict, int64_t p0) {
+    constexpr int LPR = D / 8;
+    constexpr int TOK = 256 / (2 * LPR);   // tokens per workgroup
+    const int bh = blockIdx.y, tid = threadIdx.x;
+    const int tok = tid / (2 * LPR), which = (tid / LPR) & 1, part = tid % LPR;
+    const int t = blockIdx.x * TOK + tok;
+    const bool in = t < S;
+    const int slot = in ? evict[(size_t)bh * S + t] : -1;
+    const bool ok = in && slot >= 0 && slot < C;   // out-of-range index: nothing written
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (in) v = *(const u32x4*)((which ? vn : kn) + ((size_t)bh * S + t) * D + part * 8);
+    uint2 c;
+    float sc;
+    quantize_piece<D>(v, in, c, sc);
+    if (!ok) return;
+    const size_t row = (size_t)bh * C + slot;
+    *(uint2*)((which ? vc : kc) + row * D + part * 8) = c;
+    if (part == 0) (which ? vs : ks)[row] = sc;
+    if (which == 0 && part == 0) {
+        scores[row] = new_scores[(size_t)bh * S + t];
+        if (pos) pos[row] = p0 + t;
+    }
+}
+
 }  // namespace
+
+hipError_t launch_quantize_rows(const uint16_t* x, long rows, int D, int8_t* codes,
+                                float* scales, hipStream_t stream) {
+    const long threads = rows * (D / 8);
+    const unsigned blocks = (unsigned)((threads + 255) / 256);
+    if (D == 64)
+        hipLaunchKernelGGL(quantize_rows_kernel<64>, dim3(blocks), dim3(256), 0, stream, x,
+                           rows, codes, scales);
+    else
+        hipLaunchKernelGGL(quantize_rows_kernel<128>, dim3(blocks), dim3(256), 0, stream, x,
+                           rows, codes, scales);
+    return hipGetLastError();
+}
+
+hipError_t launch_kv_scatter_q8(int BH, int D, int C, int S, int8_t* kc, float* ks, int8_t* vc,
+                                float* vs, float* scores, int64_t* pos, const uint16_t* kn,
+                                const uint16_t* vn, const float* new_scores,
+                                const int32_t* evict_idx, int64_t p0, hipStream_t stream) {
+    if (D == 64) {
+        constexpr int TOK = 256 / (2 * (64 / 8));
+        hipLaunchKernelGGL(kv_scatter_q8_kernel<64>, dim3((S + TOK - 1) / TOK, BH), dim3(256),
+                           0, stream, C, S, kc, ks, vc, vs, scores, pos, kn, vn, new_scores,
+                           evict_idx, p0);
+    } else {
+        constexpr int TOK = 256 / (2 * (128 / 8));
+        hipLaunchKernelGGL(kv_scatter_q8_kernel<128>, dim3((S + TOK - 1) / TOK, BH), dim3(256),
+                           0, stream, C, S, kc, ks, vc, vs, scores, pos, kn, vn, new_scores,
+                           evict_idx, p0);
+    }
+    return hipGetLastError();
+}
 
 hipError_t launch_score_accumulate(int BH, int C, int S, int n, float* scores,
                                    float* new_scores, const float* wsum,

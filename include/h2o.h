@@ -148,6 +148,47 @@ h2o_status_t kv_scatter(const h2o_shape_t* shape, uint16_t* k_cache,
                         const float* new_scores, const int32_t* evict_idx,
                         int64_t p0, void* stream);
 
+/* 8-bit KV cache (Q-Hitter-like H2O).  ([LtF] Chinese page §2: cache
+ * buffers can be quantised to 8 bits or fewer; Q-Hitter combines H2O with
+ * such quantisation.)  Reading used here: every cached (token, KV head) row
+ * is stored as D int8 codes plus one fp32 scale, scale = amax / 127 (amax =
+ * the row's largest |x|), code = round-half-even(x / scale), both correctly
+ * rounded fp32 divisions, |code| <= 127; a row of zeros has scale 0.  Rows
+ * must be finite.  Attention reads the cache rows as code * scale; the
+ * chunk's own K/V are used unquantised in their step and quantised when
+ * written into the cache.  Score accumulation and the slot choice are the
+ * unchanged calls above.  The int8 cache halves the bytes attention reads
+ * from HBM per cached key (2*(D + 4) instead of 4*D).
+ *
+ * h2o_attn_chunk_q8: as h2o_attn_chunk, with the cache given as
+ *   k_cache, v_cache [B, Hkv, C, D] int8 codes
+ *   k_scale, v_scale [B, Hkv, C]    fp32 per-row scales
+ * and the same workspace (h2o_workspace_size).  Inside, a logit of a cache
+ * key is (q . codes) * scale * tau with the codes converted exactly to bf16;
+ * a value row enters the PV product as bf16(code * scale). */
+h2o_status_t h2o_attn_chunk_q8(const h2o_shape_t* shape, const uint16_t* q,
+                               const int8_t* k_cache, const float* k_scale,
+                               const int8_t* v_cache, const float* v_scale,
+                               const uint16_t* k_new, const uint16_t* v_new,
+                               float* out, float* lse, float* wsum, void* ws,
+                               size_t ws_bytes, void* stream);
+
+/* Step 4 into an 8-bit cache: chunk token t is quantised (as above) and
+ * written to slot evict_idx[t] -- codes, scale, score, position; arguments
+ * as for kv_scatter with the cache as codes + scales. */
+h2o_status_t kv_scatter_q8(const h2o_shape_t* shape, int8_t* k_cache, float* k_scale,
+                           int8_t* v_cache, float* v_scale, float* scores,
+                           int64_t* pos, const uint16_t* k_new,
+                           const uint16_t* v_new, const float* new_scores,
+                           const int32_t* evict_idx, int64_t p0, void* stream);
+
+/* Quantise n_rows bf16 rows of head_dim values (x [n_rows, head_dim]) into
+ * codes [n_rows, head_dim] int8 and scales [n_rows] fp32, as above: for
+ * building an 8-bit cache from bf16 K/V (e.g. after a prefill). */
+h2o_status_t h2o_quantize_rows_q8(const uint16_t* x, int64_t n_rows,
+                                  int32_t head_dim, int8_t* codes,
+                                  float* scales, void* stream);
+
 /* SnapKV-style one-shot choice ([LtF] Chinese page §2: SnapKV scores cache
  * entries with H2O-like summed attention weights but makes the choice at a
  * single point of the generation).  Reading used here: the choice is made

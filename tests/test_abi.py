@@ -192,3 +192,14 @@ def test_snapkv_argument_checks(lib):
     # the output cache may not overlap an input (k_out placed on the chunk rows)
     assert comp(k_out=A) == I
     assert comp(k_out=O, v_out=ctypes.c_void_p((1 << 32) + (1 << 30) + 4096)) == I
+
+
+def test_binding_argument_counts_match_the_header(lib):
+    # every ctypes declaration takes as many arguments as include/h2o.h says
+    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    for name in _declared_functions():
+        m = re.search(rf"\b{name}\s*\(([^)]*)\)\s*;", text, flags=re.S)
+        assert m, name
+        params = [p for p in m.group(1).split(",") if p.strip() and p.strip() != "void"]
+        argtypes = getattr(lib, name).argtypes
+        assert argtypes is not None and len(argtypes) == len(params), (name, len(params))
