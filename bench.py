@@ -46,6 +46,9 @@ def parse():
                     help="print a summary of a rocprofv3 --stats csv run and exit")
     ap.add_argument("--summarize-pmc", metavar="DIR",
                     help="print per-kernel FETCH_SIZE/WRITE_SIZE of a rocprofv3 --pmc csv run")
+    ap.add_argument("--serial-policy", action="store_true",
+                    help="issue the policy calls (accumulate, choice, scatter) on the same "
+                         "stream as the attention instead of a second stream")
     ap.add_argument("--kv8", action="store_true",
                     help="8-bit KV cache (int8 codes + one fp32 scale per row): attention "
                          "over the int8 cache and the quantising scatter")
@@ -534,31 +537,51 @@ def main():
     inputs = make_inputs(wl, args.warmup + args.steps, gen)
     out = torch.empty((B, Hq, S, D), dtype=torch.float32, device="cuda")
     lse = torch.empty((B, Hq, S), dtype=torch.float32, device="cuda")
-    wsum = torch.empty((B, Hkv, C + S), dtype=torch.float32, device="cuda")
-    new_scores = torch.empty((B, Hkv, S), dtype=torch.float32, device="cuda")
-    evict = torch.empty((B, Hkv, S), dtype=torch.int32, device="cuda")
+    # per layer: the policy calls of a layer may still run while the next
+    # layer's attention writes its own summed weights
+    for st in layers:
+        st["wsum"] = torch.empty((B, Hkv, C + S), dtype=torch.float32, device="cuda")
+        st["new_scores"] = torch.empty((B, Hkv, S), dtype=torch.float32, device="cuda")
+        st["evict"] = torch.empty((B, Hkv, S), dtype=torch.int32, device="cuda")
     ws = torch.empty(h2o.h2o_workspace_size(shape), dtype=torch.uint8, device="cuda")
     stream = torch.cuda.current_stream()
+    # The policy calls of layer l (accumulate, choice, scatter) need only that
+    # layer's summed weights; the attention of layer l+1 does not depend on
+    # them, and the attention of layer l at the next step needs the scatter.
+    # They run on a second stream (default priority), ordered by events.
+    # With one layer there is nothing to overlap (the next step's attention
+    # waits for the scatter), and the events only add latency.
+    pstream = stream if (args.serial_policy or L == 1) else torch.cuda.Stream()
+    ev_attn = [torch.cuda.Event() for _ in range(L)]
+    ev_pol = [torch.cuda.Event() for _ in range(L)]
     p0_base = (C // S + 2) * S
 
     def run_step(i):
         p0 = p0_base + i * S
         for li, st in enumerate(layers):
             q, kn, vn = inputs[i][li]
+            wsum, new_scores, evict = st["wsum"], st["new_scores"], st["evict"]
+            if pstream is not stream:
+                stream.wait_event(ev_pol[li])        # the cache after last step's scatter
             if args.kv8:
                 h2o.h2o_attn_chunk_q8(shape, q, st["kq"], st["ks"], st["vq"], st["vs"], kn, vn,
                                       out, lse, wsum, ws, stream)
             else:
                 h2o.h2o_attn_chunk(shape, q, st["k"], st["v"], kn, vn, out, lse, wsum, ws,
                                    stream)
-            h2o.h2o_score_accumulate(shape, st["scores"], new_scores, wsum, stream)
-            h2o.h2o_evict_select(shape, st["scores"], evict, stream)
+            if pstream is not stream:
+                ev_attn[li].record(stream)
+                pstream.wait_event(ev_attn[li])
+            h2o.h2o_score_accumulate(shape, st["scores"], new_scores, wsum, pstream)
+            h2o.h2o_evict_select(shape, st["scores"], evict, pstream)
             if args.kv8:
                 h2o.kv_scatter_q8(shape, st["kq"], st["ks"], st["vq"], st["vs"], st["scores"],
-                                  st["pos"], kn, vn, new_scores, evict, p0, stream)
+                                  st["pos"], kn, vn, new_scores, evict, p0, pstream)
             else:
                 h2o.kv_scatter(shape, st["k"], st["v"], st["scores"], st["pos"], kn, vn,
-                               new_scores, evict, p0, stream)
+                               new_scores, evict, p0, pstream)
+            if pstream is not stream:
+                ev_pol[li].record(pstream)
 
     if args.calib_copy:   # a copy of known size, to scale the HBM byte counters
         src = torch.empty(CALIB_BYTES // 4, dtype=torch.float32, device="cuda").fill_(1.0)
@@ -578,6 +601,7 @@ def main():
     t_start.record(stream)
     for i in range(args.steps):
         run_step(args.warmup + i)
+    stream.wait_stream(pstream)               # the last policy calls end the step
     t_stop.record(stream)
     torch.cuda.synchronize()
     kernel_ms, calls = h2o.h2o_timing_stop()
@@ -627,6 +651,8 @@ def main():
             "kv_cache": "int8 codes + fp32 row scales" if args.kv8 else "bf16",
             "phase": "steady state: cache full, S slots evicted per KV head per layer",
             "ms_per_layer_step": per_layer,
+            "policy_stream": "same stream" if pstream is stream else
+                             "second stream, overlapped with the next layer's attention",
             "executed_mfma_tflops_whole_step": step_tflops,
             "executed_mfma_frac_whole_step": step_tflops / PEAK_BF16_TFLOPS,
         },
