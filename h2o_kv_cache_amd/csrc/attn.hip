@@ -49,12 +49,13 @@ struct TileRange {
     int n_ct, total;
 };
 
+template <int KTT = KT>
 __device__ __forceinline__ TileRange tile_range(const AttnGeom& g, int qt) {
     TileRange t;
-    t.n_ct = (g.n + KT - 1) / KT;
+    t.n_ct = (g.n + KTT - 1) / KTT;
     const int r_last = min((qt + 1) * kRowsPerBlock, g.R) - 1;
     const int i_max = r_last / g.G;
-    t.total = t.n_ct + i_max / KT + 1;
+    t.total = t.n_ct + i_max / KTT + 1;
     return t;
 }
 
@@ -580,16 +581,16 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(
 // the column sums of P = 2^(S*c - L2) over this wave's rows into colp.
 // MASKED handles the last partial cache tile (G == 0) and chunk tiles (G > 0:
 // row r sees chunk key t iff t*G <= r).
-template <int D, bool MASKED, bool KSC = false>
+template <int D, bool MASKED, bool KSC = false, int KTT = KT>
 __device__ __forceinline__ void colsum_tile(const uint16_t* Ks, const LdsOffsets<D>& off,
                                             float* colp,
                                             const bf16x8 (&qf)[RB][D / 16],
                                             const float (&l2v)[RB][16], float c, int key0,
                                             int lim, int G, int rbase, int l32, int half,
                                             const float* ksc = nullptr) {
-    float col[KT / 32];
+    float col[KTT / 32];
 #pragma unroll
-    for (int kb = 0; kb < KT / 32; ++kb) {
+    for (int kb = 0; kb < KTT / 32; ++kb) {
         f32x16 s[RB];
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb)
@@ -623,20 +624,24 @@ __device__ __forceinline__ void colsum_tile(const uint16_t* Ks, const LdsOffsets
     // region per tile, so the key blocks above schedule as one stretch)
     if (half == 0) {
 #pragma unroll
-        for (int kb = 0; kb < KT / 32; ++kb) colp[kb * 32 + l32] = col[kb];
+        for (int kb = 0; kb < KTT / 32; ++kb) colp[kb * 32 + l32] = col[kb];
     }
 }
 
 // ---------------------------------------------------------------------------
 // pass 2: column sums of P per row tile
 // ---------------------------------------------------------------------------
+// Pass 2 reads only K, so its tiles can be twice as long as pass 1's at the
+// same LDS budget (two workgroups per CU): half the barriers per key.
+constexpr int KT2 = 2 * KT;
+
 template <int D>
 __global__ __launch_bounds__(NT, 2) void attn_colsum_kernel(
     const AttnGeom g, const int nsplit, const uint16_t* __restrict__ q,
     const uint16_t* __restrict__ kc, const uint16_t* __restrict__ kn,
     const float* __restrict__ l2, float* __restrict__ wpart) {
-    __shared__ __attribute__((aligned(16))) uint16_t Ks[2][KT * D];
-    __shared__ float colp[2][kWaves][KT];
+    __shared__ __attribute__((aligned(16))) uint16_t Ks[2][KT2 * D];
+    __shared__ float colp[2][kWaves][KT2];
 
     int qt, bh, split;
     decode_block(g.n_qt, nsplit, qt, bh, split);
@@ -661,7 +666,7 @@ __global__ __launch_bounds__(NT, 2) void attn_colsum_kernel(
         for (int v = 0; v < 16; ++v)
             l2v[rb][v] = l2[(size_t)bh * g.rows_pad + rbase + rb * 32 + acc_row(v, half)];
 
-    const TileRange tr = tile_range(g, qt);
+    const TileRange tr = tile_range<KT2>(g, qt);
     const int t_begin = (int)((long)split * tr.total / nsplit);
     const int t_end = (int)((long)(split + 1) * tr.total / nsplit);
     const uint16_t* kc_bh = kc + (size_t)bh * g.C * D;
@@ -670,9 +675,9 @@ __global__ __launch_bounds__(NT, 2) void attn_colsum_kernel(
 
     // column sums of tile t are written to wpart after the barrier that ends it
     auto flush = [&](int t, int buf) {
-        if (tid < KT) {
+        if (tid < KT2) {
             const bool chunk = t >= tr.n_ct;
-            const int key = (chunk ? (t - tr.n_ct) * KT : t * KT) + tid;
+            const int key = (chunk ? (t - tr.n_ct) * KT2 : t * KT2) + tid;
             if (key < (chunk ? g.S : g.n)) {
                 float tot = colp[buf][0][tid];
 #pragma unroll
@@ -683,9 +688,9 @@ __global__ __launch_bounds__(NT, 2) void attn_colsum_kernel(
     };
     auto issue = [&](int t, int buf) {
         const bool chunk = t >= tr.n_ct;
-        const int key0 = chunk ? (t - tr.n_ct) * KT : t * KT;
-        issue_tile<D, false>(Ks[buf], chunk ? kn_bh : kc_bh, key0, chunk ? g.S : g.n, wave,
-                             lane);
+        const int key0 = chunk ? (t - tr.n_ct) * KT2 : t * KT2;
+        issue_tile<D, false, kWaves, KT2>(Ks[buf], chunk ? kn_bh : kc_bh, key0,
+                                          chunk ? g.S : g.n, wave, lane);
     };
     if (t_begin < t_end) issue(t_begin, 0);
     wait_tiles();
@@ -694,21 +699,21 @@ __global__ __launch_bounds__(NT, 2) void attn_colsum_kernel(
     for (int t = t_begin; t < t_end; ++t) {
         const int buf = (t - t_begin) & 1;
         const bool chunk = t >= tr.n_ct;
-        const int key0 = chunk ? (t - tr.n_ct) * KT : t * KT;
+        const int key0 = chunk ? (t - tr.n_ct) * KT2 : t * KT2;
         const int lim = chunk ? g.S : g.n;
         if (t + 1 < t_end) issue(t + 1, buf ^ 1);
         if (t > t_begin) flush(t - 1, buf ^ 1);
         if (live == 0) {
             if (half == 0) {
-                colp[buf][wave][l32] = 0.f;
-                colp[buf][wave][32 + l32] = 0.f;
+#pragma unroll
+                for (int kb = 0; kb < KT2 / 32; ++kb) colp[buf][wave][kb * 32 + l32] = 0.f;
             }
-        } else if (!chunk && key0 + KT <= g.n) {
-            colsum_tile<D, false>(Ks[buf], off, colp[buf][wave], qf, l2v, g.c, 0, 0, 0, rbase, l32,
-                                  half);
+        } else if (!chunk && key0 + KT2 <= g.n) {
+            colsum_tile<D, false, false, KT2>(Ks[buf], off, colp[buf][wave], qf, l2v, g.c, 0, 0,
+                                              0, rbase, l32, half);
         } else {
-            colsum_tile<D, true>(Ks[buf], off, colp[buf][wave], qf, l2v, g.c, key0, lim,
-                                 chunk ? g.G : 0, rbase, l32, half);
+            colsum_tile<D, true, false, KT2>(Ks[buf], off, colp[buf][wave], qf, l2v, g.c, key0,
+                                             lim, chunk ? g.G : 0, rbase, l32, half);
         }
         wait_tiles();
         __syncthreads();
@@ -1361,7 +1366,8 @@ bool make_attn_plan(int B, int Hq, int Hkv, int D, int C, int S, int n, float sc
     const int max_tiles = (C + KT - 1) / KT + (S + KT - 1) / KT;
     // pass 1 holds one workgroup per CU (few-row path: two), pass 2 two
     pl->split1 = pick_split(g.n_qt * BH, max_tiles, pl->small ? 1024 : 256);
-    pl->split2 = pl->small ? 1 : pick_split(g.n_qt * BH, max_tiles, 512);
+    const int max_tiles2 = (C + KT2 - 1) / KT2 + (S + KT2 - 1) / KT2;
+    pl->split2 = pl->small ? 1 : pick_split(g.n_qt * BH, max_tiles2, 512);
     auto align = [](size_t x) { return (x + 255) & ~(size_t)255; };
     size_t off = 0;
     pl->off_o = off;
