@@ -93,7 +93,11 @@ constexpr bf16x2 kOnes2 = {(__bf16)1.0f, (__bf16)1.0f};
 // columns col0 + (key - key0).  The block's rows sit at block lkb of the LDS
 // tiles (lkb = kb except for per-wave tiles).  KSC: the K tile holds int8
 // codes, and logit j is multiplied by the key's scale ksc[lkb*32 + j].
-template <int D, bool MASKED, bool KSC = false, bool K8 = false>
+// K8 / V8: K / V come straight from swizzled int8 tiles (k8, v8; V through
+// the 8-bit transposed read) and are converted exactly; with V8 the V scale
+// of key j (vsc[lkb*32 + j]) multiplies P before its bf16 rounding, and O is
+// normalised by the exact row sum (lt_acc = l_acc).
+template <int D, bool MASKED, bool KSC = false, bool K8 = false, bool V8 = false>
 __device__ __forceinline__ void fwd_block(const uint16_t* Ks, const uint16_t* Vs,
                                           const LdsOffsets<D>& off,
                                           const bf16x8 (&qf)[RB][D / 16],
@@ -103,7 +107,9 @@ __device__ __forceinline__ void fwd_block(const uint16_t* Ks, const uint16_t* Vs
                                           int kb, int key0, int lim, bool chunk, int G,
                                           int rbase, int lane, float* lg_row, int col0,
                                           int lkb, const float* ksc = nullptr,
-                                          const uint8_t* k8 = nullptr) {
+                                          const uint8_t* k8 = nullptr,
+                                          const uint8_t* v8 = nullptr,
+                                          const float* vsc = nullptr) {
     const int l32 = lane & 31, half = lane >> 5;
     {
         f32x16 s[RB];
@@ -185,6 +191,15 @@ __device__ __forceinline__ void fwd_block(const uint16_t* Ks, const uint16_t* Vs
         // lt_acc sums the bf16-rounded P that the PV MFMA sees, so that O is
         // normalised by the weights it was built from.
         bf16x8 pf[2][RB];
+        float vs16[16];
+        if (V8) {
+#pragma unroll
+            for (int g4 = 0; g4 < 4; ++g4) {
+                const f32x4 v4 = *(const f32x4*)(vsc + lkb * 32 + 8 * g4 + 4 * half);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) vs16[4 * g4 + e] = v4[e];
+            }
+        }
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) {
             const float m_use = (m_ref[rb] == -INFINITY) ? 0.f : m_ref[rb];
@@ -192,15 +207,20 @@ __device__ __forceinline__ void fwd_block(const uint16_t* Ks, const uint16_t* Vs
             for (int v = 0; v < 16; ++v) {
                 const float p = fast_exp2(fmaf(s[rb][v], c, -m_use));
                 l_acc[rb] += p;
-                pf[v >> 3][rb][v & 7] = (__bf16)p;
+                pf[v >> 3][rb][v & 7] = (__bf16)(V8 ? p * vs16[v] : p);
             }
+            if (V8) {
+                lt_acc[rb] = l_acc[rb];
+            } else {
 #pragma unroll
-            for (int hs = 0; hs < 2; ++hs)
+                for (int hs = 0; hs < 2; ++hs)
 #pragma unroll
-                for (int e = 0; e < 8; e += 2) {
-                    const bf16x2 pair = {pf[hs][rb][e], pf[hs][rb][e + 1]};
-                    lt_acc[rb] = __builtin_amdgcn_fdot2_f32_bf16(pair, kOnes2, lt_acc[rb], false);
-                }
+                    for (int e = 0; e < 8; e += 2) {
+                        const bf16x2 pair = {pf[hs][rb][e], pf[hs][rb][e + 1]};
+                        lt_acc[rb] =
+                            __builtin_amdgcn_fdot2_f32_bf16(pair, kOnes2, lt_acc[rb], false);
+                    }
+            }
         }
 
         // k-step hs covers keys kb*32 + 16*hs + [0, 16) in the order lane-half
@@ -209,11 +229,23 @@ __device__ __forceinline__ void fwd_block(const uint16_t* Ks, const uint16_t* Vs
         for (int hs = 0; hs < 2; ++hs) {
             // keys kb*32 + 16*hs + 8*gg + 4*half + [0, 4): rows (kb*32 + 16*hs + 8*gg) below
             const uint32_t row_b = (uint32_t)(lkb * 32 + 16 * hs) * 2 * D;
+            // V8: this lane points at key row lkb*32 + 16*hs + 4*half + r8 of
+            // the int8 tile (r8 = {0,1,2,3,8,9,10,11}[(lane % 16) / 2]),
+            // columns 32*db + 16*((lane / 16) % 2) + 8*(lane % 2) + [0, 8)
+            const int j16 = lane & 15, b8 = j16 >> 1;
+            const int vrow = lkb * 32 + 16 * hs + 4 * half + (b8 & 3) + 8 * (b8 >> 2);
 #pragma unroll
             for (int db = 0; db < D / 32; ++db) {
-                const u32x2 lo = lds_read_tr(Vs, off.v[db] + row_b);
-                const u32x2 hi = lds_read_tr(Vs, off.v[db] + row_b + 8 * 2 * D);
-                const bf16x8 vf = as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]});
+                bf16x8 vf;
+                if constexpr (V8) {
+                    const int c16 = 2 * db + ((lane >> 4) & 1);
+                    vf = i8x8_to_bf16(lds_read_tr8(
+                        v8 + vrow * D + 16 * (c16 ^ i8_swz_v<D>(vrow)) + 8 * (j16 & 1)));
+                } else {
+                    const u32x2 lo = lds_read_tr(Vs, off.v[db] + row_b);
+                    const u32x2 hi = lds_read_tr(Vs, off.v[db] + row_b + 8 * 2 * D);
+                    vf = as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]});
+                }
 #pragma unroll
                 for (int rb = 0; rb < RB; ++rb)
                     o_acc[rb][db] = mfma32x32x16(vf, pf[hs][rb], o_acc[rb][db]);
@@ -1057,34 +1089,37 @@ __global__ __launch_bounds__(NT, 2) void attn_colsum_q8_kernel(
 }
 
 // few-row pass 1 over an 8-bit cache.  The waves take different 32-key
-// blocks of each tile.  K fragments are read straight from the staged int8
-// tile (swizzled) and converted in registers; each wave converts only its
-// own block of V into a bf16 block of its own, which the transposed reads
-// need.  Three staging buffers keep the workgroup small enough for two per
-// CU.  Every block runs the masked variant, so no branch separates
-// accumulator updates.
+// blocks of each tile.  Both K and V are read straight from the staged int8
+// tiles (K as row fragments, V through the 8-bit transposed read; each with
+// its own chunk swizzle) and converted exactly in registers; the K scale
+// multiplies the logit and the V scale multiplies P.  Without bf16 copies the
+// workgroup needs only its staging buffers, so three fit on a CU.  Every block
+// runs the masked variant, so no branch separates accumulator updates.
 constexpr int STQ = 3;                 // staging buffers: 2 cache tiles in flight
 
 template <int PT>
 __device__ __forceinline__ void wait_later(int later) {
-    if (later >= 1)
+    if (later >= 3)
+        wait_vm<3 * PT>();
+    else if (later == 2)
+        wait_vm<2 * PT>();
+    else if (later == 1)
         wait_vm<PT>();
     else
         wait_tiles();
 }
 
 template <int D>
-__global__ __launch_bounds__(NT_S, 2) void attn_fwd_small_q8_kernel(
+__global__ __launch_bounds__(NT_S, 3) void attn_fwd_small_q8_kernel(
     const AttnGeom g, const int nsplit, const uint16_t* __restrict__ q, const Q8Cache qc,
     const uint16_t* __restrict__ kn, const uint16_t* __restrict__ vn,
     float* __restrict__ o_part, float* __restrict__ ml_part, float* __restrict__ logits) {
     __shared__ __attribute__((aligned(16))) uint8_t stg[STQ][2 * KT * D];
     __shared__ __attribute__((aligned(16))) float ssc[STQ][2][KT];
-    __shared__ __attribute__((aligned(16))) uint16_t wv[NW_S][32 * D];
-    __shared__ __attribute__((aligned(16))) float wks[NW_S][32];
     // this wave's copy instructions per cache tile: K and V codes, one scale row
     constexpr int PER_TILE = 2 * (KT * D / 1024) / NW_S + 1;
-    static_assert(STQ - 2 <= 1, "wait_later covers one later tile");
+    static_assert(STQ - 2 <= 3, "wait_later covers up to three later tiles");
+    static_assert(STQ * 2 * KT * D >= 2 * KT * D * 2, "the bf16 chunk tile fits the staging");
 
     int qt, bh, split;
     decode_block(1, nsplit, qt, bh, split);
@@ -1107,35 +1142,16 @@ __global__ __launch_bounds__(NT_S, 2) void attn_fwd_small_q8_kernel(
     const size_t row0 = (size_t)bh * g.C;
     const uint16_t* kn_bh = kn + (size_t)bh * g.S * D;
     const uint16_t* vn_bh = vn + (size_t)bh * g.S * D;
-    uint16_t* mv = wv[wave];
-    float* mks = wks[wave];
 
     float m_ref[RB], m_seen[RB], l_acc[RB], lt_acc[RB];
     f32x16 o_acc[RB][D / 32];
     m_seen[0] = -INFINITY;
     auto issue = [&](int t, int sb) {
-        issue_tile_i8<D, NW_S, KT, true>(stg[sb], qc.kc + row0 * D, t * KT, g.n, wave, lane);
-        issue_tile_i8<D, NW_S, KT, true>(stg[sb] + KT * D, qc.vc + row0 * D, t * KT, g.n, wave,
-                                         lane);
+        issue_tile_i8<D, NW_S, KT, 1>(stg[sb], qc.kc + row0 * D, t * KT, g.n, wave, lane);
+        issue_tile_i8<D, NW_S, KT, 2>(stg[sb] + KT * D, qc.vc + row0 * D, t * KT, g.n, wave,
+                                      lane);
         issue_scales<0, 1>(ssc[sb][0], ssc[sb][1], qc.ks + row0, qc.vs + row0, t * KT, g.n,
                            wave, lane);
-    };
-    // V rows wave*32 .. +31 of a staged cache tile -> this wave's bf16 block
-    auto convert_mine = [&](int sb) {
-        constexpr int CPR = D / 16;
-#pragma unroll
-        for (int u0 = 0; u0 < 32 * CPR; u0 += 64) {
-            const int u = u0 + lane;
-            const int r = u / CPR, c = u % CPR;
-            const int key = wave * 32 + r;
-            u32x4 lo, hi;
-            i8x16_to_bf16_scaled(
-                *(const u32x4*)(stg[sb] + KT * D + key * D + 16 * (c ^ i8_swz<D>(key))),
-                ssc[sb][1][key], lo, hi);
-            *(u32x4*)(mv + tile_off<D, true>(r, 2 * c)) = lo;
-            *(u32x4*)(mv + tile_off<D, true>(r, 2 * c + 1)) = hi;
-        }
-        if (lane < 32) mks[lane] = ssc[sb][0][wave * 32 + lane];
     };
 
     for (int sweep = 0; sweep < 2; ++sweep) {
@@ -1156,36 +1172,40 @@ __global__ __launch_bounds__(NT_S, 2) void attn_fwd_small_q8_kernel(
             // the staging buffer of tile t+2 was last read by tile t-1, which
             // every wave finished before the barrier that ended it
             if (t + STQ - 1 < c_end) issue(t + STQ - 1, (sb + STQ - 1) % STQ);
-            convert_mine(sb);
-            fwd_block<D, true, true, true>(nullptr, mv, off, qf, o_acc, m_ref, m_seen, overflow,
-                                           l_acc, lt_acc, g.c, wave, key0, g.n, false, g.G, 0,
-                                           lane, sweep == 0 ? lg_row : nullptr, key0, 0, mks,
-                                           stg[sb] + (size_t)wave * 32 * D);
+            fwd_block<D, true, true, true, true>(nullptr, nullptr, off, qf, o_acc, m_ref, m_seen,
+                                                 overflow, l_acc, lt_acc, g.c, wave, key0, g.n,
+                                                 false, g.G, 0, lane,
+                                                 sweep == 0 ? lg_row : nullptr, key0, wave,
+                                                 ssc[sb][0], stg[sb], stg[sb] + KT * D,
+                                                 ssc[sb][1]);
             // tile t+1 must have landed; a tile issued after it may stay in flight
             wait_later<PER_TILE>(min(STQ - 2, c_end - 1 - (t + 1)));
             __syncthreads();
         }
         if (t_end > tr.n_ct) {   // the chunk tile (S <= 32 here: a single tile)
             const int key0 = (t_end - 1 - tr.n_ct) * KT;
-            // this wave's 32 rows straight from the bf16 chunk: V into its
-            // bf16 block, K into a bf16 block of its own in the (now idle)
-            // staging buffer 0
-            uint16_t* mk = (uint16_t*)(stg[0]) + (size_t)wave * 32 * D;
+            // bf16 K and V tiles in the (now idle) staging area: K in the
+            // space of buffer 0, V in that of buffer 1; each wave writes its
+            // own 32 rows straight from the chunk; K scales 1
+            uint16_t* mk = (uint16_t*)stg[0];
+            uint16_t* mv = (uint16_t*)stg[1];
             constexpr int CPR = D / 8;
 #pragma unroll
             for (int u0 = 0; u0 < 32 * CPR; u0 += 64) {
                 const int u = u0 + lane;
-                const int r = u / CPR, cc = u % CPR;
-                const int key = min(key0 + wave * 32 + r, g.S - 1);
+                const int r = wave * 32 + u / CPR, cc = u % CPR;
+                const int key = min(key0 + r, g.S - 1);
                 *(u32x4*)(mk + tile_off<D, false>(r, cc)) =
                     *(const u32x4*)(kn_bh + (size_t)key * D + cc * 8);
                 *(u32x4*)(mv + tile_off<D, true>(r, cc)) =
                     *(const u32x4*)(vn_bh + (size_t)key * D + cc * 8);
             }
-            if (lane < 32) mks[lane] = 1.f;
+            if (lane < 32) ssc[0][0][wave * 32 + lane] = 1.f;
             fwd_block<D, true, true>(mk, mv, off, qf, o_acc, m_ref, m_seen, overflow, l_acc,
                                      lt_acc, g.c, wave, key0, g.S, true, g.G, 0, lane,
-                                     sweep == 0 ? lg_row : nullptr, g.C + key0, 0, mks);
+                                     sweep == 0 ? lg_row : nullptr, g.C + key0, wave,
+                                     ssc[0][0]);
+            // the cache blocks set lt = l; this bf16 block adds its rounded weights
         }
         if (!__syncthreads_or(overflow)) break;
     }

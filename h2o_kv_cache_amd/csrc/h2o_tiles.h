@@ -105,7 +105,17 @@ __device__ __forceinline__ void issue_tile(uint16_t* tile, const uint16_t* __res
 template <int D>
 __device__ __forceinline__ int i8_swz(int key) { return key & (D / 16 - 1); }
 
-template <int D, int NW, int ROWS = kKeyTile, bool SWZ = false>
+//   V tiles read with the 8-bit transposed read: a 16-lane group reads 8
+//   rows key0 + {0,1,2,3,8,9,10,11} (key0 a multiple of 4 with bit 3 clear);
+//   chunk ^ ((key mod 4) | (key bit 3 moved to bit 2)) gives them 8 distinct
+//   chunk positions (4 at D = 64, where a row has only 4 chunks).
+template <int D>
+__device__ __forceinline__ int i8_swz_v(int key) {
+    return D >= 128 ? ((key & 3) | ((key >> 1) & 4)) : (key & 3);
+}
+
+// SWZ: 0 none, 1 i8_swz (K tiles), 2 i8_swz_v (V tiles)
+template <int D, int NW, int ROWS = kKeyTile, int SWZ = 0>
 __device__ __forceinline__ void issue_tile_i8(uint8_t* tile, const int8_t* __restrict__ src,
                                               int key0, int lim, int wave, int lane) {
     constexpr int CPR = D / 16;                  // 16-byte chunks per row
@@ -116,7 +126,8 @@ __device__ __forceinline__ void issue_tile_i8(uint8_t* tile, const int8_t* __res
         const int blk = blk0 + wave;
         if (blk < NBLK) {
             const int p = blk * 64 + lane;
-            const int key = p / CPR, c = (p % CPR) ^ (SWZ ? i8_swz<D>(p / CPR) : 0);
+            const int key = p / CPR;
+            const int c = (p % CPR) ^ (SWZ == 1 ? i8_swz<D>(key) : SWZ == 2 ? i8_swz_v<D>(key) : 0);
             const int gkey = min(key0 + key, lim - 1);
             dma16((const uint16_t*)(src + (size_t)gkey * D + c * 16), base + blk * 1024);
         }
@@ -161,6 +172,16 @@ __device__ __forceinline__ bf16x8 i8x8_to_bf16(const uint2 in) {
         out[p] = pack_hi(__float_as_uint(i8_at(w, k)), __float_as_uint(i8_at(w, k + 1)));
     }
     return as_bf16x8(u32x4{out[0], out[1], out[2], out[3]});
+}
+
+// 8-bit transposed LDS read (ds_read_b64_tr_b8).  In each 16-lane group,
+// output lane i receives byte i % 8 of the 8-byte pieces that input lanes
+// 2b + i / 8 (b = 0..7) point at, as its bytes b = 0..7.
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint2 lds_read_tr8(const uint8_t* p) {
+    const i32x2 v = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+        (__attribute__((address_space(3))) i32x2*)p);
+    return uint2{(uint32_t)v.x, (uint32_t)v.y};
 }
 
 __device__ __forceinline__ void i8x16_to_bf16_scaled(const u32x4 in, float s, u32x4& lo,
