@@ -582,20 +582,65 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(
         if (dc == 0) l2[(size_t)bh * g.rows_pad + r] = INFINITY;
         return;
     }
-    // per split: (m, l, lt) with l the exact and lt the bf16-weight row sum
+    // per split: (m, l, lt) with l the exact and lt the bf16-weight row sum.
+    // Splits are combined in order; the loads of CB splits are issued before
+    // any of them is used.
+    constexpr int CB = 8;
     float M = -INFINITY;
-    for (int s = 0; s < nsplit; ++s)
-        M = fmaxf(M, ml_part[(((size_t)s * BH + bh) * g.rows_pad + r) * 4]);
     float L = 0.f, Lt = 0.f;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    for (int s = 0; s < nsplit; ++s) {
-        const size_t prow = ((size_t)s * BH + bh) * g.rows_pad + r;
-        const f32x4 ml = *(const f32x4*)(ml_part + prow * 4);
-        const float w = fast_exp2(ml[0] - M);
-        L += w * ml[1];
-        Lt += w * ml[2];
-        const f32x4 o = *(const f32x4*)(o_part + prow * D + dc * 4);
-        acc += w * o;
+    if (nsplit <= 4) {   // few splits: one pass, all loads first
+        f32x4 ml[4], o[4];
+#pragma unroll
+        for (int sp = 0; sp < 4; ++sp) {
+            const size_t prow = ((size_t)sp * BH + bh) * g.rows_pad + r;
+            ml[sp] = sp < nsplit ? *(const f32x4*)(ml_part + prow * 4)
+                                 : f32x4{-INFINITY, 0.f, 0.f, 0.f};
+            o[sp] = sp < nsplit ? *(const f32x4*)(o_part + prow * D + dc * 4)
+                                : f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+#pragma unroll
+        for (int sp = 0; sp < 4; ++sp) M = fmaxf(M, ml[sp][0]);
+#pragma unroll
+        for (int sp = 0; sp < 4; ++sp) {
+            if (sp < nsplit) {
+                const float w = fast_exp2(ml[sp][0] - M);
+                L += w * ml[sp][1];
+                Lt += w * ml[sp][2];
+                acc += w * o[sp];
+            }
+        }
+    }
+    for (int s0 = 0; nsplit > 4 && s0 < nsplit; s0 += CB) {
+        float m[CB];
+#pragma unroll
+        for (int u = 0; u < CB; ++u) {
+            const int sp = s0 + u;
+            m[u] = sp < nsplit ? ml_part[(((size_t)sp * BH + bh) * g.rows_pad + r) * 4]
+                               : -INFINITY;
+        }
+#pragma unroll
+        for (int u = 0; u < CB; ++u) M = fmaxf(M, m[u]);
+    }
+    for (int s0 = 0; nsplit > 4 && s0 < nsplit; s0 += CB) {
+        f32x4 ml[CB], o[CB];
+#pragma unroll
+        for (int u = 0; u < CB; ++u) {
+            const int sp = s0 + u;
+            const size_t prow = ((size_t)sp * BH + bh) * g.rows_pad + r;
+            ml[u] = sp < nsplit ? *(const f32x4*)(ml_part + prow * 4) : f32x4{0.f, 0.f, 0.f, 0.f};
+            o[u] = sp < nsplit ? *(const f32x4*)(o_part + prow * D + dc * 4)
+                               : f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+#pragma unroll
+        for (int u = 0; u < CB; ++u) {
+            if (s0 + u < nsplit) {
+                const float w = fast_exp2(ml[u][0] - M);
+                L += w * ml[u][1];
+                Lt += w * ml[u][2];
+                acc += w * o[u];
+            }
+        }
     }
     const float inv = 1.0f / Lt;
     const int b = bh / g.Hkv, h = bh % g.Hkv;
@@ -1267,14 +1312,22 @@ __global__ __launch_bounds__(256) void wsum_reduce_kernel(
     if (idx >= (long)BH * W) return;
     const int j = (int)(idx % W);
     const int bh = (int)(idx / W);
+    // row tiles in order; the loads of 8 tiles are issued before their sums
+    // (the partials are >= 0, so the +0.0 of a skipped tile changes nothing)
     float s = 0.f;
-    if (j < g.n) {
-        for (int qt = 0; qt < g.n_qt; ++qt) s += wpart[((size_t)qt * BH + bh) * W + j];
-    } else if (j >= g.C) {
-        const int t = j - g.C;
-        for (int qt = 0; qt < g.n_qt; ++qt) {
-            const int i_hi = (min((qt + 1) * kRowsPerBlock, g.R) - 1) / g.G;
-            if (i_hi >= t) s += wpart[((size_t)qt * BH + bh) * W + j];
+    if (j < g.n || j >= g.C) {
+        const int t = j - g.C;   // chunk token (chunk columns only)
+        for (int q0 = 0; q0 < g.n_qt; q0 += 8) {
+            float v[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int qt = q0 + u;
+                const int i_hi = (min((qt + 1) * kRowsPerBlock, g.R) - 1) / g.G;
+                const bool use = qt < g.n_qt && (j < g.n || i_hi >= t);
+                v[u] = use ? wpart[((size_t)qt * BH + bh) * W + j] : 0.f;
+            }
+#pragma unroll
+            for (int u = 0; u < 8; ++u) s += v[u];
         }
     }
     wsum[idx] = s;
