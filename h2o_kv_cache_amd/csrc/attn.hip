@@ -551,12 +551,21 @@ __global__ __launch_bounds__(256) void wsum_from_logits_kernel(
     const int bh = (int)(idx / W);
     const float* lg = logits + (size_t)bh * g.R * W + j;
     const float* lb = l2 + (size_t)bh * g.rows_pad;
+    // rows in order; the logits of 8 rows are loaded before they are summed
+    // (a row that does not see the column adds +0.0 to a non-negative sum)
     float s = 0.f;
-    if (j < g.n) {
-        for (int r = 0; r < g.R; ++r) s += fast_exp2(lg[(size_t)r * W] - lb[r]);
-    } else if (j >= g.C) {
-        const int tG = (j - g.C) * g.G;   // row r sees chunk token t iff t*G <= r
-        for (int r = tG; r < g.R; ++r) s += fast_exp2(lg[(size_t)r * W] - lb[r]);
+    if (j < g.n || j >= g.C) {
+        const int r_lo = j < g.n ? 0 : (j - g.C) * g.G;   // row r sees chunk token t iff t*G <= r
+        for (int r0 = 0; r0 < g.R; r0 += 8) {
+            float x[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int r = r0 + u;
+                x[u] = (r < g.R && r >= r_lo) ? lg[(size_t)r * W] - lb[r] : -INFINITY;
+            }
+#pragma unroll
+            for (int u = 0; u < 8; ++u) s += fast_exp2(x[u]);
+        }
     }
     wsum[idx] = s;
 }

@@ -15,19 +15,18 @@ namespace {
 // ---------------------------------------------------------------------------
 // score accumulation: scores[j] += wsum[j] (j < n); new[t] = wsum[C + t]
 // ---------------------------------------------------------------------------
+// grid: (column blocks, BH); each thread handles columns j and j + 256*gridDim.x ...
 __global__ __launch_bounds__(256) void score_accumulate_kernel(
     int BH, int C, int S, int n, float* __restrict__ scores,
     float* __restrict__ new_scores, const float* __restrict__ wsum) {
     const int W = C + S;
-    const long total = (long)BH * W;
-    for (long idx = (long)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
-         idx += (long)gridDim.x * blockDim.x) {
-        const int bh = (int)(idx / W), j = (int)(idx % W);
-        const float w = wsum[idx];
+    const int bh = blockIdx.y;
+    const float* wrow = wsum + (size_t)bh * W;
+    for (int j = blockIdx.x * 256 + threadIdx.x; j < W; j += gridDim.x * 256) {
         if (j < n)
-            scores[(size_t)bh * C + j] += w;
+            scores[(size_t)bh * C + j] += wrow[j];
         else if (j >= C)
-            new_scores[(size_t)bh * S + (j - C)] = w;
+            new_scores[(size_t)bh * S + (j - C)] = wrow[j];
     }
 }
 
@@ -528,11 +527,12 @@ hipError_t launch_kv_scatter_q8(int BH, int D, int C, int S, int8_t* kc, float* 
 hipError_t launch_score_accumulate(int BH, int C, int S, int n, float* scores,
                                    float* new_scores, const float* wsum,
                                    hipStream_t stream) {
-    const long total = (long)BH * (C + S);
-    long blocks = (total + 255) / 256;
-    if (blocks > 4096) blocks = 4096;
-    hipLaunchKernelGGL(score_accumulate_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
-                       BH, C, S, n, scores, new_scores, wsum);
+    // about 2048 workgroups in all, at least one per (b, kv head)
+    int bx = (C + S + 255) / 256;
+    const int cap = (2048 + BH - 1) / BH;
+    if (bx > cap) bx = cap;
+    hipLaunchKernelGGL(score_accumulate_kernel, dim3((unsigned)bx, (unsigned)BH), dim3(256), 0,
+                       stream, BH, C, S, n, scores, new_scores, wsum);
     return hipGetLastError();
 }
 
