@@ -49,6 +49,29 @@ __device__ __forceinline__ uint32_t slot_key(const float* __restrict__ sc, int j
     return (j < n) ? score_key(sc[j]) : 0u;
 }
 
+constexpr int SU = 16;   // 64-slot steps whose keys are loaded together
+
+// Keys of slots base + 64*u + lane (u < SU) of a contiguous range ending at
+// `last`: the SU loads are unconditional (index clamped to `last`) and are
+// all issued before any is used -- the empty asm takes every loaded value,
+// so the compiler cannot sink a load into a branch of its own; slots past
+// `last` get key 0 and must be masked by the caller.
+__device__ __forceinline__ void load_keys(uint32_t (&key)[SU], const float* __restrict__ sc,
+                                          int base, int lane, int n, int last) {
+    float x[SU];
+#pragma unroll
+    for (int u = 0; u < SU; ++u) x[u] = sc[min(base + 64 * u + lane, last)];
+    asm volatile(""
+                 : "+v"(x[0]), "+v"(x[1]), "+v"(x[2]), "+v"(x[3]), "+v"(x[4]), "+v"(x[5]),
+                   "+v"(x[6]), "+v"(x[7]), "+v"(x[8]), "+v"(x[9]), "+v"(x[10]), "+v"(x[11]),
+                   "+v"(x[12]), "+v"(x[13]), "+v"(x[14]), "+v"(x[15]));
+#pragma unroll
+    for (int u = 0; u < SU; ++u) {
+        const int j = base + 64 * u + lane;
+        key[u] = (j < n && j <= last) ? score_key(x[u]) : 0u;
+    }
+}
+
 // Exclusive prefix sum over the block (1024 threads, 16 waves).
 __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t x, uint32_t* sh_wave) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -258,17 +281,14 @@ __global__ __launch_bounds__(SEL_T) void select_stream_kernel(
         const int shift = 24 - 8 * pass;
         for (int i = tid; i < 256; i += SEL_T) hist[i] = 0u;
         __syncthreads();
-        for (int base = s0; base < s1; base += 256) {
-            uint32_t key[4];
-            bool in[4];
+        for (int base = s0; base < s1; base += 64 * SU) {
+            uint32_t key[SU];
+            bool in[SU];
+            load_keys(key, sc, base, lane, n, s1 - 1);
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const int j = base + 64 * u + lane;
-                in[u] = j < s1;
-                key[u] = in[u] ? slot_key(sc, j, n) : 0u;
-            }
+            for (int u = 0; u < SU; ++u) in[u] = base + 64 * u + lane < s1;
 #pragma unroll
-            for (int u = 0; u < 4; ++u)
+            for (int u = 0; u < SU; ++u)
                 hist_add(hist, (key[u] >> shift) & 255u, in[u] && (key[u] & mask) == prefix);
         }
         __syncthreads();
@@ -283,11 +303,15 @@ __global__ __launch_bounds__(SEL_T) void select_stream_kernel(
 
     // per-wave counts below / at T, then the wave's share of the ties
     uint32_t n_lt = 0, n_eq = 0;
-    for (int base = s0; base < s1; base += 64) {
-        const int j = base + lane;
-        const uint32_t key = j < s1 ? slot_key(sc, j, n) : 0u;
-        n_lt += (uint32_t)__popcll(__ballot(j < s1 && key < T));
-        n_eq += (uint32_t)__popcll(__ballot(j < s1 && key == T));
+    for (int base = s0; base < s1; base += 64 * SU) {
+        uint32_t key[SU];
+        load_keys(key, sc, base, lane, n, s1 - 1);
+#pragma unroll
+        for (int u = 0; u < SU; ++u) {
+            const int j = base + 64 * u + lane;
+            n_lt += (uint32_t)__popcll(__ballot(j < s1 && key[u] < T));
+            n_eq += (uint32_t)__popcll(__ballot(j < s1 && key[u] == T));
+        }
     }
     if (lane == 0) {
         sh_lt[wave] = n_lt;
@@ -304,10 +328,15 @@ __global__ __launch_bounds__(SEL_T) void select_stream_kernel(
     const uint32_t eq_take = kk > eq_before ? min(kk - eq_before, n_eq) : 0u;
 
     uint32_t eq_seen = 0;
-    for (int base = s0; base < s1; base += 64) {
+    for (int base0 = s0; base0 < s1; base0 += 64 * SU) {
+      uint32_t keys[SU];
+      load_keys(keys, sc, base0, lane, n, s1 - 1);
+#pragma unroll
+      for (int u = 0; u < SU; ++u) {
+        const int base = base0 + 64 * u;
         const int j = base + lane;
         const bool in = j < s1;
-        const uint32_t key = in ? slot_key(sc, j, n) : 0u;
+        const uint32_t key = keys[u];
         const unsigned long long eqm = __ballot(in && key == T);
         const uint32_t eq_rank = eq_seen + (uint32_t)__popcll(eqm & below);
         const bool take = in && (key < T || (key == T && eq_rank < eq_take));
@@ -321,6 +350,7 @@ __global__ __launch_bounds__(SEL_T) void select_stream_kernel(
         }
         taken += (uint32_t)__popcll(tm);
         eq_seen += (uint32_t)__popcll(eqm);
+      }
     }
 }
 
