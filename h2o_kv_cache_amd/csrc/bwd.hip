@@ -299,6 +299,174 @@ __global__ __launch_bounds__(KV_NT, 1) void bwd_dkdv_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// dK, dV at D = 128 with two waves per SIMD.  Waves w and w + 4 (one SIMD)
+// share a 32-key block: the P-wave (w < 4) computes S and P and accumulates
+// dV^T += dO^T P; the dS-wave computes dP, takes P from the P-wave through
+// LDS, forms dS and accumulates dK^T += Q^T dS.  Each wave keeps one set of
+// K or V fragments and one set of accumulators (about half of the
+// single-wave kernel's registers), so two fit per SIMD; the MFMA count per
+// key block is unchanged, at the price of one more barrier per row block.
+// ---------------------------------------------------------------------------
+constexpr int PQ_WAVES = 8;
+constexpr int PQ_NT = PQ_WAVES * 64;
+constexpr int PQ_KEYS = (PQ_WAVES / 2) * BR;   // keys per workgroup
+
+template <int D>
+__global__ __launch_bounds__(PQ_NT, 1) void bwd_dkdv_pair_kernel(
+    const BwdGeom g, const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc,
+    const uint16_t* __restrict__ vc, const uint16_t* __restrict__ kn,
+    const uint16_t* __restrict__ vn, const uint16_t* __restrict__ dout,
+    const float* __restrict__ l2, const float* __restrict__ drow, float* __restrict__ dkc,
+    float* __restrict__ dvc, float* __restrict__ dkn, float* __restrict__ dvn) {
+    constexpr int TILE = BR * D;
+    constexpr int NDB = D / 32;
+    __shared__ __attribute__((aligned(16))) uint16_t tiles[2][4][TILE];
+    __shared__ __attribute__((aligned(16))) float stats[2][2 * BR];
+    // P of each pair: [pair][element group][lane][4]
+    __shared__ __attribute__((aligned(16))) float xch[PQ_WAVES / 2][4][64][4];
+
+    const int n_ct = (g.C + PQ_KEYS - 1) / PQ_KEYS;
+    const int n_kt = n_ct + (g.S + PQ_KEYS - 1) / PQ_KEYS;
+    const int bh = blockIdx.x / n_kt, kt = blockIdx.x % n_kt;
+    const int b = bh / g.Hkv, h = bh % g.Hkv;
+    const bool chunk = kt >= n_ct;
+    const int key0 = (chunk ? kt - n_ct : kt) * PQ_KEYS;
+    const int lim = chunk ? g.S : g.n;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int pair = wave & 3;
+    const bool dsw = wave >= 4;                 // the dS-wave of the pair
+    const int half = lane >> 5, l32 = lane & 31;
+
+    const int key = key0 + pair * BR + l32;
+    const bool kok = key < lim;
+    bf16x8 kvf[D / 16];   // K fragments (P-wave) or V fragments (dS-wave)
+    {
+        const size_t krow = chunk ? ((size_t)bh * g.S + key) * D : ((size_t)bh * g.C + key) * D;
+        const uint16_t* src = dsw ? (chunk ? vn : vc) : (chunk ? kn : kc);
+        load_key_frags<D>(kvf, src + krow, kok, half);
+    }
+    f32x16 acc[NDB];      // dV^T (P-wave) or dK^T (dS-wave)
+#pragma unroll
+    for (int i = 0; i < NDB; ++i)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[i][v] = 0.f;
+
+    const int nrb = (g.R + BR - 1) / BR;
+    int rb0 = chunk ? (key0 * g.G) / BR : 0;
+    if (key0 >= lim) rb0 = nrb;
+    const uint16_t* q_h = q + ((size_t)b * g.Hq + (size_t)h * g.G) * g.S * D;
+    const uint16_t* do_h = dout + ((size_t)b * g.Hq + (size_t)h * g.G) * g.S * D;
+    const float* l2_bh = l2 + (size_t)bh * g.R;
+    const float* dr_bh = drow + (size_t)bh * g.R;
+
+    auto issue = [&](int rb, int buf) {
+        const int r0 = rb * BR;
+        issue_rows<D, false, PQ_WAVES, BR>(tiles[buf][0], q_h, r0, g.R, g.G, g.S, wave, lane);
+        issue_rows<D, true, PQ_WAVES, BR>(tiles[buf][1], q_h, r0, g.R, g.G, g.S, wave, lane);
+        issue_rows<D, false, PQ_WAVES, BR>(tiles[buf][2], do_h, r0, g.R, g.G, g.S, wave, lane);
+        issue_rows<D, true, PQ_WAVES, BR>(tiles[buf][3], do_h, r0, g.R, g.G, g.S, wave, lane);
+        if (wave == 0) {
+            const int gr = min(r0 + l32, g.R - 1);
+            dma4((half ? dr_bh : l2_bh) + gr,
+                 __builtin_amdgcn_readfirstlane(lds_addr(stats[buf])));
+        }
+    };
+
+    const LdsOffsets<D> off(lane);
+    const float c = g.c;
+    float* my_x = &xch[pair][0][lane][0];
+    if (rb0 < nrb) issue(rb0, 0);
+    wait_tiles();
+    __syncthreads();
+    for (int rb = rb0; rb < nrb; ++rb) {
+        const int buf = (rb - rb0) & 1;
+        if (rb + 1 < nrb) issue(rb + 1, buf ^ 1);
+        const int r0 = rb * BR;
+
+        // S = Q K^T (P-wave) or dP = dO V^T (dS-wave): element v of a lane is
+        // row r0 + 8*(v/4) + 4*half + v%4 against the lane's key
+        const uint16_t* A = tiles[buf][dsw ? 2 : 0];
+        f32x16 sd;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) sd[v] = 0.f;
+#pragma unroll
+        for (int ks = 0; ks < D / 16; ++ks)
+            sd = mfma32x32x16(as_bf16x8(lds_read16(A, off.k[ks])), kvf[ks], sd);
+
+        bool vis[16];
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+            const int row = r0 + acc_row(v, half);
+            vis[v] = kok && row < g.R && (!chunk || row / g.G >= key);
+        }
+        // P-wave: P = 2^(S c - L2) (selects: masked entries exactly 0), to LDS
+        bf16x8 bop[2];   // B operand of the row contraction: P or dS, in bf16
+        if (!dsw) {
+            float p[16];
+#pragma unroll
+            for (int g4 = 0; g4 < 4; ++g4) {
+                const f32x4 a = *(const f32x4*)&stats[buf][8 * g4 + 4 * half];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int v = 4 * g4 + e;
+                    p[v] = vis[v] ? fast_exp2(fmaf(sd[v], c, -a[e])) : 0.f;
+                }
+                *(f32x4*)(my_x + g4 * 64 * 4) = f32x4{p[4 * g4], p[4 * g4 + 1], p[4 * g4 + 2],
+                                                      p[4 * g4 + 3]};
+            }
+#pragma unroll
+            for (int v = 0; v < 16; ++v) bop[v >> 3][v & 7] = (__bf16)p[v];
+        }
+        __syncthreads();
+        // dS-wave: dS = P * (dP - D)
+        if (dsw) {
+#pragma unroll
+            for (int g4 = 0; g4 < 4; ++g4) {
+                const f32x4 pp = *(const f32x4*)(my_x + g4 * 64 * 4);
+                const f32x4 d = *(const f32x4*)&stats[buf][BR + 8 * g4 + 4 * half];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int v = 4 * g4 + e;
+                    const float ds = vis[v] ? pp[e] * (sd[v] - d[e]) : 0.f;
+                    bop[v >> 3][v & 7] = (__bf16)ds;
+                }
+            }
+        }
+
+        // dV^T += dO^T P (P-wave) or dK^T += Q^T dS (dS-wave): k-step hs covers
+        // rows r0 + 16*hs + {4*half + [0,4), 8 + 4*half + [0,4)}
+        const uint16_t* T = tiles[buf][dsw ? 1 : 3];
+#pragma unroll
+        for (int hs = 0; hs < 2; ++hs) {
+            const uint32_t row_b = (uint32_t)(16 * hs) * 2 * D;
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) {
+                const u32x2 lo = lds_read_tr(T, off.v[db] + row_b);
+                const u32x2 hi = lds_read_tr(T, off.v[db] + row_b + 8 * 2 * D);
+                acc[db] = mfma32x32x16(as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]}), bop[hs],
+                                       acc[db]);
+            }
+        }
+        wait_tiles();
+        __syncthreads();
+    }
+
+    if (key >= (chunk ? g.S : g.C)) return;
+    const size_t row = chunk ? ((size_t)bh * g.S + key) * D : ((size_t)bh * g.C + key) * D;
+    float* dst = (dsw ? (chunk ? dkn : dkc) : (chunk ? dvn : dvc)) + row;
+    const float sc = dsw ? g.tau : 1.f;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int gq = 0; gq < 4; ++gq) {
+            const int d = db * 32 + 8 * gq + 4 * half;
+            *(f32x4*)(dst + d) = sc * f32x4{acc[db][4 * gq + 0], acc[db][4 * gq + 1],
+                                            acc[db][4 * gq + 2], acc[db][4 * gq + 3]};
+        }
+}
+
+// ---------------------------------------------------------------------------
 // dQ: row-major
 // ---------------------------------------------------------------------------
 constexpr int Q_WAVES = 8;
@@ -482,7 +650,12 @@ hipError_t launch_bwd_d(const BwdGeom& g, const uint16_t* q, const uint16_t* kc,
         H2O_CHECK();
     }
     H2O_EVENT(1);
-    {
+    if constexpr (D == 128) {
+        const int n_kt = (g.C + PQ_KEYS - 1) / PQ_KEYS + (g.S + PQ_KEYS - 1) / PQ_KEYS;
+        hipLaunchKernelGGL(bwd_dkdv_pair_kernel<D>, dim3(BH * n_kt), dim3(PQ_NT), 0, stream, g,
+                           q, kc, vc, kn, vn, dout, l2, drow, dkc, dvc, dkn, dvn);
+        H2O_CHECK();
+    } else {
         constexpr int KV_KEYS = kv_keys<D>();
         const int n_kt = (g.C + KV_KEYS - 1) / KV_KEYS + (g.S + KV_KEYS - 1) / KV_KEYS;
         hipLaunchKernelGGL(bwd_dkdv_kernel<D>, dim3(BH * n_kt), dim3(KV_NT), 0, stream, g, q, kc,
