@@ -153,12 +153,16 @@ __global__ __launch_bounds__(KV_NT, 1) void bwd_dkdv_kernel(
 
     // this lane's keys: key0 + wave*64 + kb*32 + l32
     bf16x8 kf[KV_KB][D / 16], vf[KV_KB][D / 16];
-    int key[KV_KB];
+    int key[KV_KB], vis_lo[KV_KB], vis_hi[KV_KB];
     bool kok[KV_KB];
 #pragma unroll
     for (int kb = 0; kb < KV_KB; ++kb) {
         key[kb] = key0 + wave * (KV_KB * BR) + kb * BR + l32;
         kok[kb] = key[kb] < lim;
+        // row r (query r / G) sees the key iff it exists, r < R, and for a chunk
+        // key j, r / G >= j, i.e. r >= j * G
+        vis_lo[kb] = chunk ? key[kb] * g.G : 0;
+        vis_hi[kb] = kok[kb] ? g.R : 0;
         const size_t krow = chunk ? ((size_t)bh * g.S + key[kb]) * D : ((size_t)bh * g.C + key[kb]) * D;
         load_key_frags<D>(kf[kb], (chunk ? kn : kc) + krow, kok[kb], half);
         load_key_frags<D>(vf[kb], (chunk ? vn : vc) + krow, kok[kb], half);
@@ -245,7 +249,7 @@ __global__ __launch_bounds__(KV_NT, 1) void bwd_dkdv_kernel(
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
                 const int row = r0 + acc_row(v, half);
-                const bool vis = kok[kb] && row < g.R && (!chunk || row / g.G >= key[kb]);
+                const bool vis = row >= vis_lo[kb] && row < vis_hi[kb];
                 const float p = vis ? fast_exp2(fmaf(s[kb][v], c, -l2v[v])) : 0.f;
                 const float ds = vis ? p * (dp[kb][v] - drv[v]) : 0.f;
                 pf[kb][v >> 3][v & 7] = (__bf16)p;
@@ -340,6 +344,9 @@ __global__ __launch_bounds__(PQ_NT, 1) void bwd_dkdv_pair_kernel(
 
     const int key = key0 + pair * BR + l32;
     const bool kok = key < lim;
+    // row r (query r / G) sees the key iff it exists, r < R, and for a chunk
+    // key j, r / G >= j, i.e. r >= j * G
+    const int vis_lo = chunk ? key * g.G : 0, vis_hi = kok ? g.R : 0;
     bf16x8 kvf[D / 16];   // K fragments (P-wave) or V fragments (dS-wave)
     {
         const size_t krow = chunk ? ((size_t)bh * g.S + key) * D : ((size_t)bh * g.C + key) * D;
@@ -398,7 +405,7 @@ __global__ __launch_bounds__(PQ_NT, 1) void bwd_dkdv_pair_kernel(
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
             const int row = r0 + acc_row(v, half);
-            vis[v] = kok && row < g.R && (!chunk || row / g.G >= key);
+            vis[v] = row >= vis_lo && row < vis_hi;
         }
         // P-wave: P = 2^(S c - L2) (selects: masked entries exactly 0), to LDS
         bf16x8 bop[2];   // B operand of the row contraction: P or dS, in bf16
