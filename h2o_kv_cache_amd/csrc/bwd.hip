@@ -310,10 +310,27 @@ __global__ __launch_bounds__(KV_NT, 1) void bwd_dkdv_kernel(
 // K or V fragments and one set of accumulators (about half of the
 // single-wave kernel's registers), so two fit per SIMD; the MFMA count per
 // key block is unchanged, at the price of one more barrier per row block.
+// The row-block loop is unrolled by the two tile buffers so that every LDS
+// operand address is a per-lane register plus an immediate, and the mask is
+// applied only to row blocks that are not wholly visible to the key block.
 // ---------------------------------------------------------------------------
 constexpr int PQ_WAVES = 8;
 constexpr int PQ_NT = PQ_WAVES * 64;
 constexpr int PQ_KEYS = (PQ_WAVES / 2) * BR;   // keys per workgroup
+
+template <int N>
+struct IntC {
+    static constexpr int value = N;
+};
+
+__device__ __forceinline__ u32x4 lds_ld16(uint32_t addr) {
+    return *(const __attribute__((address_space(3))) u32x4*)(size_t)addr;
+}
+__device__ __forceinline__ u32x2 lds_ld_tr(uint32_t addr) {
+    const i16x4 v =
+        __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(size_t)addr);
+    return __builtin_bit_cast(u32x2, v);
+}
 
 template <int D>
 __global__ __launch_bounds__(PQ_NT, 1) void bwd_dkdv_pair_kernel(
@@ -324,6 +341,11 @@ __global__ __launch_bounds__(PQ_NT, 1) void bwd_dkdv_pair_kernel(
     float* __restrict__ dvc, float* __restrict__ dkn, float* __restrict__ dvn) {
     constexpr int TILE = BR * D;
     constexpr int NDB = D / 32;
+    constexpr int CPR = D / 8;                       // 16-byte chunks per row
+    constexpr uint32_t BUF_B = 4 * TILE * 2;         // bytes of one buffer's tiles
+    // each lane copies one 16-byte chunk of each tile per row block
+    static_assert(BR * CPR == PQ_NT, "one copy per lane per tile");
+    static_assert(D == 128, "written for eight k-steps of 16");
     __shared__ __attribute__((aligned(16))) uint16_t tiles[2][4][TILE];
     __shared__ __attribute__((aligned(16))) float stats[2][2 * BR];
     // P of each pair: [pair][element group][lane][4]
@@ -342,11 +364,15 @@ __global__ __launch_bounds__(PQ_NT, 1) void bwd_dkdv_pair_kernel(
     const bool dsw = wave >= 4;                 // the dS-wave of the pair
     const int half = lane >> 5, l32 = lane & 31;
 
-    const int key = key0 + pair * BR + l32;
+    const int kp0 = key0 + pair * BR;           // the pair's key block
+    const int key = kp0 + l32;
     const bool kok = key < lim;
     // row r (query r / G) sees the key iff it exists, r < R, and for a chunk
-    // key j, r / G >= j, i.e. r >= j * G
+    // key j, r / G >= j, i.e. r >= j * G; a row block [r0, r0 + 32) sees the
+    // whole key block iff r0 >= full_lo and r0 + 32 <= full_hi
     const int vis_lo = chunk ? key * g.G : 0, vis_hi = kok ? g.R : 0;
+    const int full_lo = chunk ? (kp0 + BR - 1) * g.G : 0;
+    const int full_hi = kp0 + BR - 1 < lim ? g.R : 0;
     bf16x8 kvf[D / 16];   // K fragments (P-wave) or V fragments (dS-wave)
     {
         const size_t krow = chunk ? ((size_t)bh * g.S + key) * D : ((size_t)bh * g.C + key) * D;
@@ -367,96 +393,148 @@ __global__ __launch_bounds__(PQ_NT, 1) void bwd_dkdv_pair_kernel(
     const float* l2_bh = l2 + (size_t)bh * g.R;
     const float* dr_bh = drow + (size_t)bh * g.R;
 
-    auto issue = [&](int rb, int buf) {
-        const int r0 = rb * BR;
-        issue_rows<D, false, PQ_WAVES, BR>(tiles[buf][0], q_h, r0, g.R, g.G, g.S, wave, lane);
-        issue_rows<D, true, PQ_WAVES, BR>(tiles[buf][1], q_h, r0, g.R, g.G, g.S, wave, lane);
-        issue_rows<D, false, PQ_WAVES, BR>(tiles[buf][2], do_h, r0, g.R, g.G, g.S, wave, lane);
-        issue_rows<D, true, PQ_WAVES, BR>(tiles[buf][3], do_h, r0, g.R, g.G, g.S, wave, lane);
+    // Row-block copies: lane (wave, lane) copies chunk p % CPR of row p / CPR
+    // (p = 64 * wave + lane) of each tile, stored at LDS slot p under the
+    // tile's swizzle.  Packed row r is query r / G of head h*G + r % G; the
+    // lane tracks (r % G, r / G) of its row from block to block, and rows past
+    // R re-read row R - 1 (query S - 1 of head G - 1).
+    const int cp = wave * 64 + lane;
+    const int crow = cp / CPR;
+    const int c_row = (cp % CPR) ^ tile_swz<D, false>(crow);   // row-fragment tiles
+    const int c_tr = (cp % CPR) ^ tile_swz<D, true>(crow);     // transposed-read tiles
+    const int g_div = BR / g.G, g_mod = BR % g.G;
+    int nx_r = rb0 * BR + crow;                 // this lane's row in the next block to copy
+    int nx_a = nx_r % g.G, nx_i = nx_r / g.G;
+    auto issue_next = [&](auto BUFC) {
+        constexpr int BUF = decltype(BUFC)::value;
+        const bool past = nx_r >= g.R;
+        const int a = past ? g.G - 1 : nx_a, i = past ? g.S - 1 : nx_i;
+        const size_t ro = ((size_t)a * g.S + i) * D;
+        const uint32_t lb = __builtin_amdgcn_readfirstlane(lds_addr(tiles[BUF][0])) + wave * 1024;
+        dma16(q_h + ro + c_row * 8, lb);
+        dma16(q_h + ro + c_tr * 8, lb + TILE * 2);
+        dma16(do_h + ro + c_row * 8, lb + 2 * TILE * 2);
+        dma16(do_h + ro + c_tr * 8, lb + 3 * TILE * 2);
         if (wave == 0) {
-            const int gr = min(r0 + l32, g.R - 1);
+            const int gr = min(nx_r - crow + l32, g.R - 1);
             dma4((half ? dr_bh : l2_bh) + gr,
-                 __builtin_amdgcn_readfirstlane(lds_addr(stats[buf])));
+                 __builtin_amdgcn_readfirstlane(lds_addr(stats[BUF])));
+        }
+        nx_r += BR;
+        nx_a += g_mod;
+        nx_i += g_div;
+        if (nx_a >= g.G) {
+            nx_a -= g.G;
+            nx_i += 1;
         }
     };
 
+    // per-lane LDS byte addresses, in buffer 0, of this wave's operands: the
+    // row-fragment reads of S = Q K^T (P-wave) or dP = dO V^T (dS-wave), and
+    // the transposed reads of dO (P-wave) or Q (dS-wave)
     const LdsOffsets<D> off(lane);
+    uint32_t ra[D / 16], ta[NDB];
+    {
+        const uint32_t rbase = lds_addr(tiles[0][dsw ? 2 : 0]);
+        const uint32_t tbase = lds_addr(tiles[0][dsw ? 1 : 3]);
+#pragma unroll
+        for (int ks = 0; ks < D / 16; ++ks) ra[ks] = rbase + off.k[ks];
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) ta[db] = tbase + off.v[db];
+    }
     const float c = g.c;
     float* my_x = &xch[pair][0][lane][0];
-    if (rb0 < nrb) issue(rb0, 0);
-    wait_tiles();
-    __syncthreads();
-    for (int rb = rb0; rb < nrb; ++rb) {
-        const int buf = (rb - rb0) & 1;
-        if (rb + 1 < nrb) issue(rb + 1, buf ^ 1);
+
+    // P-wave: P = 2^(S c - L2) (masked entries exactly 0) to LDS and, in bf16,
+    // to `bop`
+    auto p_block = [&](auto BUFC, auto MASKC, int r0, const f32x16& sd, bf16x8 (&bop)[2]) {
+        constexpr int BUF = decltype(BUFC)::value;
+        constexpr bool MASK = decltype(MASKC)::value != 0;
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+            const f32x4 a = *(const f32x4*)&stats[BUF][8 * g4 + 4 * half];
+            float p[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int v = 4 * g4 + e;
+                p[e] = fast_exp2(fmaf(sd[v], c, -a[e]));
+                if (MASK) {
+                    const int row = r0 + acc_row(v, half);
+                    p[e] = (row >= vis_lo && row < vis_hi) ? p[e] : 0.f;
+                }
+                bop[v >> 3][v & 7] = (__bf16)p[e];
+            }
+            *(f32x4*)(my_x + g4 * 64 * 4) = f32x4{p[0], p[1], p[2], p[3]};
+        }
+    };
+
+    auto step = [&](auto BUFC, int rb) {
+        constexpr int BUF = decltype(BUFC)::value;
+        if (rb + 1 < nrb) issue_next(IntC<BUF ^ 1>{});
         const int r0 = rb * BR;
 
         // S = Q K^T (P-wave) or dP = dO V^T (dS-wave): element v of a lane is
         // row r0 + 8*(v/4) + 4*half + v%4 against the lane's key
-        const uint16_t* A = tiles[buf][dsw ? 2 : 0];
+        // all eight operand reads are issued before the first product (the
+        // empty asm takes them together)
+        u32x4 ar[D / 16];
+#pragma unroll
+        for (int ks = 0; ks < D / 16; ++ks) ar[ks] = lds_ld16(ra[ks] + BUF * BUF_B);
+        asm volatile("" : "+v"(ar[0]), "+v"(ar[1]), "+v"(ar[2]), "+v"(ar[3]), "+v"(ar[4]),
+                     "+v"(ar[5]), "+v"(ar[6]), "+v"(ar[7]));
         f32x16 sd;
 #pragma unroll
         for (int v = 0; v < 16; ++v) sd[v] = 0.f;
 #pragma unroll
-        for (int ks = 0; ks < D / 16; ++ks)
-            sd = mfma32x32x16(as_bf16x8(lds_read16(A, off.k[ks])), kvf[ks], sd);
+        for (int ks = 0; ks < D / 16; ++ks) sd = mfma32x32x16(as_bf16x8(ar[ks]), kvf[ks], sd);
 
-        bool vis[16];
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-            const int row = r0 + acc_row(v, half);
-            vis[v] = row >= vis_lo && row < vis_hi;
-        }
-        // P-wave: P = 2^(S c - L2) (selects: masked entries exactly 0), to LDS
         bf16x8 bop[2];   // B operand of the row contraction: P or dS, in bf16
         if (!dsw) {
-            float p[16];
-#pragma unroll
-            for (int g4 = 0; g4 < 4; ++g4) {
-                const f32x4 a = *(const f32x4*)&stats[buf][8 * g4 + 4 * half];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int v = 4 * g4 + e;
-                    p[v] = vis[v] ? fast_exp2(fmaf(sd[v], c, -a[e])) : 0.f;
-                }
-                *(f32x4*)(my_x + g4 * 64 * 4) = f32x4{p[4 * g4], p[4 * g4 + 1], p[4 * g4 + 2],
-                                                      p[4 * g4 + 3]};
-            }
-#pragma unroll
-            for (int v = 0; v < 16; ++v) bop[v >> 3][v & 7] = (__bf16)p[v];
+            if (r0 >= full_lo && r0 + BR <= full_hi)
+                p_block(BUFC, IntC<0>{}, r0, sd, bop);
+            else
+                p_block(BUFC, IntC<1>{}, r0, sd, bop);
         }
         __syncthreads();
-        // dS-wave: dS = P * (dP - D)
+        // dS-wave: dS = P * (dP - D); P is exactly 0 where masked and dP - D is
+        // finite (K, V of missing keys read as 0, rows past R re-read a valid
+        // row), so dS needs no mask of its own
         if (dsw) {
 #pragma unroll
             for (int g4 = 0; g4 < 4; ++g4) {
                 const f32x4 pp = *(const f32x4*)(my_x + g4 * 64 * 4);
-                const f32x4 d = *(const f32x4*)&stats[buf][BR + 8 * g4 + 4 * half];
+                const f32x4 d = *(const f32x4*)&stats[BUF][BR + 8 * g4 + 4 * half];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int v = 4 * g4 + e;
-                    const float ds = vis[v] ? pp[e] * (sd[v] - d[e]) : 0.f;
-                    bop[v >> 3][v & 7] = (__bf16)ds;
+                    bop[v >> 3][v & 7] = (__bf16)(pp[e] * (sd[v] - d[e]));
                 }
             }
         }
 
         // dV^T += dO^T P (P-wave) or dK^T += Q^T dS (dS-wave): k-step hs covers
         // rows r0 + 16*hs + {4*half + [0,4), 8 + 4*half + [0,4)}
-        const uint16_t* T = tiles[buf][dsw ? 1 : 3];
 #pragma unroll
         for (int hs = 0; hs < 2; ++hs) {
-            const uint32_t row_b = (uint32_t)(16 * hs) * 2 * D;
+            const uint32_t o = BUF * BUF_B + (uint32_t)(16 * hs) * 2 * D;
 #pragma unroll
             for (int db = 0; db < NDB; ++db) {
-                const u32x2 lo = lds_read_tr(T, off.v[db] + row_b);
-                const u32x2 hi = lds_read_tr(T, off.v[db] + row_b + 8 * 2 * D);
+                const u32x2 lo = lds_ld_tr(ta[db] + o);
+                const u32x2 hi = lds_ld_tr(ta[db] + o + 8 * 2 * D);
                 acc[db] = mfma32x32x16(as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]}), bop[hs],
                                        acc[db]);
             }
         }
         wait_tiles();
         __syncthreads();
+    };
+
+    if (rb0 < nrb) issue_next(IntC<0>{});
+    wait_tiles();
+    __syncthreads();
+    for (int rb = rb0; rb < nrb; rb += 2) {
+        step(IntC<0>{}, rb);
+        if (rb + 1 < nrb) step(IntC<1>{}, rb + 1);
     }
 
     if (key >= (chunk ? g.S : g.C)) return;
