@@ -318,6 +318,22 @@ constexpr int PQ_WAVES = 8;
 constexpr int PQ_NT = PQ_WAVES * 64;
 constexpr int PQ_KEYS = (PQ_WAVES / 2) * BR;   // keys per workgroup
 
+// Swizzle of bf16 tiles read both as row fragments and transposed, so that
+// one copy serves both reads (64 banks of 4 bytes, 256 bytes per cycle):
+//   D = 128: chunk ^ (4*(r mod 4) + (r/4) mod 4).  Row-fragment reads (16
+//     lanes, one chunk of 16 consecutive rows) see a permutation of the 16
+//     chunk positions; transposed reads (32 lanes, four chunks of rows
+//     4a..4a+3) see the rows' 64-byte runs in four disjoint bank groups.
+//   D = 64 (two rows per 256-byte bank line): chunk ^ (4*((r/2) mod 2) +
+//     (r/4) mod 4): the 8 even (and the 8 odd) rows of 16 see distinct chunk
+//     positions, and rows 4a, 4a+2 (4a+1, 4a+3) runs differ in chunk bit 2.
+// Both depend on row bits 0..3 only: rows 16 apart share the swizzle.
+template <int D>
+__device__ __forceinline__ int pq_swz(int r) {
+    static_assert(D == 64 || D == 128, "head dim");
+    return D == 128 ? (((r & 3) << 2) | ((r >> 2) & 3)) : ((((r >> 1) & 1) << 2) | ((r >> 2) & 3));
+}
+
 template <int N>
 struct IntC {
     static constexpr int value = N;
@@ -342,11 +358,13 @@ __global__ __launch_bounds__(PQ_NT, 1) void bwd_dkdv_pair_kernel(
     constexpr int TILE = BR * D;
     constexpr int NDB = D / 32;
     constexpr int CPR = D / 8;                       // 16-byte chunks per row
-    constexpr uint32_t BUF_B = 4 * TILE * 2;         // bytes of one buffer's tiles
+    constexpr uint32_t BUF_B = 2 * TILE * 2;         // bytes of one buffer's tiles
     // each lane copies one 16-byte chunk of each tile per row block
     static_assert(BR * CPR == PQ_NT, "one copy per lane per tile");
     static_assert(D == 128, "written for eight k-steps of 16");
-    __shared__ __attribute__((aligned(16))) uint16_t tiles[2][4][TILE];
+    // per buffer: Q and dO of 32 rows, one copy each, read both as row
+    // fragments and transposed (swizzle pq_swz)
+    __shared__ __attribute__((aligned(16))) uint16_t tiles[2][2][TILE];
     __shared__ __attribute__((aligned(16))) float stats[2][2 * BR];
     // P of each pair: [pair][element group][lane][4]
     __shared__ __attribute__((aligned(16))) float xch[PQ_WAVES / 2][4][64][4];
@@ -400,8 +418,7 @@ __global__ __launch_bounds__(PQ_NT, 1) void bwd_dkdv_pair_kernel(
     // R re-read row R - 1 (query S - 1 of head G - 1).
     const int cp = wave * 64 + lane;
     const int crow = cp / CPR;
-    const int c_row = (cp % CPR) ^ tile_swz<D, false>(crow);   // row-fragment tiles
-    const int c_tr = (cp % CPR) ^ tile_swz<D, true>(crow);     // transposed-read tiles
+    const int cu = (cp % CPR) ^ pq_swz<D>(crow);
     const int g_div = BR / g.G, g_mod = BR % g.G;
     int nx_r = rb0 * BR + crow;                 // this lane's row in the next block to copy
     int nx_a = nx_r % g.G, nx_i = nx_r / g.G;
@@ -411,10 +428,8 @@ __global__ __launch_bounds__(PQ_NT, 1) void bwd_dkdv_pair_kernel(
         const int a = past ? g.G - 1 : nx_a, i = past ? g.S - 1 : nx_i;
         const size_t ro = ((size_t)a * g.S + i) * D;
         const uint32_t lb = __builtin_amdgcn_readfirstlane(lds_addr(tiles[BUF][0])) + wave * 1024;
-        dma16(q_h + ro + c_row * 8, lb);
-        dma16(q_h + ro + c_tr * 8, lb + TILE * 2);
-        dma16(do_h + ro + c_row * 8, lb + 2 * TILE * 2);
-        dma16(do_h + ro + c_tr * 8, lb + 3 * TILE * 2);
+        dma16(q_h + ro + cu * 8, lb);
+        dma16(do_h + ro + cu * 8, lb + TILE * 2);
         if (wave == 0) {
             const int gr = min(nx_r - crow + l32, g.R - 1);
             dma4((half ? dr_bh : l2_bh) + gr,
@@ -429,18 +444,30 @@ __global__ __launch_bounds__(PQ_NT, 1) void bwd_dkdv_pair_kernel(
         }
     };
 
-    // per-lane LDS byte addresses, in buffer 0, of this wave's operands: the
-    // row-fragment reads of S = Q K^T (P-wave) or dP = dO V^T (dS-wave), and
-    // the transposed reads of dO (P-wave) or Q (dS-wave)
-    const LdsOffsets<D> off(lane);
-    uint32_t ra[D / 16], ta[NDB];
+    // per-lane LDS byte addresses, in buffer 0, of this wave's operands:
+    //   ra[ks]: row-fragment read of S = Q K^T (P-wave) or dP = dO V^T
+    //           (dS-wave): row l32, dims 16*ks + 8*half + [0, 8);
+    //   ta[k][db]: transposed read of dO (P-wave) or Q (dS-wave) for rows
+    //           8*k + 4*half + (lane%16)/4 (k = 0, 1; rows 16 further on share
+    //           the swizzle and add an immediate), dims
+    //           32*db + 16*((lane/16)%2) + 4*(lane%4) + [0, 4).
+    uint32_t ra[D / 16], ta[2][NDB];
     {
-        const uint32_t rbase = lds_addr(tiles[0][dsw ? 2 : 0]);
-        const uint32_t tbase = lds_addr(tiles[0][dsw ? 1 : 3]);
+        const uint32_t rbase = lds_addr(tiles[0][dsw ? 1 : 0]);
+        const uint32_t tbase = lds_addr(tiles[0][dsw ? 0 : 1]);
 #pragma unroll
-        for (int ks = 0; ks < D / 16; ++ks) ra[ks] = rbase + off.k[ks];
+        for (int ks = 0; ks < D / 16; ++ks)
+            ra[ks] = rbase + 2u * (uint32_t)(l32 * D + (((2 * ks + half) ^ pq_swz<D>(l32)) << 3));
+        const int j = lane & 15;
 #pragma unroll
-        for (int db = 0; db < NDB; ++db) ta[db] = tbase + off.v[db];
+        for (int k = 0; k < 2; ++k) {
+            const int r = 8 * k + 4 * half + (j >> 2);
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) {
+                const int d = db * 32 + (lane & 16) + 4 * (j & 3);
+                ta[k][db] = tbase + 2u * (uint32_t)(r * D + (((d >> 3) ^ pq_swz<D>(r)) << 3) + (d & 7));
+            }
+        }
     }
     const float c = g.c;
     float* my_x = &xch[pair][0][lane][0];
@@ -519,8 +546,8 @@ __global__ __launch_bounds__(PQ_NT, 1) void bwd_dkdv_pair_kernel(
             const uint32_t o = BUF * BUF_B + (uint32_t)(16 * hs) * 2 * D;
 #pragma unroll
             for (int db = 0; db < NDB; ++db) {
-                const u32x2 lo = lds_ld_tr(ta[db] + o);
-                const u32x2 hi = lds_ld_tr(ta[db] + o + 8 * 2 * D);
+                const u32x2 lo = lds_ld_tr(ta[0][db] + o);
+                const u32x2 hi = lds_ld_tr(ta[1][db] + o);
                 acc[db] = mfma32x32x16(as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]}), bop[hs],
                                        acc[db]);
             }
@@ -567,8 +594,12 @@ __global__ __launch_bounds__(Q_NT, 1) void bwd_dq_kernel(
     const float* __restrict__ l2, const float* __restrict__ drow, const int nsplit,
     float* __restrict__ dq, float* __restrict__ dq_part) {
     constexpr int TILE = Q_KT * D;
-    // per buffer: K (row-fragment swizzle), K (transposed-read swizzle), V (row fragments)
-    __shared__ __attribute__((aligned(16))) uint16_t tiles[2][3][TILE];
+    constexpr int CPR = D / 8;
+    constexpr int NDB = D / 32;
+    constexpr uint32_t BUF_B = 2 * TILE * 2;         // bytes of one buffer's tiles
+    // per buffer: K (read as row fragments and transposed) and V (row
+    // fragments), both with swizzle pq_swz
+    __shared__ __attribute__((aligned(16))) uint16_t tiles[2][2][TILE];
 
     const int n_rt = (g.R + Q_ROWS - 1) / Q_ROWS;
     int rt, bh, split;
@@ -577,11 +608,17 @@ __global__ __launch_bounds__(Q_NT, 1) void bwd_dq_kernel(
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int half = lane >> 5, l32 = lane & 31;
-    const int r = rt * Q_ROWS + wave * BR + l32;     // this lane's packed row
+    const int wr0 = rt * Q_ROWS + wave * BR;         // the wave's first packed row
+    const int r = wr0 + l32;                         // this lane's packed row
     const bool rok = r < g.R;
     const int rr = rok ? r : g.R - 1;
     const int i = rr / g.G;                          // its query
     const size_t head_row = ((size_t)b * g.Hq + (size_t)h * g.G + rr % g.G) * g.S + i;
+    // a key block [kk0, kk0 + 32) is wholly visible to the wave's rows iff
+    // they all exist, the keys exist, and (chunk keys) kk0 + 31 <= the
+    // smallest query of the rows
+    const bool rows_all = wr0 + BR <= g.R;
+    const int i_min = wr0 / g.G;
 
     // Q and dO fragments of the row: B operands of S^T = K Q^T and dP^T = V dO^T
     bf16x8 qf[D / 16], of[D / 16];
@@ -601,36 +638,67 @@ __global__ __launch_bounds__(Q_NT, 1) void bwd_dq_kernel(
     const uint16_t* vc_bh = vc + (size_t)bh * g.C * D;
     const uint16_t* kn_bh = kn + (size_t)bh * g.S * D;
     const uint16_t* vn_bh = vn + (size_t)bh * g.S * D;
-    auto issue = [&](int t, int buf) {
+    auto issue = [&](auto BUFC, int t) {
+        constexpr int BUF = decltype(BUFC)::value;
         const bool ch = t >= n_ct;
         const int k0 = ch ? (t - n_ct) * Q_KT : t * Q_KT;
         const int lim = ch ? g.S : g.n;
-        issue_tile<D, false, Q_WAVES, Q_KT>(tiles[buf][0], ch ? kn_bh : kc_bh, k0, lim, wave, lane);
-        issue_tile<D, true, Q_WAVES, Q_KT>(tiles[buf][1], ch ? kn_bh : kc_bh, k0, lim, wave, lane);
-        issue_tile<D, false, Q_WAVES, Q_KT>(tiles[buf][2], ch ? vn_bh : vc_bh, k0, lim, wave, lane);
+        const uint16_t* ksrc = ch ? kn_bh : kc_bh;
+        const uint16_t* vsrc = ch ? vn_bh : vc_bh;
+        constexpr int ITER = Q_KT * CPR / (Q_WAVES * 64);
+        static_assert(ITER * Q_WAVES * 64 == Q_KT * CPR, "whole 1 KiB blocks");
+        const uint32_t kb_lds = __builtin_amdgcn_readfirstlane(lds_addr(tiles[BUF][0]));
+#pragma unroll
+        for (int it = 0; it < ITER; ++it) {
+            const int blk = it * Q_WAVES + wave;
+            const int p = blk * 64 + lane;
+            const int key = p / CPR;
+            const size_t src = (size_t)min(k0 + key, lim - 1) * D + ((p % CPR) ^ pq_swz<D>(key)) * 8;
+            dma16(ksrc + src, kb_lds + blk * 1024);
+            dma16(vsrc + src, kb_lds + TILE * 2 + blk * 1024);
+        }
     };
 
-    f32x16 acc[D / 32];
+    f32x16 acc[NDB];
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db)
+    for (int db = 0; db < NDB; ++db)
 #pragma unroll
         for (int v = 0; v < 16; ++v) acc[db][v] = 0.f;
-    const LdsOffsets<D> off(lane);
+    // per-lane LDS byte addresses in buffer 0 (key blocks 32 rows further on,
+    // and rows 16 further on, add immediates):
+    //   kra[ks]: row fragments of K (key l32, dims 16*ks + 8*half + [0, 8));
+    //            those of V are one tile further on;
+    //   kta[k][db]: transposed K for keys 8*k + 4*half + (lane%16)/4, dims
+    //               32*db + 16*((lane/16)%2) + 4*(lane%4) + [0, 4)
+    uint32_t kra[D / 16], kta[2][NDB];
+    {
+        const uint32_t kbase = lds_addr(tiles[0][0]);
+#pragma unroll
+        for (int ks = 0; ks < D / 16; ++ks)
+            kra[ks] = kbase + 2u * (uint32_t)(l32 * D + (((2 * ks + half) ^ pq_swz<D>(l32)) << 3));
+        const int j = lane & 15;
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            const int kr = 8 * k + 4 * half + (j >> 2);
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) {
+                const int d = db * 32 + (lane & 16) + 4 * (j & 3);
+                kta[k][db] =
+                    kbase + 2u * (uint32_t)(kr * D + (((d >> 3) ^ pq_swz<D>(kr)) << 3) + (d & 7));
+            }
+        }
+    }
     const float c = g.c;
-    if (t_begin < t_end) issue(t_begin, 0);
-    wait_tiles();
-    __syncthreads();
-    for (int t = t_begin; t < t_end; ++t) {
-        const int buf = (t - t_begin) & 1;
-        if (t + 1 < t_end) issue(t + 1, buf ^ 1);
+
+    auto step = [&](auto BUFC, int t) {
+        constexpr int BUF = decltype(BUFC)::value;
+        if (t + 1 < t_end) issue(IntC<BUF ^ 1>{}, t + 1);
         const bool ch = t >= n_ct;
         const int k0 = ch ? (t - n_ct) * Q_KT : t * Q_KT;
         const int lim = ch ? g.S : g.n;
-        const uint16_t* Kk = tiles[buf][0];
-        const uint16_t* Kv = tiles[buf][1];
-        const uint16_t* Vk = tiles[buf][2];
 #pragma unroll
         for (int kb = 0; kb < Q_KT / BR; ++kb) {
+            const uint32_t ob = BUF * BUF_B + (uint32_t)(kb * BR) * 2 * D;
             // S^T = K Q^T and dP^T = V dO^T: element v is key
             // k0 + 32*kb + 8*(v/4) + 4*half + v%4 against this lane's row
             f32x16 s, dp;
@@ -638,28 +706,35 @@ __global__ __launch_bounds__(Q_NT, 1) void bwd_dq_kernel(
             for (int v = 0; v < 16; ++v) s[v] = dp[v] = 0.f;
 #pragma unroll
             for (int ks = 0; ks < D / 16; ++ks) {
-                const bf16x8 ka = as_bf16x8(lds_read16(Kk, off.k[ks] + kb * BR * 2 * D));
-                const bf16x8 va = as_bf16x8(lds_read16(Vk, off.k[ks] + kb * BR * 2 * D));
-                s = mfma32x32x16(ka, qf[ks], s);
-                dp = mfma32x32x16(va, of[ks], dp);
+                s = mfma32x32x16(as_bf16x8(lds_ld16(kra[ks] + ob)), qf[ks], s);
+                dp = mfma32x32x16(as_bf16x8(lds_ld16(kra[ks] + ob + TILE * 2)), of[ks], dp);
             }
             bf16x8 sf[2];
+            const int kk0 = k0 + kb * BR;
+            if (rows_all && kk0 + BR <= lim && (!ch || kk0 + BR - 1 <= i_min)) {
 #pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const int kk = k0 + kb * BR + acc_row(v, half);
-                const bool vis = rok && kk < lim && (!ch || kk <= i);
-                const float p = vis ? fast_exp2(fmaf(s[v], c, -l2r)) : 0.f;
-                const float ds = vis ? p * (dp[v] - drr) : 0.f;
-                sf[v >> 3][v & 7] = (__bf16)ds;
+                for (int v = 0; v < 16; ++v) {
+                    const float p = fast_exp2(fmaf(s[v], c, -l2r));
+                    sf[v >> 3][v & 7] = (__bf16)(p * (dp[v] - drr));
+                }
+            } else {
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    const int kk = kk0 + acc_row(v, half);
+                    const bool vis = rok && kk < lim && (!ch || kk <= i);
+                    const float p = vis ? fast_exp2(fmaf(s[v], c, -l2r)) : 0.f;
+                    const float ds = vis ? p * (dp[v] - drr) : 0.f;
+                    sf[v >> 3][v & 7] = (__bf16)ds;
+                }
             }
             // dQ^T += K^T dS^T
 #pragma unroll
             for (int hs = 0; hs < 2; ++hs) {
-                const uint32_t row_b = (uint32_t)(kb * BR + 16 * hs) * 2 * D;
+                const uint32_t o = ob + (uint32_t)(16 * hs) * 2 * D;
 #pragma unroll
-                for (int db = 0; db < D / 32; ++db) {
-                    const u32x2 lo = lds_read_tr(Kv, off.v[db] + row_b);
-                    const u32x2 hi = lds_read_tr(Kv, off.v[db] + row_b + 8 * 2 * D);
+                for (int db = 0; db < NDB; ++db) {
+                    const u32x2 lo = lds_ld_tr(kta[0][db] + o);
+                    const u32x2 hi = lds_ld_tr(kta[1][db] + o);
                     acc[db] = mfma32x32x16(as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]}),
                                            sf[hs], acc[db]);
                 }
@@ -667,6 +742,14 @@ __global__ __launch_bounds__(Q_NT, 1) void bwd_dq_kernel(
         }
         wait_tiles();
         __syncthreads();
+    };
+
+    if (t_begin < t_end) issue(IntC<0>{}, t_begin);
+    wait_tiles();
+    __syncthreads();
+    for (int t = t_begin; t < t_end; t += 2) {
+        step(IntC<0>{}, t);
+        if (t + 1 < t_end) step(IntC<1>{}, t + 1);
     }
     if (!rok) return;
     // one key split: dQ itself; several: this split's partial (scaled later)
