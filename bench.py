@@ -124,19 +124,18 @@ def _pmc_kib(d, counter):
 def traffic_summary(fetch_dir, write_dir):
     """HBM bytes per dispatch of each h2o kernel: counter KiB x 1024, scaled by
     (true bytes / counted bytes) of the 1 GiB calibration copy."""
-    import hashlib
     fetch = _pmc_kib(fetch_dir, "FETCH_SIZE")
     write = _pmc_kib(write_dir, "WRITE_SIZE")
     copy = next(k for k in fetch if "copyBuffer" in k)
     f_scale = CALIB_BYTES / (fetch[copy][0] * 1024.0)
     w_scale = CALIB_BYTES / (write[copy][0] * 1024.0)
-    src = os.path.join(ROOT, "h2o_kv_cache_amd", "csrc", "attn.hip")
     print(f"# calibration: the 1 GiB copy reads FETCH_SIZE {fetch[copy][0]:.1f} KiB, "
           f"WRITE_SIZE {write[copy][0]:.1f} KiB")
     print(f"fetch_scale {f_scale:.5f}")
     print(f"write_scale {w_scale:.5f}")
     print("# bytes = counter KiB x 1024 x scale, averaged over the dispatches")
-    print(f"source_sha1 {hashlib.sha1(open(src, 'rb').read()).hexdigest()}")
+    print("# sources_sha1: attn.hip, h2o_tiles.h, h2o_device.h, h2o_launch.h")
+    print(f"sources_sha1 {kernel_sources_sha1()}")
     for k in fetch:
         if k in write and "copyBuffer" not in k and not k.startswith("at::") \
                 and not k.startswith("elementwise"):
@@ -144,6 +143,16 @@ def traffic_summary(fetch_dir, write_dir):
             wb = write[k][0] * 1024.0 * w_scale
             print(f"{k:28s} fetch_bytes {fb:14.0f} write_bytes {wb:14.0f}   "
                   f"dispatches {fetch[k][1]}")
+
+
+def kernel_sources_sha1():
+    """SHA-1 over the sources the attention kernels are built from (attn.hip
+    and the headers it includes), in a fixed order."""
+    import hashlib
+    h = hashlib.sha1()
+    for name in ("attn.hip", "h2o_tiles.h", "h2o_device.h", "h2o_launch.h"):
+        h.update(open(os.path.join(ROOT, "h2o_kv_cache_amd", "csrc", name), "rb").read())
+    return h.hexdigest()
 
 
 def pairs_per_layer_step(B, Hq, C, S, n):
@@ -186,17 +195,14 @@ def measured_traffic(workload, kernel):
     """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
     summary (FETCH_SIZE + WRITE_SIZE, copy-calibrated), or None when there is
     none for this workload or the kernel source changed since it was taken."""
-    import hashlib
     import re
     tag = {"qwen3_4b_128k": "qwen3_4b_128k"}.get(workload)
     path = os.path.join(ROOT, "profiles", f"attn_fwd_{tag}_hbm_bytes.txt")
     if tag is None or not os.path.exists(path):
         return None
     text = open(path).read()
-    src = os.path.join(ROOT, "h2o_kv_cache_amd", "csrc", "attn.hip")
-    sha = hashlib.sha1(open(src, "rb").read()).hexdigest()
-    m = re.search(r"^source_sha1 (\w+)", text, re.M)
-    if not m or m.group(1) != sha:
+    m = re.search(r"^sources_sha1 (\w+)", text, re.M)
+    if not m or m.group(1) != kernel_sources_sha1():
         return None
     m = re.search(rf"^{re.escape(kernel)}\s+fetch_bytes\s+(\d+)\s+write_bytes\s+(\d+)",
                   text, re.M)
@@ -332,7 +338,8 @@ def run_backward(args, wl):
             "algorithmic_flop_per_layer_step": 8.0 * D * pairs,
             "algorithmic_tflops_whole_step": 8.0 * D * pairs * L / (ms_per_step * 1e-3) / 1e12,
         },
-        "roofline": dict(kernel="bwd_dkdv_kernel<%d> (dP, dV, dK)" % D, traffic=None,
+        "roofline": dict(kernel=("bwd_dkdv_pair_kernel<128> (S, P, dP, dV, dK)" if D == 128
+                                 else "bwd_dkdv_kernel<%d> (S, P, dP, dV, dK)" % D), traffic=None,
                          avg_launch_ms=dkdv_ms, launches=calls, **roof),
     }
     print(json.dumps(result), flush=True)
