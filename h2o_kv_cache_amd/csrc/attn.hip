@@ -688,10 +688,12 @@ __device__ __forceinline__ void colsum_tile(const uint16_t* Ks, const LdsOffsets
 #pragma unroll
             for (int rb = 0; rb < RB; ++rb) s[rb] = mfma32x32x16(qf[rb][ks], kf, s[rb]);
         }
-        float cs = 0.f;
         const int key = key0 + kb * 32 + l32;
         // KSC: the lane's key scale folds into the logit scale
         const float ck = KSC ? c * ksc[kb * 32 + l32] : c;
+        // P in place of S, then a pairwise sum: the 16 exponentials of a row
+        // block are independent, and the sum is a tree of depth 4 instead of
+        // a chain of 16 dependent adds
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
@@ -699,11 +701,20 @@ __device__ __forceinline__ void colsum_tile(const uint16_t* Ks, const LdsOffsets
                 const float p = fast_exp2(fmaf(s[rb][v], ck, -l2v[rb][v]));
                 if (MASKED) {
                     const int r = rbase + rb * 32 + acc_row(v, half);
-                    cs += (key < lim && key * G <= r) ? p : 0.f;
+                    s[rb][v] = (key < lim && key * G <= r) ? p : 0.f;
                 } else {
-                    cs += p;
+                    s[rb][v] = p;
                 }
             }
+#pragma unroll
+        for (int rb = 1; rb < RB; ++rb)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) s[0][v] += s[rb][v];
+#pragma unroll
+        for (int w = 8; w >= 1; w >>= 1)
+#pragma unroll
+            for (int v = 0; v < w; ++v) s[0][v] += s[0][v + w];
+        const float cs = s[0][0];
         col[kb] = cs + xor32(cs);
     }
     // both halves hold the sums; the lower half stores them (one divergent
