@@ -12,20 +12,22 @@
 // L2 the row's base-2 log-sum-exp):
 //   dP = dO V^T,  D_i = sum_j P_ij dP_ij = dO_i . O_i,  dS = P * (dP - D),
 //   dQ = scale dS K,   dK = scale dS^T Q,   dV = P^T dO.
-// Three kernels:
-//   bwd_prep_kernel  per packed row: L2 and D.
-//   bwd_dkdv_kernel  key-major.  A wave owns one (D = 128) or two (D = 64)
-//                    32-key blocks of one KV head, keeps their K and V
-//                    fragments and its dK^T, dV^T
-//                    accumulators in registers, and walks the rows of the G
-//                    query heads in 32-row blocks: S = Q K^T and dP = dO V^T
-//                    (a lane owns a key and 16 rows), then dV^T += dO^T P and
-//                    dK^T += Q^T dS straight from those accumulators (the
-//                    contraction runs over rows, whose fragments are read
-//                    transposed from LDS).
-//   bwd_dq_kernel    row-major, shaped like the forward's pass 1:
-//                    S^T = K Q^T and dP^T = V dO^T (a lane owns a row), then
-//                    dQ^T += K^T dS^T.
+// Kernels:
+//   bwd_prep_kernel       per packed row: L2 and D.
+//   bwd_dkdv_pair_kernel  key-major, D = 128.  Two waves of one SIMD share a
+//                         32-key block of one KV head: one keeps the K
+//                         fragments and dV^T accumulators (S, P, dV), the
+//                         other the V fragments and dK^T accumulators (dP,
+//                         dS, dK), P passing between them through LDS.  They
+//                         walk the rows of the G query heads in 32-row blocks
+//                         (a lane owns a key and 16 rows); the contractions
+//                         over rows read their row fragments transposed from
+//                         LDS.
+//   bwd_dkdv_kernel       key-major, D = 64: one wave owns two 32-key blocks
+//                         with both sets of fragments and accumulators.
+//   bwd_dq_kernel         row-major, shaped like the forward's pass 1:
+//                         S^T = K Q^T and dP^T = V dO^T (a lane owns a row),
+//                         then dQ^T += K^T dS^T.
 // Rows are packed as in the forward: row r of a (b, kv head h) is query r / G
 // of head h*G + r % G.  Every reduction has a fixed order.
 #include "h2o_device.h"
@@ -114,12 +116,13 @@ __device__ __forceinline__ void load_key_frags(bf16x8 (&f)[D / 16], const uint16
 }
 
 // ---------------------------------------------------------------------------
-// dK, dV: key-major
+// dK, dV: key-major, one wave per SIMD (D = 64; D = 128 uses the pair kernel
+// below)
 // ---------------------------------------------------------------------------
 constexpr int KV_WAVES = 4;                 // one wave per SIMD (up to 512 registers)
 constexpr int KV_NT = KV_WAVES * 64;
-// 32-key blocks per wave: each Q / dO fragment read feeds KB MFMAs; at D = 128
-// the K, V fragments and dK, dV accumulators of two blocks exceed 512 registers
+// 32-key blocks per wave: each Q / dO fragment read feeds KB MFMAs (at D = 128
+// the fragments and accumulators of two blocks would exceed 512 registers)
 template <int D>
 constexpr int kv_kb() { return D == 128 ? 1 : 2; }
 template <int D>
