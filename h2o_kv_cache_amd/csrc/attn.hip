@@ -82,6 +82,7 @@ __device__ __forceinline__ void load_q(bf16x8 (&qf)[RB][D / 16], const uint16_t*
 
 // Headroom (base 2) of the fixed per-row reference max in pass 1.
 constexpr float kHeadroom = 64.f;
+constexpr float kSumLimit = 0x1p64f;   // 2^kHeadroom
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 constexpr bf16x2 kOnes2 = {(__bf16)1.0f, (__bf16)1.0f};
@@ -97,7 +98,8 @@ constexpr bf16x2 kOnes2 = {(__bf16)1.0f, (__bf16)1.0f};
 // the 8-bit transposed read) and are converted exactly; with V8 the V scale
 // of key j (vsc[lkb*32 + j]) multiplies P before its bf16 rounding, and O is
 // normalised by the exact row sum (lt_acc = l_acc).
-template <int D, bool MASKED, bool KSC = false, bool K8 = false, bool V8 = false>
+template <int D, bool MASKED, bool KSC = false, bool K8 = false, bool V8 = false,
+          bool TRACK = true>
 __device__ __forceinline__ void fwd_block(const uint16_t* Ks, const uint16_t* Vs,
                                           const LdsOffsets<D>& off,
                                           const bf16x8 (&qf)[RB][D / 16],
@@ -163,26 +165,29 @@ __device__ __forceinline__ void fwd_block(const uint16_t* Ks, const uint16_t* Vs
                 if (!MASKED || key0 + kl < lim) lg_row[col0 + kl] = s[0][v] * c;
             }
         }
-        float mt[RB];
+        // TRACK: the reference max of a row is fixed by the first tile in
+        // which the row sees a key (O and l are still 0 then, so nothing is
+        // rescaled).  Later tiles may exceed it by up to kHeadroom (P <= 2^64,
+        // far from fp32 overflow); beyond that the row is flagged and the
+        // workgroup redoes its tiles with the exact row max in m_seen.
+        // !TRACK: the caller has fixed every row's reference; no tile max is
+        // formed (the caller checks the row sums instead).
+        if constexpr (TRACK) {
+            float mt[RB];
 #pragma unroll
-        for (int rb = 0; rb < RB; ++rb) {
-            float mx = s[rb][0];
+            for (int rb = 0; rb < RB; ++rb) {
+                float mx = s[rb][0];
 #pragma unroll
-            for (int v = 1; v < 16; ++v) mx = fmaxf(mx, s[rb][v]);
-            mx = fmaxf(mx, xor32(mx));
-            mt[rb] = mx * c;
-        }
-
-        // The reference max of a row is fixed by the first tile in which the
-        // row sees a key (O and l are still 0 then, so nothing is rescaled).
-        // Later tiles may exceed it by up to kHeadroom (P <= 2^64, far from
-        // fp32 overflow); beyond that the row is flagged and the workgroup
-        // redoes its tiles with the exact row max in m_seen.
+                for (int v = 1; v < 16; ++v) mx = fmaxf(mx, s[rb][v]);
+                mx = fmaxf(mx, xor32(mx));
+                mt[rb] = mx * c;
+            }
 #pragma unroll
-        for (int rb = 0; rb < RB; ++rb) {
-            m_seen[rb] = fmaxf(m_seen[rb], mt[rb]);
-            m_ref[rb] = (m_ref[rb] == -INFINITY) ? mt[rb] : m_ref[rb];
-            overflow |= mt[rb] > m_ref[rb] + kHeadroom;
+            for (int rb = 0; rb < RB; ++rb) {
+                m_seen[rb] = fmaxf(m_seen[rb], mt[rb]);
+                m_ref[rb] = (m_ref[rb] == -INFINITY) ? mt[rb] : m_ref[rb];
+                overflow |= mt[rb] > m_ref[rb] + kHeadroom;
+            }
         }
 
         // P = 2^(s*c - m), row sums, P^T fragments in bf16: element v of the
@@ -202,7 +207,7 @@ __device__ __forceinline__ void fwd_block(const uint16_t* Ks, const uint16_t* Vs
         }
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) {
-            const float m_use = (m_ref[rb] == -INFINITY) ? 0.f : m_ref[rb];
+            const float m_use = (!TRACK || m_ref[rb] != -INFINITY) ? m_ref[rb] : 0.f;
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
                 const float p = fast_exp2(fmaf(s[rb][v], c, -m_use));
@@ -255,7 +260,7 @@ __device__ __forceinline__ void fwd_block(const uint16_t* Ks, const uint16_t* Vs
 }
 
 // One KT-key tile of pass 1 for one wave: its 32-key blocks in order.
-template <int D, bool MASKED, bool KSC = false>
+template <int D, bool MASKED, bool KSC = false, bool TRACK = true>
 __device__ __forceinline__ void fwd_tile(const uint16_t* Ks, const uint16_t* Vs,
                                          const LdsOffsets<D>& off,
                                          const bf16x8 (&qf)[RB][D / 16],
@@ -266,9 +271,10 @@ __device__ __forceinline__ void fwd_tile(const uint16_t* Ks, const uint16_t* Vs,
                                          int lane, const float* ksc = nullptr) {
 #pragma unroll
     for (int kb = 0; kb < KT / 32; ++kb)
-        fwd_block<D, MASKED, KSC>(Ks, Vs, off, qf, o_acc, m_ref, m_seen, overflow, l_acc,
-                                  lt_acc, c, kb, key0, lim, chunk, G, rbase, lane, nullptr, 0,
-                                  kb, ksc);
+        fwd_block<D, MASKED, KSC, false, false, TRACK>(Ks, Vs, off, qf, o_acc, m_ref, m_seen,
+                                                      overflow, l_acc, lt_acc, c, kb, key0, lim,
+                                                      chunk, G, rbase, lane, nullptr, 0, kb,
+                                                      ksc);
 }
 
 // ---------------------------------------------------------------------------
@@ -319,9 +325,73 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_kernel(
         issue_tile<D, true>(Vs[buf], chunk ? vn_bh : vc_bh, key0, lim, wave, lane);
     };
 
-    // sweep 0 fixes each row's reference max at its first visible tile; in the
-    // rare case a row's logits later overshoot it by more than kHeadroom, a
-    // second sweep reruns the tiles with the exact row max
+    // Main sweep.  The reference of row r (query i = r / G) is its own
+    // base-2 logit against chunk key i, which every row sees: P = 2^(s*c -
+    // ref) needs no per-tile max.  A row whose logits in this split exceed
+    // the reference by more than kHeadroom makes its sum of P exceed
+    // 2^kHeadroom (P >= 0), which sends the workgroup to the tracked sweeps
+    // below.  Logits far below the reference underflow to P = 0: their weight
+    // relative to the row's own key is below fp32 resolution.
+    {
+        bool overflow = false;
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+            const int r = rbase + rb * 32 + l32;
+            const bool ok = r < g.R;
+            const uint16_t* kself = kn_bh + (size_t)(ok ? r / g.G : 0) * D + 8 * half;
+            float dot = 0.f;
+#pragma unroll
+            for (int k16 = 0; k16 < D / 16; ++k16) {
+                const bf16x8 kv = as_bf16x8(*(const u32x4*)(kself + 16 * k16));
+#pragma unroll
+                for (int e = 0; e < 8; ++e) dot = fmaf((float)qf[rb][k16][e], (float)kv[e], dot);
+            }
+            dot += xor32(dot);
+            m_ref[rb] = ok ? dot * g.c : 0.f;
+            l_acc[rb] = 0.f;
+            lt_acc[rb] = 0.f;
+#pragma unroll
+            for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) o_acc[rb][db][v] = 0.f;
+        }
+        if (t_begin < t_end) issue(t_begin, 0);
+        wait_tiles();
+        __syncthreads();
+        const int n_full = g.n / KT;
+        const int t_mid = max(t_begin, min(t_end, n_full));
+        for (int t = t_begin; t < t_mid; ++t) {
+            const int buf = (t - t_begin) & 1;
+            if (t + 1 < t_end) issue(t + 1, buf ^ 1);
+            if (live > 0)
+                fwd_tile<D, false, false, false>(Ks[buf], Vs[buf], off, qf, o_acc, m_ref, m_seen,
+                                                 overflow, l_acc, lt_acc, g.c, 0, 0, false, 0,
+                                                 rbase, lane);
+            wait_tiles();
+            __syncthreads();
+        }
+        for (int t = t_mid; t < t_end; ++t) {
+            const int buf = (t - t_begin) & 1;
+            const bool chunk = t >= tr.n_ct;
+            const int key0 = chunk ? (t - tr.n_ct) * KT : t * KT;
+            const int lim = chunk ? g.S : g.n;
+            if (t + 1 < t_end) issue(t + 1, buf ^ 1);
+            if (live > 0)
+                fwd_tile<D, true, false, false>(Ks[buf], Vs[buf], off, qf, o_acc, m_ref, m_seen,
+                                                overflow, l_acc, lt_acc, g.c, key0, lim, chunk,
+                                                g.G, rbase, lane);
+            wait_tiles();
+            __syncthreads();
+        }
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) overflow |= !(l_acc[rb] <= kSumLimit);
+        if (!__syncthreads_or(overflow)) goto store;
+    }
+
+    // Tracked sweeps (rare): the first fixes each row's reference max at its
+    // first visible tile and records every tile max in m_seen; if a row's
+    // logits still overshoot that reference by more than kHeadroom, the
+    // second reruns the tiles with the exact row max
     for (int sweep = 0; sweep < 2; ++sweep) {
         bool overflow = false;
 #pragma unroll
@@ -365,6 +435,7 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_kernel(
         if (!__syncthreads_or(overflow)) break;
     }
 
+store:
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
         const float l = l_acc[rb] + xor32(l_acc[rb]);
