@@ -84,6 +84,11 @@ __device__ __forceinline__ void load_q(bf16x8 (&qf)[RB][D / 16], const uint16_t*
 constexpr float kHeadroom = 64.f;
 constexpr float kSumLimit = 0x1p64f;   // 2^kHeadroom
 
+template <bool B>
+struct TrackC {
+    static constexpr bool value = B;
+};
+
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 constexpr bf16x2 kOnes2 = {(__bf16)1.0f, (__bf16)1.0f};
 
@@ -1022,18 +1027,10 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_q8_kernel(
                              t >= tr.n_ct, tid);
     };
 
-    for (int sweep = 0; sweep < 2; ++sweep) {
-        bool overflow = false;
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb) {
-            m_ref[rb] = (sweep == 0) ? -INFINITY : m_seen[rb];
-            l_acc[rb] = 0.f;
-            lt_acc[rb] = 0.f;
-#pragma unroll
-            for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-                for (int v = 0; v < 16; ++v) o_acc[rb][db][v] = 0.f;
-        }
+    // One sweep over this split's tiles (TRACK: with the tile max, as in
+    // the tracked sweeps of attn_fwd_kernel).
+    auto sweep_tiles = [&](auto TRC, bool& overflow) {
+        constexpr bool TRACK = decltype(TRC)::value;
         // prologue: tile t_begin converted, tile t_begin+1 staged
         if (t_begin < t_end) {
             issue(t_begin, 0);
@@ -1053,9 +1050,9 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_q8_kernel(
             const int bb = (t - t_begin) & 1;
             if (t + 2 < t_end) issue(t + 2, bb);
             if (live > 0)
-                fwd_tile<D, false, true>(Ks[bb], Vs[bb], off, qf, o_acc, m_ref, m_seen, overflow,
-                                         l_acc, lt_acc, g.c, 0, 0, false, 0, rbase, lane,
-                                         ksc[bb]);
+                fwd_tile<D, false, true, TRACK>(Ks[bb], Vs[bb], off, qf, o_acc, m_ref, m_seen,
+                                                overflow, l_acc, lt_acc, g.c, 0, 0, false, 0,
+                                                rbase, lane, ksc[bb]);
             if (t + 1 < t_end) convert(t + 1, bb ^ 1);
             wait_tiles();
             __syncthreads();
@@ -1067,16 +1064,64 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_q8_kernel(
             const int lim = chunk ? g.S : g.n;
             if (t + 2 < t_end) issue(t + 2, bb);
             if (live > 0)
-                fwd_tile<D, true, true>(Ks[bb], Vs[bb], off, qf, o_acc, m_ref, m_seen, overflow,
-                                        l_acc, lt_acc, g.c, key0, lim, chunk, g.G, rbase, lane,
-                                        ksc[bb]);
+                fwd_tile<D, true, true, TRACK>(Ks[bb], Vs[bb], off, qf, o_acc, m_ref, m_seen,
+                                               overflow, l_acc, lt_acc, g.c, key0, lim, chunk,
+                                               g.G, rbase, lane, ksc[bb]);
             if (t + 1 < t_end) convert(t + 1, bb ^ 1);
             wait_tiles();
             __syncthreads();
         }
+    };
+    auto zero_state = [&]() {
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+            l_acc[rb] = 0.f;
+            lt_acc[rb] = 0.f;
+#pragma unroll
+            for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) o_acc[rb][db][v] = 0.f;
+        }
+    };
+
+    // Main sweep: each row's reference is its own base-2 logit against its
+    // chunk key (bf16 in both caches), as in attn_fwd_kernel; row sums above
+    // 2^kHeadroom send the workgroup to the tracked sweeps.
+    {
+        bool overflow = false;
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+            const int r = rbase + rb * 32 + l32;
+            const bool ok = r < g.R;
+            const uint16_t* kself = kn_bh + (size_t)(ok ? r / g.G : 0) * D + 8 * half;
+            float dot = 0.f;
+#pragma unroll
+            for (int k16 = 0; k16 < D / 16; ++k16) {
+                const bf16x8 kv = as_bf16x8(*(const u32x4*)(kself + 16 * k16));
+#pragma unroll
+                for (int e = 0; e < 8; ++e) dot = fmaf((float)qf[rb][k16][e], (float)kv[e], dot);
+            }
+            dot += xor32(dot);
+            m_ref[rb] = ok ? dot * g.c : 0.f;
+        }
+        zero_state();
+        sweep_tiles(TrackC<false>{}, overflow);
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) overflow |= !(l_acc[rb] <= kSumLimit);
+        if (!__syncthreads_or(overflow)) goto store;
+    }
+    // tracked sweeps (rare): first-tile reference with every tile max
+    // recorded, then, if still overshot, the exact row max
+    for (int sweep = 0; sweep < 2; ++sweep) {
+        bool overflow = false;
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) m_ref[rb] = (sweep == 0) ? -INFINITY : m_seen[rb];
+        zero_state();
+        sweep_tiles(TrackC<true>{}, overflow);
         if (!__syncthreads_or(overflow)) break;
     }
 
+store:
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
         const float l = l_acc[rb] + xor32(l_acc[rb]);
