@@ -88,6 +88,10 @@ template <bool B>
 struct TrackC {
     static constexpr bool value = B;
 };
+template <int N>
+struct BufC {
+    static constexpr int value = N;
+};
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 constexpr bf16x2 kOnes2 = {(__bf16)1.0f, (__bf16)1.0f};
@@ -365,15 +369,21 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_kernel(
         __syncthreads();
         const int n_full = g.n / KT;
         const int t_mid = max(t_begin, min(t_end, n_full));
-        for (int t = t_begin; t < t_mid; ++t) {
-            const int buf = (t - t_begin) & 1;
-            if (t + 1 < t_end) issue(t + 1, buf ^ 1);
+        // unrolled by the two buffers, so that the LDS tile addresses are
+        // constants folded into the reads' offsets
+        auto full_tile = [&](auto BUFC, int t) {
+            constexpr int BUF = decltype(BUFC)::value;
+            if (t + 1 < t_end) issue(t + 1, BUF ^ 1);
             if (live > 0)
-                fwd_tile<D, false, false, false>(Ks[buf], Vs[buf], off, qf, o_acc, m_ref, m_seen,
+                fwd_tile<D, false, false, false>(Ks[BUF], Vs[BUF], off, qf, o_acc, m_ref, m_seen,
                                                  overflow, l_acc, lt_acc, g.c, 0, 0, false, 0,
                                                  rbase, lane);
             wait_tiles();
             __syncthreads();
+        };
+        for (int t = t_begin; t < t_mid; t += 2) {
+            full_tile(BufC<0>{}, t);
+            if (t + 1 < t_mid) full_tile(BufC<1>{}, t + 1);
         }
         for (int t = t_mid; t < t_end; ++t) {
             const int buf = (t - t_begin) & 1;
