@@ -879,8 +879,10 @@ __global__ __launch_bounds__(NT, 2) void attn_colsum_kernel(
     wait_tiles();
     __syncthreads();
 
-    for (int t = t_begin; t < t_end; ++t) {
-        const int buf = (t - t_begin) & 1;
+    // unrolled by the two buffers, so that the LDS tile addresses are
+    // constants folded into the reads' offsets
+    auto step = [&](auto BUFC, int t) {
+        constexpr int buf = decltype(BUFC)::value;
         const bool chunk = t >= tr.n_ct;
         const int key0 = chunk ? (t - tr.n_ct) * KT2 : t * KT2;
         const int lim = chunk ? g.S : g.n;
@@ -900,6 +902,10 @@ __global__ __launch_bounds__(NT, 2) void attn_colsum_kernel(
         }
         wait_tiles();
         __syncthreads();
+    };
+    for (int t = t_begin; t < t_end; t += 2) {
+        step(BufC<0>{}, t);
+        if (t + 1 < t_end) step(BufC<1>{}, t + 1);
     }
     if (t_begin < t_end) flush(t_end - 1, (t_end - 1 - t_begin) & 1);
 }
