@@ -528,45 +528,51 @@ __global__ __launch_bounds__(NT_S, 1) void attn_fwd_small_kernel(
     float m_ref[RB], m_seen[RB], l_acc[RB], lt_acc[RB];
     f32x16 o_acc[RB][D / 32];
     m_seen[0] = -INFINITY;
+    // Each wave copies the 32 K and V rows of its own key block of a tile and
+    // reads only those, so the waves share no tile data: a wave waits for
+    // its own copies (loads complete in issue order) and needs no barrier
+    // per tile.  A stage is rewritten by the wave that read it, after its
+    // reads of it have returned.
     auto issue = [&](int t, int buf) {
         const bool chunk = t >= tr.n_ct;
         const int key0 = chunk ? (t - tr.n_ct) * KT : t * KT;
         const int lim = chunk ? g.S : g.n;
-        issue_tile<D, false, NW_S>(Ks[buf], chunk ? kn_bh : kc_bh, key0, lim, wave, lane);
-        issue_tile<D, true, NW_S>(Vs[buf], chunk ? vn_bh : vc_bh, key0, lim, wave, lane);
+        issue_tile<D, false, 1, 32>(Ks[buf] + wave * 32 * D, chunk ? kn_bh : kc_bh,
+                                    key0 + wave * 32, lim, 0, lane);
+        issue_tile<D, true, 1, 32>(Vs[buf] + wave * 32 * D, chunk ? vn_bh : vc_bh,
+                                   key0 + wave * 32, lim, 0, lane);
     };
-    for (int sweep = 0; sweep < 2; ++sweep) {
-        bool overflow = false;
-        m_ref[0] = (sweep == 0) ? -INFINITY : m_seen[0];
-        l_acc[0] = 0.f;
-        lt_acc[0] = 0.f;
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-            for (int v = 0; v < 16; ++v) o_acc[0][db][v] = 0.f;
+    auto sweep_tiles = [&](auto TRC, bool& overflow, float* lg) {
+        constexpr bool TRACK = decltype(TRC)::value;
         // prologue: tiles t_begin .. t_begin+2 in flight, wait for the first
         for (int i = 0; i < STAGES_S - 1 && t_begin + i < t_end; ++i) issue(t_begin + i, i);
-        wait_tiles();
-        __syncthreads();
+        {
+            const int later = min(STAGES_S - 2, t_end - 1 - t_begin);
+            if (later >= 2)
+                wait_vm<2 * PER_TILE>();
+            else if (later == 1)
+                wait_vm<PER_TILE>();
+            else
+                wait_tiles();
+        }
         for (int t = t_begin; t < t_end; ++t) {
             const int buf = (t - t_begin) % STAGES_S;
             const bool chunk = t >= tr.n_ct;
             const int key0 = chunk ? (t - tr.n_ct) * KT : t * KT;
             const int lim = chunk ? g.S : g.n;
             const int col0 = chunk ? g.C + key0 : key0;
-            // the stage of tile t+3 was last read by tile t-1, which every wave
-            // finished before the barrier that ended it
+            // the stage of tile t+3 was last read, by this wave, for tile t-1
             if (t + STAGES_S - 1 < t_end) issue(t + STAGES_S - 1, (buf + STAGES_S - 1) % STAGES_S);
             if (!chunk && key0 + KT <= g.n)
-                fwd_block<D, false>(Ks[buf], Vs[buf], off, qf, o_acc, m_ref, m_seen, overflow,
-                                    l_acc, lt_acc, g.c, wave, key0, lim, false, 0, 0, lane,
-                                    sweep == 0 ? lg_row : nullptr, col0, wave);
+                fwd_block<D, false, false, false, false, TRACK>(
+                    Ks[buf], Vs[buf], off, qf, o_acc, m_ref, m_seen, overflow, l_acc, lt_acc, g.c,
+                    wave, key0, lim, false, 0, 0, lane, lg, col0, wave);
             else
-                fwd_block<D, true>(Ks[buf], Vs[buf], off, qf, o_acc, m_ref, m_seen, overflow,
-                                   l_acc, lt_acc, g.c, wave, key0, lim, chunk, g.G, 0, lane,
-                                   sweep == 0 ? lg_row : nullptr, col0, wave);
-            // tile t+1 must have landed; tiles issued after it may stay in flight
-            // (loads complete in issue order)
+                fwd_block<D, true, false, false, false, TRACK>(
+                    Ks[buf], Vs[buf], off, qf, o_acc, m_ref, m_seen, overflow, l_acc, lt_acc, g.c,
+                    wave, key0, lim, chunk, g.G, 0, lane, lg, col0, wave);
+            // this wave's copies of tile t+1 must have landed; tiles issued
+            // after it may stay in flight
             const int later = min(STAGES_S - 2, t_end - 1 - (t + 1));
             if (later >= 2)
                 wait_vm<2 * PER_TILE>();
@@ -574,11 +580,51 @@ __global__ __launch_bounds__(NT_S, 1) void attn_fwd_small_kernel(
                 wait_vm<PER_TILE>();
             else
                 wait_tiles();
-            __syncthreads();
         }
+    };
+    auto zero_state = [&]() {
+        l_acc[0] = 0.f;
+        lt_acc[0] = 0.f;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) o_acc[0][db][v] = 0.f;
+    };
+
+    // Main sweep: each row's reference is its own base-2 logit against its
+    // diagonal chunk key, as in attn_fwd_kernel (no per-tile max); row sums
+    // above 2^kHeadroom send the workgroup to the tracked sweeps.  The
+    // logits are written here only (they do not depend on the reference).
+    {
+        bool overflow = false;
+        const int r = l32;
+        const bool ok = r < g.R;
+        const uint16_t* kself = kn_bh + (size_t)(ok ? r / g.G : 0) * D + 8 * half;
+        float dot = 0.f;
+#pragma unroll
+        for (int k16 = 0; k16 < D / 16; ++k16) {
+            const bf16x8 kv = as_bf16x8(*(const u32x4*)(kself + 16 * k16));
+#pragma unroll
+            for (int e = 0; e < 8; ++e) dot = fmaf((float)qf[0][k16][e], (float)kv[e], dot);
+        }
+        dot += xor32(dot);
+        m_ref[0] = ok ? dot * g.c : 0.f;
+        zero_state();
+        sweep_tiles(TrackC<false>{}, overflow, lg_row);
+        overflow |= !(l_acc[0] <= kSumLimit);
+        if (!__syncthreads_or(overflow)) goto merge;
+    }
+    // tracked sweeps (rare): first-tile reference with every tile max
+    // recorded, then, if still overshot, the exact row max
+    for (int sweep = 0; sweep < 2; ++sweep) {
+        bool overflow = false;
+        m_ref[0] = (sweep == 0) ? -INFINITY : m_seen[0];
+        zero_state();
+        sweep_tiles(TrackC<true>{}, overflow, nullptr);
         if (!__syncthreads_or(overflow)) break;
     }
 
+merge:
     // merge the waves' (m, l, lt, O) through LDS (the tiles are free now)
     const float l = l_acc[0] + xor32(l_acc[0]);
     const float lt = lt_acc[0] + xor32(lt_acc[0]);
