@@ -41,6 +41,10 @@ namespace {
 
 constexpr int KT = kKeyTile;
 constexpr int RB = kRowBlocks;
+
+// Row stride (floats) of the stored logits of the few-row path: C + S rounded
+// up to a multiple of 4, so that a row starts on a 16-byte boundary.
+__host__ __device__ inline int logit_stride(const AttnGeom& g) { return (g.C + g.S + 3) & ~3; }
 constexpr int NT = kWaves * 64;   // threads per workgroup
 
 // Key tiles seen by one row tile: cache tiles [0, n_ct), then the chunk tiles
@@ -168,10 +172,21 @@ __device__ __forceinline__ void fwd_block(const uint16_t* Ks, const uint16_t* Vs
             }
         }
         if (lg_row) {   // base-2 logits of the real keys (few-row path only)
+            if constexpr (!MASKED) {
+                // keys 8*g4 + 4*half + [0, 4) of the block are contiguous: one
+                // 16-byte store each (col0 is a multiple of the tile length
+                // and the row stride of the logits a multiple of 4 floats)
 #pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const int kl = kb * 32 + acc_row(v, half);
-                if (!MASKED || key0 + kl < lim) lg_row[col0 + kl] = s[0][v] * c;
+                for (int g4 = 0; g4 < 4; ++g4)
+                    *(f32x4*)(lg_row + col0 + kb * 32 + 8 * g4 + 4 * half) =
+                        f32x4{s[0][4 * g4] * c, s[0][4 * g4 + 1] * c, s[0][4 * g4 + 2] * c,
+                              s[0][4 * g4 + 3] * c};
+            } else {
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    const int kl = kb * 32 + acc_row(v, half);
+                    if (key0 + kl < lim) lg_row[col0 + kl] = s[0][v] * c;
+                }
             }
         }
         // TRACK: the reference max of a row is fixed by the first tile in
@@ -515,7 +530,7 @@ __global__ __launch_bounds__(NT_S, 1) void attn_fwd_small_kernel(
     bf16x8 qf[RB][D / 16];
     load_q<D>(qf, q, g, b, h, 0, l32, half);
     const LdsOffsets<D> off(lane);
-    float* lg_row = (l32 < g.R) ? logits + ((size_t)bh * g.R + l32) * W : nullptr;
+    float* lg_row = (l32 < g.R) ? logits + ((size_t)bh * g.R + l32) * logit_stride(g) : nullptr;
 
     const TileRange tr = tile_range(g, 0);
     const int t_begin = (int)((long)split * tr.total / nsplit);
@@ -681,7 +696,8 @@ __global__ __launch_bounds__(256) void wsum_from_logits_kernel(
     if (idx >= (long)g.B * g.Hkv * W) return;
     const int j = (int)(idx % W);
     const int bh = (int)(idx / W);
-    const float* lg = logits + (size_t)bh * g.R * W + j;
+    const int WL = logit_stride(g);
+    const float* lg = logits + (size_t)bh * g.R * WL + j;
     const float* lb = l2 + (size_t)bh * g.rows_pad;
     // rows in order; the logits of 8 rows are loaded before they are summed
     // (a row that does not see the column adds +0.0 to a non-negative sum)
@@ -693,7 +709,7 @@ __global__ __launch_bounds__(256) void wsum_from_logits_kernel(
 #pragma unroll
             for (int u = 0; u < 8; ++u) {
                 const int r = r0 + u;
-                x[u] = (r < g.R && r >= r_lo) ? lg[(size_t)r * W] - lb[r] : -INFINITY;
+                x[u] = (r < g.R && r >= r_lo) ? lg[(size_t)r * WL] - lb[r] : -INFINITY;
             }
 #pragma unroll
             for (int u = 0; u < 8; ++u) s += fast_exp2(x[u]);
@@ -1376,7 +1392,7 @@ __global__ __launch_bounds__(NT_S, 3) void attn_fwd_small_q8_kernel(
     bf16x8 qf[RB][D / 16];
     load_q<D>(qf, q, g, b, h, 0, l32, half);
     const LdsOffsets<D> off(lane);
-    float* lg_row = (l32 < g.R) ? logits + ((size_t)bh * g.R + l32) * W : nullptr;
+    float* lg_row = (l32 < g.R) ? logits + ((size_t)bh * g.R + l32) * logit_stride(g) : nullptr;
 
     const TileRange tr = tile_range(g, 0);
     const int t_begin = (int)((long)split * tr.total / nsplit);
@@ -1648,7 +1664,8 @@ bool make_attn_plan(int B, int Hq, int Hkv, int D, int C, int S, int n, float sc
     pl->off_l2 = off;
     off = align(off + (size_t)BH * g.rows_pad * sizeof(float));
     pl->off_wp = off;   // row-tile partial sums, or the logits of the few-row path
-    off = align(off + (size_t)(pl->small ? g.R : g.n_qt) * BH * (C + S) * sizeof(float));
+    off = align(off + (size_t)(pl->small ? g.R * logit_stride(g) : g.n_qt * (C + S)) * BH *
+                          sizeof(float));
     pl->bytes = off;
     return true;
 }
