@@ -341,7 +341,17 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_kernel(
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) m_seen[rb] = -INFINITY;
 
+    // tiles whose rows all exist (the full cache tiles) are copied with the
+    // scalar-base form and fixed lane offsets; the others clamp their rows
+    const TileCopy<D, false> kcopy(wave, lane);
+    const TileCopy<D, true> vcopy(wave, lane);
+    const int n_full_tiles = g.n / KT;
     auto issue = [&](int t, int buf) {
+        if (t < n_full_tiles) {
+            kcopy.issue(Ks[buf], kc_bh + (size_t)t * KT * D, wave);
+            vcopy.issue(Vs[buf], vc_bh + (size_t)t * KT * D, wave);
+            return;
+        }
         const bool chunk = t >= tr.n_ct;
         const int key0 = chunk ? (t - tr.n_ct) * KT : t * KT;
         const int lim = chunk ? g.S : g.n;

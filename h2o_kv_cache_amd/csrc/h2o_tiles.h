@@ -98,6 +98,51 @@ __device__ __forceinline__ void issue_tile(uint16_t* tile, const uint16_t* __res
     }
 }
 
+// One 16-byte HBM -> LDS copy per lane with a wave-uniform 64-bit base in
+// SGPRs and a 32-bit per-lane byte offset (the instruction's scalar-base
+// form): lane l writes bytes [16*l, 16*l + 16) past the wave-uniform LDS
+// address `lds`.  Same contract as dma16.
+__device__ __forceinline__ void dma16_s(const void* sbase, uint32_t voff, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
+                 :
+                 : "s"(lds), "v"(voff), "s"(sbase)
+                 : "memory", "m0");
+}
+
+__device__ __forceinline__ const uint16_t* uniform_ptr(const uint16_t* p) {
+    const uint64_t v = (uint64_t)(uintptr_t)p;
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+    return (const uint16_t*)(uintptr_t)(((uint64_t)hi << 32) | lo);
+}
+
+// The copy of issue_tile for a tile whose ROWS rows all exist: the lanes'
+// byte offsets inside a tile are fixed, so they are formed once, and each
+// tile only moves the scalar base (row key0 of the source).
+template <int D, bool VT, int NW = kWaves, int ROWS = kKeyTile>
+struct TileCopy {
+    static constexpr int CPR = D / 8;
+    static constexpr int ITER = ROWS * CPR / (NW * 64);
+    static_assert(ITER * NW * 64 == ROWS * CPR, "tile must split into whole 1 KiB blocks");
+    uint32_t voff[ITER];
+    __device__ __forceinline__ TileCopy(int wave, int lane) {
+#pragma unroll
+        for (int it = 0; it < ITER; ++it) {
+            const int p = (it * NW + wave) * 64 + lane;
+            const int key = p / CPR;
+            const int chunk = (p % CPR) ^ tile_swz<D, VT>(key);
+            voff[it] = 2u * (uint32_t)(key * D + chunk * 8);
+        }
+    }
+    // rows key0 .. key0 + ROWS - 1 of src; `rows` = src + key0 * D
+    __device__ __forceinline__ void issue(uint16_t* tile, const uint16_t* rows, int wave) const {
+        const uint32_t base = __builtin_amdgcn_readfirstlane(lds_addr(tile));
+        const uint16_t* sb = uniform_ptr(rows);
+#pragma unroll
+        for (int it = 0; it < ITER; ++it) dma16_s(sb, voff[it], base + (it * NW + wave) * 1024);
+    }
+};
+
 // 8-bit cache tiles: ROWS x D int8 codes, row-major and unswizzled (they are
 // converted to bf16 tiles, not read as MFMA operands), copied by waves
 // 0..NW-1 in 1 KiB blocks; rows past `lim` re-read row lim-1.  The per-row
