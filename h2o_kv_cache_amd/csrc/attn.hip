@@ -941,7 +941,14 @@ __global__ __launch_bounds__(NT, 2) void attn_colsum_kernel(
             }
         }
     };
+    // full cache tiles: scalar-base copies with fixed lane offsets
+    const TileCopy<D, false, kWaves, KT2> kcopy(wave, lane);
+    const int n_full_tiles = g.n / KT2;
     auto issue = [&](int t, int buf) {
+        if (t < n_full_tiles) {
+            kcopy.issue(Ks[buf], kc_bh + (size_t)t * KT2 * D, wave);
+            return;
+        }
         const bool chunk = t >= tr.n_ct;
         const int key0 = chunk ? (t - tr.n_ct) * KT2 : t * KT2;
         issue_tile<D, false, kWaves, KT2>(Ks[buf], chunk ? kn_bh : kc_bh, key0,

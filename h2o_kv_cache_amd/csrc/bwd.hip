@@ -641,6 +641,16 @@ __global__ __launch_bounds__(Q_NT, 1) void bwd_dq_kernel(
     const uint16_t* vc_bh = vc + (size_t)bh * g.C * D;
     const uint16_t* kn_bh = kn + (size_t)bh * g.S * D;
     const uint16_t* vn_bh = vn + (size_t)bh * g.S * D;
+    // lane byte offsets of the K and V copies inside a tile (both use pq_swz)
+    constexpr int ITER = Q_KT * CPR / (Q_WAVES * 64);
+    static_assert(ITER * Q_WAVES * 64 == Q_KT * CPR, "whole 1 KiB blocks");
+    uint32_t coff[ITER];
+#pragma unroll
+    for (int it = 0; it < ITER; ++it) {
+        const int p = (it * Q_WAVES + wave) * 64 + lane;
+        const int key = p / CPR;
+        coff[it] = 2u * (uint32_t)(key * D + (((p % CPR) ^ pq_swz<D>(key)) << 3));
+    }
     auto issue = [&](auto BUFC, int t) {
         constexpr int BUF = decltype(BUFC)::value;
         const bool ch = t >= n_ct;
@@ -648,9 +658,18 @@ __global__ __launch_bounds__(Q_NT, 1) void bwd_dq_kernel(
         const int lim = ch ? g.S : g.n;
         const uint16_t* ksrc = ch ? kn_bh : kc_bh;
         const uint16_t* vsrc = ch ? vn_bh : vc_bh;
-        constexpr int ITER = Q_KT * CPR / (Q_WAVES * 64);
-        static_assert(ITER * Q_WAVES * 64 == Q_KT * CPR, "whole 1 KiB blocks");
         const uint32_t kb_lds = __builtin_amdgcn_readfirstlane(lds_addr(tiles[BUF][0]));
+        if (!ch && k0 + Q_KT <= g.n) {
+            // every row exists: scalar base (row k0) and the fixed lane offsets
+            const uint16_t* kb = uniform_ptr(ksrc + (size_t)k0 * D);
+            const uint16_t* vb = uniform_ptr(vsrc + (size_t)k0 * D);
+#pragma unroll
+            for (int it = 0; it < ITER; ++it) {
+                dma16_s(kb, coff[it], kb_lds + (it * Q_WAVES + wave) * 1024);
+                dma16_s(vb, coff[it], kb_lds + TILE * 2 + (it * Q_WAVES + wave) * 1024);
+            }
+            return;
+        }
 #pragma unroll
         for (int it = 0; it < ITER; ++it) {
             const int blk = it * Q_WAVES + wave;
