@@ -558,7 +558,16 @@ __global__ __launch_bounds__(NT_S, 1) void attn_fwd_small_kernel(
     // its own copies (loads complete in issue order) and needs no barrier
     // per tile.  A stage is rewritten by the wave that read it, after its
     // reads of it have returned.
+    const TileCopy<D, false, 1, 32> kcopy(0, lane);
+    const TileCopy<D, true, 1, 32> vcopy(0, lane);
+    const int n_full_tiles = g.n / KT;
     auto issue = [&](int t, int buf) {
+        if (t < n_full_tiles) {   // every row exists: scalar base, fixed lane offsets
+            const size_t row0 = (size_t)t * KT + wave * 32;
+            kcopy.issue(Ks[buf] + wave * 32 * D, kc_bh + row0 * D, 0);
+            vcopy.issue(Vs[buf] + wave * 32 * D, vc_bh + row0 * D, 0);
+            return;
+        }
         const bool chunk = t >= tr.n_ct;
         const int key0 = chunk ? (t - tr.n_ct) * KT : t * KT;
         const int lim = chunk ? g.S : g.n;
