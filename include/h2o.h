@@ -271,7 +271,9 @@ h2o_status_t h2o_attn_chunk_bwd(const h2o_shape_t* shape, const uint16_t* q,
  * call records an event before its first kernel and after each of its four
  * kernels on its stream (pass 1: output and log-sum-exp; split merge; pass 2:
  * summed-weight partials; partial reduction), for the first max_calls calls.
- * h2o_timing_stop(ms, calls) waits for the last recorded event, writes the
+ * The events are created without a system-scope memory fence (they only
+ * time; recording them does not write back or invalidate the caches).
+ * h2o_timing_stop(ms, calls) synchronizes the device, writes the
  * summed milliseconds of the four kernels to ms[0..3] and the number of timed
  * calls to *calls, and destroys the events.  h2o_attn_chunk_bwd calls are
  * timed the same way, with ms[0..2] its three kernels (row statistics; key,
