@@ -124,7 +124,8 @@ __device__ __forceinline__ void fwd_block(const uint16_t* Ks, const uint16_t* Vs
                                           int lkb, const float* ksc = nullptr,
                                           const uint8_t* k8 = nullptr,
                                           const uint8_t* v8 = nullptr,
-                                          const float* vsc = nullptr) {
+                                          const float* vsc = nullptr,
+                                          float* lg_stage = nullptr) {
     const int l32 = lane & 31, half = lane >> 5;
     {
         f32x16 s[RB];
@@ -170,6 +171,15 @@ __device__ __forceinline__ void fwd_block(const uint16_t* Ks, const uint16_t* Vs
                     s[rb][v] = ok ? s[rb][v] : -INFINITY;
                 }
             }
+        }
+        if (!MASKED && lg_stage) {
+            // base-2 logits of the block to the wave's LDS stage [row][32 keys]
+            // (rows past R included; the caller copies the real rows out)
+#pragma unroll
+            for (int g4 = 0; g4 < 4; ++g4)
+                *(f32x4*)(lg_stage + l32 * 32 + 8 * g4 + 4 * half) =
+                    f32x4{s[0][4 * g4] * c, s[0][4 * g4 + 1] * c, s[0][4 * g4 + 2] * c,
+                          s[0][4 * g4 + 3] * c};
         }
         if (lg_row) {   // base-2 logits of the real keys (few-row path only)
             if constexpr (!MASKED) {
@@ -523,6 +533,10 @@ __global__ __launch_bounds__(NT_S, 1) void attn_fwd_small_kernel(
     float* __restrict__ o_part, float* __restrict__ ml_part, float* __restrict__ logits) {
     // stage b: K tile in KV[b], V tile in KV[STAGES_S + b]; reused for the final merge
     __shared__ __attribute__((aligned(16))) uint16_t KV[2 * STAGES_S][KT * D];
+    // per wave: the base-2 logits of its key blocks of up to LGS_ROWS / R
+    // consecutive full tiles, [tile][row][key], written out together
+    constexpr int LGS_ROWS = 64;
+    __shared__ __attribute__((aligned(16))) float lgs[NW_S][LGS_ROWS * 32];
     uint16_t (*Ks)[KT * D] = KV;
     uint16_t (*Vs)[KT * D] = KV + STAGES_S;
     // this wave's copy instructions per tile (K and V)
@@ -576,8 +590,28 @@ __global__ __launch_bounds__(NT_S, 1) void attn_fwd_small_kernel(
         issue_tile<D, true, 1, 32>(Vs[buf] + wave * 32 * D, chunk ? vn_bh : vc_bh,
                                    key0 + wave * 32, lim, 0, lane);
     };
-    auto sweep_tiles = [&](auto TRC, bool& overflow, float* lg) {
+    float* const logits_bh = logits + (size_t)bh * g.R * logit_stride(g);
+    // write_logits (wave-uniform): the main sweep stores the logits; the
+    // tracked sweeps do not (the logits do not depend on the reference)
+    auto sweep_tiles = [&](auto TRC, bool& overflow, bool write_logits) {
         constexpr bool TRACK = decltype(TRC)::value;
+        float* const lg = write_logits ? lg_row : nullptr;
+        // logits of full tiles batched in the LDS stage: nb tiles from key
+        // b_key0 on; flushed when the stage is full, before a masked tile,
+        // and at the end, so the stores of a batch go out back to back
+        const int tf = LGS_ROWS / g.R;
+        int nb = 0, b_key0 = 0;
+        auto flush = [&]() {
+            const int per = g.R * 8;   // 16-byte pieces per tile
+            for (int cix = lane; cix < nb * per; cix += 64) {
+                const int slot = cix / per, rem = cix - slot * per;
+                const int row = rem >> 3, k4 = rem & 7;
+                const f32x4 v = *(const f32x4*)&lgs[wave][(slot * g.R + row) * 32 + 4 * k4];
+                *(f32x4*)(logits_bh + (size_t)row * logit_stride(g) + b_key0 + slot * KT +
+                          wave * 32 + 4 * k4) = v;
+            }
+            nb = 0;
+        };
         // prologue: tiles t_begin .. t_begin+2 in flight, wait for the first
         for (int i = 0; i < STAGES_S - 1 && t_begin + i < t_end; ++i) issue(t_begin + i, i);
         {
@@ -597,14 +631,22 @@ __global__ __launch_bounds__(NT_S, 1) void attn_fwd_small_kernel(
             const int col0 = chunk ? g.C + key0 : key0;
             // the stage of tile t+3 was last read, by this wave, for tile t-1
             if (t + STAGES_S - 1 < t_end) issue(t + STAGES_S - 1, (buf + STAGES_S - 1) % STAGES_S);
-            if (!chunk && key0 + KT <= g.n)
+            if (!chunk && key0 + KT <= g.n) {
+                // full tile: the logits of the real rows go to the LDS stage
+                if (nb == 0) b_key0 = key0;
+                float* const stage =
+                    (write_logits && l32 < g.R) ? &lgs[wave][nb * g.R * 32] : nullptr;
                 fwd_block<D, false, false, false, false, TRACK>(
                     Ks[buf], Vs[buf], off, qf, o_acc, m_ref, m_seen, overflow, l_acc, lt_acc, g.c,
-                    wave, key0, lim, false, 0, 0, lane, lg, col0, wave);
-            else
+                    wave, key0, lim, false, 0, 0, lane, nullptr, col0, wave, nullptr, nullptr,
+                    nullptr, nullptr, stage);
+                if (write_logits && ++nb == tf) flush();
+            } else {
+                if (nb > 0) flush();
                 fwd_block<D, true, false, false, false, TRACK>(
                     Ks[buf], Vs[buf], off, qf, o_acc, m_ref, m_seen, overflow, l_acc, lt_acc, g.c,
                     wave, key0, lim, chunk, g.G, 0, lane, lg, col0, wave);
+            }
             // this wave's copies of tile t+1 must have landed; tiles issued
             // after it may stay in flight
             const int later = min(STAGES_S - 2, t_end - 1 - (t + 1));
@@ -615,6 +657,7 @@ __global__ __launch_bounds__(NT_S, 1) void attn_fwd_small_kernel(
             else
                 wait_tiles();
         }
+        if (nb > 0) flush();
     };
     auto zero_state = [&]() {
         l_acc[0] = 0.f;
@@ -644,7 +687,7 @@ __global__ __launch_bounds__(NT_S, 1) void attn_fwd_small_kernel(
         dot += xor32(dot);
         m_ref[0] = ok ? dot * g.c : 0.f;
         zero_state();
-        sweep_tiles(TrackC<false>{}, overflow, lg_row);
+        sweep_tiles(TrackC<false>{}, overflow, true);
         overflow |= !(l_acc[0] <= kSumLimit);
         if (!__syncthreads_or(overflow)) goto merge;
     }
@@ -654,7 +697,7 @@ __global__ __launch_bounds__(NT_S, 1) void attn_fwd_small_kernel(
         bool overflow = false;
         m_ref[0] = (sweep == 0) ? -INFINITY : m_seen[0];
         zero_state();
-        sweep_tiles(TrackC<true>{}, overflow, nullptr);
+        sweep_tiles(TrackC<true>{}, overflow, false);
         if (!__syncthreads_or(overflow)) break;
     }
 
