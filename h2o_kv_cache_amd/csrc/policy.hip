@@ -106,8 +106,8 @@ __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t x, uint32_t* s
 __device__ __forceinline__ void hist_add(uint32_t* hist, uint32_t bin, bool active) {
     const unsigned long long act = __ballot(active);
     if (act == 0ull) return;
-    const int lead = __builtin_ctzll(act);
-    const uint32_t lead_bin = __shfl(bin, lead, 64);
+    const int lead = __builtin_ctzll(act);   // wave-uniform (from a ballot)
+    const uint32_t lead_bin = __builtin_amdgcn_readlane(bin, lead);
     const bool same = active && bin == lead_bin;
     const unsigned long long m = __ballot(same);
     if ((int)(threadIdx.x & 63) == lead) atomicAdd(&hist[lead_bin], (uint32_t)__popcll(m));
