@@ -1443,9 +1443,15 @@ __global__ __launch_bounds__(NT_S, 3) void attn_fwd_small_q8_kernel(
     const uint16_t* __restrict__ kn, const uint16_t* __restrict__ vn,
     float* __restrict__ o_part, float* __restrict__ ml_part, float* __restrict__ logits) {
     __shared__ __attribute__((aligned(16))) uint8_t stg[STQ][2 * KT * D];
-    __shared__ __attribute__((aligned(16))) float ssc[STQ][2][KT];
-    // this wave's copy instructions per cache tile: K and V codes, one scale row
-    constexpr int PER_TILE = 2 * (KT * D / 1024) / NW_S + 1;
+    // per stage and wave: the K scales then the V scales of its 32 keys
+    __shared__ __attribute__((aligned(16))) float ssc[STQ][NW_S][64];
+    // per wave: the base-2 logits of its key blocks of up to Q8_LGS_ROWS / R
+    // consecutive full tiles, [tile][row][key] (R <= Q8_LGS_ROWS)
+    constexpr int Q8_LGS_ROWS = 8;
+    __shared__ __attribute__((aligned(16))) float lgs[NW_S][Q8_LGS_ROWS * 32];
+    // this wave's copy instructions per cache tile: K and V codes of its 32
+    // rows, one 4-byte copy of its 64 scales
+    constexpr int PER_TILE = 2 * (32 * D / 16 / 64) + 1;
     static_assert(STQ - 2 <= 3, "wait_later covers up to three later tiles");
     static_assert(STQ * 2 * KT * D >= 2 * KT * D * 2, "the bf16 chunk tile fits the staging");
 
@@ -1456,12 +1462,13 @@ __global__ __launch_bounds__(NT_S, 3) void attn_fwd_small_q8_kernel(
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l32 = lane & 31, half = lane >> 5;
-    const int W = g.C + g.S;
 
     bf16x8 qf[RB][D / 16];
     load_q<D>(qf, q, g, b, h, 0, l32, half);
     const LdsOffsets<D> off(lane);
-    float* lg_row = (l32 < g.R) ? logits + ((size_t)bh * g.R + l32) * logit_stride(g) : nullptr;
+    const int WL = logit_stride(g);
+    float* lg_row = (l32 < g.R) ? logits + ((size_t)bh * g.R + l32) * WL : nullptr;
+    float* const logits_bh = logits + (size_t)bh * g.R * WL;
 
     const TileRange tr = tile_range(g, 0);
     const int t_begin = (int)((long)split * tr.total / nsplit);
@@ -1474,47 +1481,76 @@ __global__ __launch_bounds__(NT_S, 3) void attn_fwd_small_q8_kernel(
     float m_ref[RB], m_seen[RB], l_acc[RB], lt_acc[RB];
     f32x16 o_acc[RB][D / 32];
     m_seen[0] = -INFINITY;
+    // Each wave copies the codes of the 32 rows of its own key block of a
+    // tile, and their K and V scales, and reads only those: the waves share
+    // no tile data and need no barrier per tile.  A stage is rewritten by the
+    // wave that read it, after its reads of it have returned.
     auto issue = [&](int t, int sb) {
-        issue_tile_i8<D, NW_S, KT, 1>(stg[sb], qc.kc + row0 * D, t * KT, g.n, wave, lane);
-        issue_tile_i8<D, NW_S, KT, 2>(stg[sb] + KT * D, qc.vc + row0 * D, t * KT, g.n, wave,
-                                      lane);
-        issue_scales<0, 1>(ssc[sb][0], ssc[sb][1], qc.ks + row0, qc.vs + row0, t * KT, g.n,
-                           wave, lane);
+        const int k0 = t * KT + wave * 32;
+        issue_tile_i8<D, 1, 32, 1>(stg[sb] + wave * 32 * D, qc.kc + row0 * D, k0, g.n, 0, lane);
+        issue_tile_i8<D, 1, 32, 2>(stg[sb] + KT * D + wave * 32 * D, qc.vc + row0 * D, k0, g.n, 0,
+                                   lane);
+        const int gkey = min(k0 + l32, g.n - 1);
+        dma4((half ? qc.vs : qc.ks) + row0 + gkey,
+             __builtin_amdgcn_readfirstlane(lds_addr(&ssc[sb][wave][0])));
     };
+    // scale pointers as fwd_block indexes them: element lkb*32 + j, lkb = wave
+    auto kscale = [&](int sb) { return &ssc[sb][0][0] + wave * 32; };
+    auto vscale = [&](int sb) { return &ssc[sb][0][0] + wave * 32 + 32; };
 
-    for (int sweep = 0; sweep < 2; ++sweep) {
-        bool overflow = false;
-        m_ref[0] = (sweep == 0) ? -INFINITY : m_seen[0];
-        l_acc[0] = 0.f;
-        lt_acc[0] = 0.f;
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-            for (int v = 0; v < 16; ++v) o_acc[0][db][v] = 0.f;
+    // write_logits (wave-uniform): the main sweep stores the logits
+    auto sweep_tiles = [&](auto TRC, bool& overflow, bool write_logits) {
+        constexpr bool TRACK = decltype(TRC)::value;
+        float* const lg = write_logits ? lg_row : nullptr;
+        const bool staged = write_logits && g.R <= Q8_LGS_ROWS;
+        const int tf = staged ? Q8_LGS_ROWS / g.R : 1;
+        int nb = 0, b_key0 = 0;
+        auto flush = [&]() {
+            const int per = g.R * 8;   // 16-byte pieces per tile
+            for (int cix = lane; cix < nb * per; cix += 64) {
+                const int slot = cix / per, rem = cix - slot * per;
+                const int row = rem >> 3, k4 = rem & 7;
+                const f32x4 v = *(const f32x4*)&lgs[wave][(slot * g.R + row) * 32 + 4 * k4];
+                *(f32x4*)(logits_bh + (size_t)row * WL + b_key0 + slot * KT + wave * 32 +
+                          4 * k4) = v;
+            }
+            nb = 0;
+        };
         for (int i = 0; i < STQ - 1 && t_begin + i < c_end; ++i) issue(t_begin + i, i);
-        wait_tiles();
-        __syncthreads();
+        wait_later<PER_TILE>(min(STQ - 2, c_end - 1 - t_begin));
         for (int t = t_begin; t < c_end; ++t) {
             const int sb = (t - t_begin) % STQ;
             const int key0 = t * KT;
-            // the staging buffer of tile t+2 was last read by tile t-1, which
-            // every wave finished before the barrier that ended it
+            // the stage of tile t+2 was last read, by this wave, for tile t-1
             if (t + STQ - 1 < c_end) issue(t + STQ - 1, (sb + STQ - 1) % STQ);
-            fwd_block<D, true, true, true, true>(nullptr, nullptr, off, qf, o_acc, m_ref, m_seen,
-                                                 overflow, l_acc, lt_acc, g.c, wave, key0, g.n,
-                                                 false, g.G, 0, lane,
-                                                 sweep == 0 ? lg_row : nullptr, key0, wave,
-                                                 ssc[sb][0], stg[sb], stg[sb] + KT * D,
-                                                 ssc[sb][1]);
-            // tile t+1 must have landed; a tile issued after it may stay in flight
+            if (key0 + KT <= g.n) {
+                if (nb == 0) b_key0 = key0;
+                float* const stage =
+                    (staged && l32 < g.R) ? &lgs[wave][nb * g.R * 32] : nullptr;
+                fwd_block<D, false, true, true, true, TRACK>(
+                    nullptr, nullptr, off, qf, o_acc, m_ref, m_seen, overflow, l_acc, lt_acc, g.c,
+                    wave, key0, g.n, false, g.G, 0, lane, staged ? nullptr : lg, key0, wave,
+                    kscale(sb), stg[sb], stg[sb] + KT * D, vscale(sb), stage);
+                if (staged && ++nb == tf) flush();
+            } else {
+                if (nb > 0) flush();
+                fwd_block<D, true, true, true, true, TRACK>(
+                    nullptr, nullptr, off, qf, o_acc, m_ref, m_seen, overflow, l_acc, lt_acc, g.c,
+                    wave, key0, g.n, false, g.G, 0, lane, lg, key0, wave, kscale(sb), stg[sb],
+                    stg[sb] + KT * D, vscale(sb));
+            }
+            // this wave's copies of tile t+1 must have landed; a tile issued
+            // after it may stay in flight
             wait_later<PER_TILE>(min(STQ - 2, c_end - 1 - (t + 1)));
-            __syncthreads();
         }
+        if (nb > 0) flush();
         if (t_end > tr.n_ct) {   // the chunk tile (S <= 32 here: a single tile)
             const int key0 = (t_end - 1 - tr.n_ct) * KT;
-            // bf16 K and V tiles in the (now idle) staging area: K in the
-            // space of buffer 0, V in that of buffer 1; each wave writes its
-            // own 32 rows straight from the chunk; K scales 1
+            // bf16 K and V tiles in the staging area (K in the space of
+            // buffer 0, V in that of buffer 1); each wave writes its own 32
+            // rows straight from the chunk, after every wave is done with the
+            // cache tiles there; K scales 1
+            __syncthreads();
             uint16_t* mk = (uint16_t*)stg[0];
             uint16_t* mv = (uint16_t*)stg[1];
             constexpr int CPR = D / 8;
@@ -1528,16 +1564,55 @@ __global__ __launch_bounds__(NT_S, 3) void attn_fwd_small_q8_kernel(
                 *(u32x4*)(mv + tile_off<D, true>(r, cc)) =
                     *(const u32x4*)(vn_bh + (size_t)key * D + cc * 8);
             }
-            if (lane < 32) ssc[0][0][wave * 32 + lane] = 1.f;
-            fwd_block<D, true, true>(mk, mv, off, qf, o_acc, m_ref, m_seen, overflow, l_acc,
-                                     lt_acc, g.c, wave, key0, g.S, true, g.G, 0, lane,
-                                     sweep == 0 ? lg_row : nullptr, g.C + key0, wave,
-                                     ssc[0][0]);
+            if (lane < 32) ssc[0][wave][lane] = 1.f;
+            fwd_block<D, true, true, false, false, TRACK>(
+                mk, mv, off, qf, o_acc, m_ref, m_seen, overflow, l_acc, lt_acc, g.c, wave, key0,
+                g.S, true, g.G, 0, lane, lg, g.C + key0, wave, kscale(0));
             // the cache blocks set lt = l; this bf16 block adds its rounded weights
         }
+    };
+    auto zero_state = [&]() {
+        l_acc[0] = 0.f;
+        lt_acc[0] = 0.f;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) o_acc[0][db][v] = 0.f;
+    };
+
+    // Main sweep: each row's reference is its own base-2 logit against its
+    // diagonal chunk key (bf16), as in attn_fwd_kernel; row sums above
+    // 2^kHeadroom send the workgroup to the tracked sweeps.
+    {
+        bool overflow = false;
+        const int r = l32;
+        const bool ok = r < g.R;
+        const uint16_t* kself = kn_bh + (size_t)(ok ? r / g.G : 0) * D + 8 * half;
+        float dot = 0.f;
+#pragma unroll
+        for (int k16 = 0; k16 < D / 16; ++k16) {
+            const bf16x8 kv = as_bf16x8(*(const u32x4*)(kself + 16 * k16));
+#pragma unroll
+            for (int e = 0; e < 8; ++e) dot = fmaf((float)qf[0][k16][e], (float)kv[e], dot);
+        }
+        dot += xor32(dot);
+        m_ref[0] = ok ? dot * g.c : 0.f;
+        zero_state();
+        sweep_tiles(TrackC<false>{}, overflow, true);
+        overflow |= !(l_acc[0] <= kSumLimit);
+        if (!__syncthreads_or(overflow)) goto merge;
+    }
+    // tracked sweeps (rare): first-tile reference with every tile max
+    // recorded, then, if still overshot, the exact row max
+    for (int sweep = 0; sweep < 2; ++sweep) {
+        bool overflow = false;
+        m_ref[0] = (sweep == 0) ? -INFINITY : m_seen[0];
+        zero_state();
+        sweep_tiles(TrackC<true>{}, overflow, false);
         if (!__syncthreads_or(overflow)) break;
     }
 
+merge:
     // merge the waves' (m, l, lt, O) through LDS (the staging buffers are free)
     const float l = l_acc[0] + xor32(l_acc[0]);
     const float lt = lt_acc[0] + xor32(lt_acc[0]);

@@ -114,15 +114,18 @@ def test_attention_q8_small(name, B, Hq, Hkv, D, C, S, n):
     _check_attn(g, r, n, C, name)
 
 
-def test_attention_q8_wide_logit_spread():
+@pytest.mark.parametrize("B,Hq,Hkv,D,C,S,n,slot,col", [
+    (1, 4, 1, 128, 1024, 128, 1024, 700, 90),    # row-tile kernel
+    (2, 8, 2, 128, 1000, 1, 1000, 300, -1),      # few-row (decode) kernel; the one
+])                                               # chunk key (each row's own) stays plain
+def test_attention_q8_wide_logit_spread(B, Hq, Hkv, D, C, S, n, slot, col):
     """All-positive queries against one cache slot and one chunk key of
     constant 8.0 (int8 codes 127, scale 8/127): their base-2 logits exceed
     every row's own diagonal logit, and the first-tile maximum, by more than
     100, so pass 1 has to take its fallback sweeps and end with the exact
     row maxima."""
-    B, Hq, Hkv, D, C, S, n, slot, col = 1, 4, 1, 128, 1024, 128, 1024, 700, 90
     log(f"q8 attention wide logit spread: C={C} S={S} heavy slot {slot} chunk column {col}")
-    rng = np.random.default_rng(1301)
+    rng = np.random.default_rng(1301 + S)
     kq, ks, vq, vs, qb, knb, vnb = _q8_inputs(rng, B, Hq, Hkv, D, C, S, n, heavy=False,
                                              garbage=False)
     qb = synth.to_bf16(np.abs(f32(qb)) + np.float32(0.25))[0]
@@ -130,7 +133,8 @@ def test_attention_q8_wide_logit_spread():
     bq, bs = oracle.quantize_rows_int8(big)
     kq[:, :, slot] = bq[0]
     ks[:, :, slot] = bs[0]
-    knb[:, :, col] = synth.to_bf16(big[0])[0]
+    if col >= 0:
+        knb[:, :, col] = synth.to_bf16(big[0])[0]
     g = _gpu_attn_q8(shape_of(B, Hq, Hkv, D, C, S, n), kq, ks, vq, vs, qb, knb, vnb)
     r = oracle.attention_chunk_q8(f32(qb), kq, ks, vq, vs, f32(knb), f32(vnb), n)
     _check_attn(g, r, n, C, "wide_spread")
