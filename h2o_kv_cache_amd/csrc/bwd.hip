@@ -512,6 +512,19 @@ __global__ __launch_bounds__(PQ_NT, 1) void bwd_dkdv_pair_kernel(
         for (int ks = 0; ks < D / 16; ++ks) ar[ks] = lds_ld16(ra[ks] + BUF * BUF_B);
         asm volatile("" : "+v"(ar[0]), "+v"(ar[1]), "+v"(ar[2]), "+v"(ar[3]), "+v"(ar[4]),
                      "+v"(ar[5]), "+v"(ar[6]), "+v"(ar[7]));
+        // the transposed operand of the row contraction (dO for the P-wave, Q
+        // for the dS-wave) does not depend on P, so its 16 reads are issued
+        // here, under the products, and not after the barrier
+        u32x2 trv[2][NDB][2];
+#pragma unroll
+        for (int hs = 0; hs < 2; ++hs) {
+            const uint32_t o = BUF * BUF_B + (uint32_t)(16 * hs) * 2 * D;
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) {
+                trv[hs][db][0] = lds_ld_tr(ta[0][db] + o);
+                trv[hs][db][1] = lds_ld_tr(ta[1][db] + o);
+            }
+        }
         f32x16 sd;
 #pragma unroll
         for (int v = 0; v < 16; ++v) sd[v] = 0.f;
@@ -546,11 +559,10 @@ __global__ __launch_bounds__(PQ_NT, 1) void bwd_dkdv_pair_kernel(
         // rows r0 + 16*hs + {4*half + [0,4), 8 + 4*half + [0,4)}
 #pragma unroll
         for (int hs = 0; hs < 2; ++hs) {
-            const uint32_t o = BUF * BUF_B + (uint32_t)(16 * hs) * 2 * D;
 #pragma unroll
             for (int db = 0; db < NDB; ++db) {
-                const u32x2 lo = lds_ld_tr(ta[0][db] + o);
-                const u32x2 hi = lds_ld_tr(ta[1][db] + o);
+                const u32x2 lo = trv[hs][db][0];
+                const u32x2 hi = trv[hs][db][1];
                 acc[db] = mfma32x32x16(as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]}), bop[hs],
                                        acc[db]);
             }
