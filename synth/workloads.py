@@ -87,6 +87,10 @@ WORKLOADS = {
     # small chunks at 64k: C=8192, S=128 (the pages' 128-token setting), 36 layers
     "qwen3_4b_64k_s128": Workload("qwen3_4b_64k_s128", 5, 1, 32, 8, 128, 8192, 128,
                                   65536, 36, 1.0, 0.05, 4.0, False),
+    # one GPU's share of the 128k layers under 8-way KV-head sharding: one KV
+    # head with its 4 query heads, same cache, chunk and value distribution
+    "qwen3_4b_128k_head": Workload("qwen3_4b_128k_head", 7, 1, 4, 1, 128, 16384, 1024,
+                                   131072, 36, 1.0, 0.05, 4.0, False),
     # SnapKV-style one-shot choice at the end of a 131072-token prompt: the
     # cache holds the first 130048 prompt tokens (positions 0..130047), the
     # last 1024 form the observation window (the chunk); 15360 slots are

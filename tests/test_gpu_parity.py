@@ -88,6 +88,11 @@ def test_qwen3_128k_steady_step():
     _steady(WORKLOADS["qwen3_4b_128k"], heads=[2, 7], layer=3)
 
 
+def test_qwen3_128k_one_head_share_steady_step():
+    # one KV head: 16 row-tile workgroups, so pass 1 runs 16 key splits
+    _steady(WORKLOADS["qwen3_4b_128k_head"], heads=[0], layer=1)
+
+
 def test_qwen3_128k_fill_step():
     wl = WORKLOADS["qwen3_4b_128k"]
     _steady(wl, heads=[1], step=9, n_valid=9 * wl.chunk_len)
