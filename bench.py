@@ -26,6 +26,8 @@ import os
 import sys
 import time
 
+import numpy as np
+
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
@@ -605,14 +607,21 @@ def main():
     t_start = torch.cuda.Event(enable_timing=True)
     t_stop = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
+    # step boundaries on the attention stream (the policy calls of a step
+    # overlap the next step's attention; the last step ends when they do)
+    marks = [t_start] + [torch.cuda.Event(enable_timing=True) for _ in range(args.steps - 1)]
     t_start.record(stream)
     for i in range(args.steps):
+        if i > 0:
+            marks[i].record(stream)
         run_step(args.warmup + i)
     stream.wait_stream(pstream)               # the last policy calls end the step
     t_stop.record(stream)
     torch.cuda.synchronize()
     kernel_ms, calls = h2o.h2o_timing_stop()
     elapsed_ms = t_start.elapsed_time(t_stop)
+    marks.append(t_stop)
+    step_ms = np.array([marks[i].elapsed_time(marks[i + 1]) for i in range(args.steps)])
 
     ms_per_step = elapsed_ms / args.steps
     tokens_per_s = B * S * args.steps / (elapsed_ms / 1e3)
@@ -662,6 +671,7 @@ def main():
                              "second stream, overlapped with the next layer's attention",
             "executed_mfma_tflops_whole_step": step_tflops,
             "executed_mfma_frac_whole_step": step_tflops / PEAK_BF16_TFLOPS,
+            "step_ms_p10_p50_p90": [float(np.percentile(step_ms, q)) for q in (10, 50, 90)],
         },
         "roofline": dict(
             kernel=fwd_kernel + " (pass 1: QK^T, online softmax, PV)",
