@@ -40,6 +40,9 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--graph", action="store_true",
+                    help="time the K steps as one captured HIP graph replay (policy calls "
+                         "on the attention stream only: one layer or --serial-policy)")
     ap.add_argument("--workload", default="qwen3_4b_128k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calib-copy", action="store_true",
@@ -543,7 +546,7 @@ def main():
                 st[name + "q"], st[name + "s"] = codes, scales
                 del st[name]
         torch.cuda.synchronize()
-    inputs = make_inputs(wl, args.warmup + args.steps, gen)
+    inputs = make_inputs(wl, args.warmup + args.steps * (2 if args.graph else 1), gen)
     out = torch.empty((B, Hq, S, D), dtype=torch.float32, device="cuda")
     lse = torch.empty((B, Hq, S), dtype=torch.float32, device="cuda")
     # per layer: the policy calls of a layer may still run while the next
@@ -561,11 +564,18 @@ def main():
     # With one layer there is nothing to overlap (the next step's attention
     # waits for the scatter), and the events only add latency.
     pstream = stream if (args.serial_policy or L == 1) else torch.cuda.Stream()
+    main_stream, policy_stream = stream, pstream
+    if args.graph and pstream is not stream:
+        print("--graph captures the policy calls on the attention stream: use it with one "
+              "layer or --serial-policy", file=sys.stderr)
+        sys.exit(2)
     ev_attn = [torch.cuda.Event() for _ in range(L)]
     ev_pol = [torch.cuda.Event() for _ in range(L)]
     p0_base = (C // S + 2) * S
 
-    def run_step(i):
+    def run_step(i, s_main=None):
+        stream = s_main if s_main is not None else main_stream
+        pstream = stream if policy_stream is main_stream else policy_stream
         p0 = p0_base + i * S
         for li, st in enumerate(layers):
             q, kn, vn = inputs[i][li]
@@ -622,6 +632,24 @@ def main():
     elapsed_ms = t_start.elapsed_time(t_stop)
     marks.append(t_stop)
     step_ms = np.array([marks[i].elapsed_time(marks[i + 1]) for i in range(args.steps)])
+    eager_ms = elapsed_ms
+    if args.graph:
+        # the next K steps (their own inputs and positions) captured once,
+        # replayed once untimed, then timed as one replay
+        graph = torch.cuda.CUDAGraph()
+        torch.cuda.synchronize()
+        with torch.cuda.graph(graph):
+            cap = torch.cuda.current_stream()
+            for i in range(args.steps):
+                run_step(args.warmup + args.steps + i, cap)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        t_start.record(stream)
+        graph.replay()
+        t_stop.record(stream)
+        torch.cuda.synchronize()
+        elapsed_ms = t_start.elapsed_time(t_stop)
 
     ms_per_step = elapsed_ms / args.steps
     tokens_per_s = B * S * args.steps / (elapsed_ms / 1e3)
@@ -672,6 +700,9 @@ def main():
             "executed_mfma_tflops_whole_step": step_tflops,
             "executed_mfma_frac_whole_step": step_tflops / PEAK_BF16_TFLOPS,
             "step_ms_p10_p50_p90": [float(np.percentile(step_ms, q)) for q in (10, 50, 90)],
+            "timing": ("one HIP graph replay of the K steps; per-kernel split and step "
+                       "percentiles from the eager loop (%.4f ms/step eager)"
+                       % (eager_ms / args.steps)) if args.graph else "eager launches",
         },
         "roofline": dict(
             kernel=fwd_kernel + " (pass 1: QK^T, online softmax, PV)",
