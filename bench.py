@@ -45,6 +45,9 @@ def parse():
                          "on the attention stream only: one layer or --serial-policy)")
     ap.add_argument("--workload", default="qwen3_4b_128k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--whole-run", action="store_true",
+                    help="every step of the workload from an empty cache (fill, then "
+                         "eviction) through all layers; tokens/s over the summed step times")
     ap.add_argument("--calib-copy", action="store_true",
                     help="copy a 1 GiB buffer once before timing (counter calibration)")
     ap.add_argument("--summarize-stats", metavar="DIR",
@@ -381,6 +384,109 @@ def cpu_baseline_snapkv(wl):
                        f"scaled x{wl.n_kv_heads * wl.batch} heads x{wl.layers} layers")}
 
 
+def run_whole(args, wl):
+    """The whole run of a chunked workload: every step from an empty cache --
+    the fill steps (the choice appends), then the eviction steps -- through
+    all layers, with the policy calls on a second stream as in the steady-state
+    line.  Each step's inputs are generated before it, outside its events;
+    tokens/s = all tokens / the summed step times."""
+    import torch
+    import h2o_kv_cache_amd as h2o
+    B, Hq, Hkv, D, C, S, L = (wl.batch, wl.n_q_heads, wl.n_kv_heads, wl.head_dim,
+                              wl.cache_len, wl.chunk_len, wl.layers)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(20261203)
+    bf16 = torch.bfloat16
+
+    def empty_layer():
+        return dict(k=torch.zeros((B, Hkv, C, D), dtype=bf16, device="cuda"),
+                    v=torch.zeros((B, Hkv, C, D), dtype=bf16, device="cuda"),
+                    scores=torch.zeros((B, Hkv, C), device="cuda"),
+                    pos=torch.full((B, Hkv, C), -1, dtype=torch.int64, device="cuda"),
+                    wsum=torch.empty((B, Hkv, C + S), device="cuda"),
+                    new_scores=torch.empty((B, Hkv, S), device="cuda"),
+                    evict=torch.empty((B, Hkv, S), dtype=torch.int32, device="cuda"))
+    layers = [empty_layer() for _ in range(L)]
+    steps = wl.steps
+    ns = [min(C, i * S) for i in range(steps)]
+    ws = torch.empty(max(h2o.h2o_workspace_size(h2o.Shape(B, Hq, Hkv, D, C, S, n))
+                         for n in sorted(set(ns))), dtype=torch.uint8, device="cuda")
+    out = torch.empty((B, Hq, S, D), device="cuda")
+    lse = torch.empty((B, Hq, S), device="cuda")
+    stream = torch.cuda.current_stream()
+    pstream = stream if (args.serial_policy or L == 1) else torch.cuda.Stream()
+    ev_attn = [torch.cuda.Event() for _ in range(L)]
+    ev_pol = [torch.cuda.Event() for _ in range(L)]
+
+    def layer_step(shape, st, q, kn, vn, p0, li):
+        if pstream is not stream:
+            stream.wait_event(ev_pol[li])
+        h2o.h2o_attn_chunk(shape, q, st["k"], st["v"], kn, vn, out, lse, st["wsum"], ws, stream)
+        if pstream is not stream:
+            ev_attn[li].record(stream)
+            pstream.wait_event(ev_attn[li])
+        h2o.h2o_score_accumulate(shape, st["scores"], st["new_scores"], st["wsum"], pstream)
+        h2o.h2o_evict_select(shape, st["scores"], st["evict"], pstream)
+        h2o.kv_scatter(shape, st["k"], st["v"], st["scores"], st["pos"], kn, vn,
+                       st["new_scores"], st["evict"], p0, pstream)
+        if pstream is not stream:
+            ev_pol[li].record(pstream)
+
+    # untimed: one fill-phase and one eviction-phase step on a scratch layer
+    scratch = empty_layer()
+    warm = make_inputs(wl.with_(layers=1), 1, gen)[0][0]
+    for n in (0, C):
+        layer_step(h2o.Shape(B, Hq, Hkv, D, C, S, n), scratch, *warm, n, 0)
+    torch.cuda.synchronize()
+    del scratch
+
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    step_ms = []
+    for i in range(steps):
+        chunk = make_inputs(wl, 1, gen)[0]
+        torch.cuda.synchronize()
+        shape = h2o.Shape(B, Hq, Hkv, D, C, S, ns[i])
+        e0.record(stream)
+        for li, st in enumerate(layers):
+            layer_step(shape, st, *chunk[li], i * S, li)
+        stream.wait_stream(pstream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        step_ms.append(e0.elapsed_time(e1))
+        del chunk
+    total_ms = float(sum(step_ms))
+    fill = [t for t, n in zip(step_ms, ns) if n + S <= C]
+    evict = [t for t, n in zip(step_ms, ns) if n + S > C]
+    pct = lambda x: [float(np.percentile(x, q)) for q in (10, 50, 90)] if x else None
+    result = {
+        "metric": "H2O chunk-step tokens/s over the whole run (fill + eviction steps), "
+                  "all layers",
+        "value": B * S * steps / (total_ms / 1e3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": 0,
+        "ms_per_step": total_ms / steps,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": wl.name, "batch": B, "q_heads": Hq, "kv_heads": Hkv, "head_dim": D,
+            "cache_len": C, "chunk_len": S, "layers": L, "context": wl.seq_len,
+            "fill_steps": len(fill), "eviction_steps": len(evict),
+            "fill_step_ms_p10_p50_p90": pct(fill),
+            "eviction_step_ms_p10_p50_p90": pct(evict),
+            "policy_stream": "same stream" if pstream is stream else
+                             "second stream, overlapped with the next layer's attention",
+            "timing": "events around each step; inputs generated between steps",
+        },
+    }
+    print(json.dumps(result), flush=True)
+
+
 def run_snapkv(args, wl):
     """Time the SnapKV-style one-shot choice at the end of a prompt, over all
     layers: per layer the window chunk's attention over the prompt cache
@@ -526,6 +632,13 @@ def main():
     torch.cuda.set_device(0)
     if args.backward:
         run_backward(args, wl)
+        return
+    if args.whole_run:
+        if wl.prefilled or wl.keep_budget > 0:
+            print("--whole-run covers chunked workloads that start from an empty cache",
+                  file=sys.stderr)
+            sys.exit(2)
+        run_whole(args, wl)
         return
     if wl.keep_budget > 0:
         run_snapkv(args, wl)
