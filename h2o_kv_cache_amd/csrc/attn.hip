@@ -749,35 +749,51 @@ merge:
 }
 
 // Summed weights straight from the stored logits (few-row path): column j
-// sums 2^(u_rj - L2_r) over the rows that see it, in row order.
+// sums 2^(u_rj - L2_r) over the rows that see it, in row order.  A thread
+// takes four consecutive columns, one 16-byte load per row (the logit rows
+// are padded to a multiple of 4 floats, so the quad stays inside the row).
 __global__ __launch_bounds__(256) void wsum_from_logits_kernel(
     const AttnGeom g, const float* __restrict__ logits, const float* __restrict__ l2,
     float* __restrict__ wsum) {
     const int W = g.C + g.S;
+    const int nq = (W + 3) / 4;   // column quads per (b, kv head)
     const long idx = (long)blockIdx.x * blockDim.x + threadIdx.x;
-    if (idx >= (long)g.B * g.Hkv * W) return;
-    const int j = (int)(idx % W);
-    const int bh = (int)(idx / W);
+    if (idx >= (long)g.B * g.Hkv * nq) return;
+    const int j0 = (int)(idx % nq) * 4;
+    const int bh = (int)(idx / nq);
     const int WL = logit_stride(g);
-    const float* lg = logits + (size_t)bh * g.R * WL + j;
+    const float* lg = logits + (size_t)bh * g.R * WL + j0;
     const float* lb = l2 + (size_t)bh * g.rows_pad;
-    // rows in order; the logits of 8 rows are loaded before they are summed
-    // (a row that does not see the column adds +0.0 to a non-negative sum)
-    float s = 0.f;
-    if (j < g.n || j >= g.C) {
-        const int r_lo = j < g.n ? 0 : (j - g.C) * g.G;   // row r sees chunk token t iff t*G <= r
-        for (int r0 = 0; r0 < g.R; r0 += 8) {
-            float x[8];
+    // column j0 + e is a valid cache slot or a chunk token, seen by rows
+    // r >= r_lo[e] (row r sees chunk token t iff t*G <= r)
+    bool col[4];
+    int r_lo[4];
 #pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                const int r = r0 + u;
-                x[u] = (r < g.R && r >= r_lo) ? lg[(size_t)r * WL] - lb[r] : -INFINITY;
-            }
-#pragma unroll
-            for (int u = 0; u < 8; ++u) s += fast_exp2(x[u]);
-        }
+    for (int e = 0; e < 4; ++e) {
+        const int jj = j0 + e;
+        col[e] = jj < W && (jj < g.n || jj >= g.C);
+        r_lo[e] = jj < g.C ? 0 : (jj - g.C) * g.G;
     }
-    wsum[idx] = s;
+    // rows in order; the logits of 8 rows are loaded before they are summed
+    float s[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int r0 = 0; r0 < g.R; r0 += 8) {
+        f32x4 x[8];
+        float lr[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int r = min(r0 + u, g.R - 1);
+            x[u] = *(const f32x4*)(lg + (size_t)r * WL);
+            lr[u] = lb[r];
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                if (r0 + u < g.R && col[e] && r0 + u >= r_lo[e]) s[e] += fast_exp2(x[u][e] - lr[u]);
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+        if (j0 + e < W) wsum[(size_t)bh * W + j0 + e] = s[e];
 }
 
 // ---------------------------------------------------------------------------
@@ -1757,7 +1773,8 @@ hipError_t launch_attention_d(const AttnPlan& pl, const uint16_t* q,
     H2O_EVENT(2);
     const long wtotal = (long)BH * (g.C + g.S);
     if (pl.small) {
-        hipLaunchKernelGGL(wsum_from_logits_kernel, dim3((unsigned)((wtotal + 255) / 256)),
+        const long qtotal = (long)BH * ((g.C + g.S + 3) / 4);
+        hipLaunchKernelGGL(wsum_from_logits_kernel, dim3((unsigned)((qtotal + 255) / 256)),
                            dim3(256), 0, stream, g, wpart, l2, wsum);
         H2O_CHECK();
         H2O_EVENT(3);
