@@ -165,22 +165,22 @@ __global__ __launch_bounds__(SEL_T) void evict_select_kernel(
         for (int t = tid; t < S; t += SEL_T) out[t] = n + t;
         return;
     }
-    const int j0 = tid * KPT;
-    uint32_t key[KPT];
-#pragma unroll
-    for (int e = 0; e < KPT; ++e) {
-        const int j = j0 + e;
-        key[e] = (j < C) ? slot_key(sc, j, n) : 0xFFFFFFFFu;
-    }
-    // slots past C carry key ~0 and must never be counted or taken
-    const int cnt = max(0, min(KPT, C - j0));
-
     if (S == 1) {   // cache full (n == C): lexicographic min of (key, slot)
+        // the minimum does not depend on which thread reads which slot, so
+        // thread t takes slots t, t + SEL_T, ... (coalesced loads, all issued
+        // before the compares)
+        uint32_t kk[KPT];
+#pragma unroll
+        for (int e = 0; e < KPT; ++e) {
+            const int j = e * SEL_T + tid;
+            kk[e] = j < C ? slot_key(sc, j, n) : 0xFFFFFFFFu;
+        }
         unsigned long long best = ~0ull;
 #pragma unroll
         for (int e = 0; e < KPT; ++e) {
-            const unsigned long long kj = ((unsigned long long)key[e] << 32) | (unsigned)(j0 + e);
-            best = (e < cnt && kj < best) ? kj : best;
+            const int j = e * SEL_T + tid;
+            const unsigned long long kj = ((unsigned long long)kk[e] << 32) | (unsigned)j;
+            best = (j < C && kj < best) ? kj : best;
         }
 #pragma unroll
         for (int off = 32; off >= 1; off >>= 1) {
@@ -194,6 +194,15 @@ __global__ __launch_bounds__(SEL_T) void evict_select_kernel(
         if (tid == 0) out[0] = (int32_t)(sh_min & 0xFFFFFFFFull);
         return;
     }
+    const int j0 = tid * KPT;
+    uint32_t key[KPT];
+#pragma unroll
+    for (int e = 0; e < KPT; ++e) {
+        const int j = j0 + e;
+        key[e] = (j < C) ? slot_key(sc, j, n) : 0xFFFFFFFFu;
+    }
+    // slots past C carry key ~0 and must never be counted or taken
+    const int cnt = max(0, min(KPT, C - j0));
 
     uint32_t prefix = 0u, mask = 0u, k = (uint32_t)S;   // k: 1-based rank
     for (int pass = 0; pass < 4; ++pass) {
