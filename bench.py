@@ -221,22 +221,47 @@ def measured_traffic(workload, kernel):
             "source": os.path.relpath(path, ROOT)}
 
 
+def _host_info():
+    """BLAS threads the oracle's matrix products use, the BLAS library behind
+    NumPy, the CPU model and the host's core counts (after NumPy is loaded,
+    so that its BLAS pool is visible)."""
+    import numpy as np  # noqa: F401  (loads the BLAS pool)
+    threads, blas = len(os.sched_getaffinity(0)), "unknown"
+    try:
+        from threadpoolctl import threadpool_info
+        pools = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        if pools:
+            threads = max(i.get("num_threads", 1) for i in pools)
+            blas = ", ".join(f"{i.get('internal_api')} {i.get('version')}" for i in pools)
+    except Exception:
+        pass
+    model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return {"threads": int(threads), "blas": blas, "cpu_model": model,
+            "host_cpus": os.cpu_count(), "affinity_cpus": len(os.sched_getaffinity(0))}
+
+
 def cpu_baseline(wl, min_seconds=10.0, max_heads=24, q8=False):
-    """The oracle (float64, as it stands) on single-KV-head slices of steady
-    layer-steps, repeated until about ``min_seconds`` of CPU work; scaled to
-    tokens/s of the whole workload.  q8: the 8-bit cache step."""
+    """The oracle as it stands, run in float32 (its ``dtype`` argument), on
+    single-KV-head slices of steady layer-steps, repeated until about
+    ``min_seconds`` of CPU work; scaled to tokens/s of the whole workload.
+    q8: the 8-bit cache step."""
     import numpy as np
     import oracle
     import synth
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:
-        threads = len(os.sched_getaffinity(0))
+    host = _host_info()
+    threads = host["threads"]
+    f32 = np.float32
     G = wl.group
     sub = wl.with_(n_kv_heads=1, n_q_heads=G, batch=1)
     st = synth.steady_state(sub)
-    k, v, sc = st.k, st.v, st.scores.astype(np.float64)
+    k, v, sc = st.k, st.v, st.scores.astype(np.float32)
     if q8:
         kq, ks = oracle.quantize_rows_int8(k)
         vq, vs = oracle.quantize_rows_int8(v)
@@ -245,17 +270,18 @@ def cpu_baseline(wl, min_seconds=10.0, max_heads=24, q8=False):
         ch = synth.gen_chunk(sub, 0, sub.fill_steps + 2 + heads)
         t0 = time.perf_counter()
         if q8:
-            oracle.h2o_step_q8(kq, ks, vq, vs, sc, st.pos, st.n_valid, ch.q, ch.k, ch.v, ch.p0)
+            oracle.h2o_step_q8(kq, ks, vq, vs, sc, st.pos, st.n_valid, ch.q, ch.k, ch.v, ch.p0,
+                               dtype=f32)
         else:
-            oracle.h2o_step(k, v, sc, st.pos, st.n_valid, ch.q, ch.k, ch.v, ch.p0)
+            oracle.h2o_step(k, v, sc, st.pos, st.n_valid, ch.q, ch.k, ch.v, ch.p0, dtype=f32)
         spent += time.perf_counter() - t0
         heads += 1
     per_head = spent / heads
     total = per_head * wl.n_kv_heads * wl.batch * wl.layers   # s per step, all heads/layers
     return {"value": wl.chunk_len * wl.batch / total, "unit": "tokens/s", "cores": int(threads),
-            "kind": "oracle",
+            "kind": "oracle", "dtype": "float32", **host,
             "sample": (f"{heads} steady layer-steps of one KV head each ({G} query heads, "
-                       f"C={wl.cache_len}, S={wl.chunk_len}), float64, {spent:.1f} s; "
+                       f"C={wl.cache_len}, S={wl.chunk_len}), float32, {spent:.1f} s; "
                        f"scaled x{wl.n_kv_heads * wl.batch} heads x{wl.layers} layers")}
 
 
@@ -354,33 +380,30 @@ def run_backward(args, wl):
 
 
 def cpu_baseline_snapkv(wl):
-    """The oracle (float64) on one KV head of one layer of the SnapKV-style
+    """The oracle (float32) on one KV head of one layer of the SnapKV-style
     one-shot choice (window attention over the prompt cache, keep choice,
     compaction), scaled to window tokens/s of the whole workload."""
     import numpy as np
     import oracle
     import synth
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:
-        threads = len(os.sched_getaffinity(0))
+    host = _host_info()
+    threads = host["threads"]
     G = wl.group
     sub = wl.with_(n_kv_heads=1, n_q_heads=G, batch=1)
     st = synth.prefilled_state(sub)
     ch = synth.gen_chunk(sub, 0, 0)
     k, v = st.k, st.v
     t0 = time.perf_counter()
-    _, _, wsum = oracle.attention_chunk(ch.q, k, v, ch.k, ch.v, st.n_valid)
+    _, _, wsum = oracle.attention_chunk(ch.q, k, v, ch.k, ch.v, st.n_valid, dtype=np.float32)
     keep = oracle.snapkv_keep(wsum, st.n_valid, wl.keep_budget)
     oracle.snapkv_compact(k, v, st.pos, ch.k, ch.v, wsum, keep,
                           wl.keep_budget + wl.chunk_len, ch.p0)
     spent = time.perf_counter() - t0
     total = spent * wl.n_kv_heads * wl.batch * wl.layers
     return {"value": wl.chunk_len * wl.batch / total, "unit": "tokens/s", "cores": int(threads),
-            "kind": "oracle",
+            "kind": "oracle", "dtype": "float32", **host,
             "sample": (f"one KV head ({G} query heads) of one layer: window attention over "
-                       f"{wl.cache_len} slots, keep choice, compaction; float64, {spent:.1f} s; "
+                       f"{wl.cache_len} slots, keep choice, compaction; float32, {spent:.1f} s; "
                        f"scaled x{wl.n_kv_heads * wl.batch} heads x{wl.layers} layers")}
 
 

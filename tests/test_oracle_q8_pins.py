@@ -96,3 +96,99 @@ def test_scatter_writes_the_quantised_chunk():
             assert pos[0, h, j] == 40 + t
         untouched = [j for j in range(C) if j not in ev[0, h]]
         assert (kq[0, h, untouched] == 0).all() and (pos[0, h, untouched] == -1).all()
+
+
+def _representable_rows(rng, shape, e_lo, e_hi):
+    """Rows that the 8-bit format stores exactly: integer vectors whose
+    largest magnitude is 127, times 2^e with one e per row.  Returns the
+    values and, for an independent check of the stored rows, the integers
+    and the exponents."""
+    ints = rng.integers(-126, 127, size=shape).astype(np.float32)
+    ints[..., 0] = np.where(rng.random(shape[:-1]) < 0.5, 127, -127)
+    e = rng.integers(e_lo, e_hi, size=shape[:-1])
+    return ints * np.float32(2.0) ** e[..., None].astype(np.float32), ints, e
+
+
+def test_scatter_writes_codes_scale_and_score_of_every_token():
+    # K and V rows exactly representable with different exponent ranges, so
+    # every written code and scale is known in advance; distinct new scores
+    # per (head, token), so a token or head index slip shows
+    rng = np.random.default_rng(24)
+    B, Hkv, C, D, S = 2, 2, 11, 8, 4
+    kn, ki, ke = _representable_rows(rng, (B, Hkv, S, D), -6, -1)
+    vn, vi, ve = _representable_rows(rng, (B, Hkv, S, D), 1, 5)
+    kq = np.full((B, Hkv, C, D), 3, np.int8)
+    vq = np.full((B, Hkv, C, D), -3, np.int8)
+    ks = np.full((B, Hkv, C), 7.0, np.float32)
+    vs = np.full((B, Hkv, C), 9.0, np.float32)
+    sc = np.full((B, Hkv, C), -1.0)
+    pos = np.full((B, Hkv, C), -1, np.int64)
+    new_sc = np.arange(B * Hkv * S, dtype=np.float64).reshape(B, Hkv, S) + 0.25
+    ev = np.array([[[0, 3, 4, 10], [1, 2, 7, 8]], [[5, 6, 9, 10], [0, 1, 2, 3]]])
+    oracle.kv_scatter_q8(kq, ks, vq, vs, sc, pos, kn, vn, new_sc, ev, p0=100)
+    for b in range(B):
+        for h in range(Hkv):
+            for t in range(S):
+                j = ev[b, h, t]
+                assert kq[b, h, j].tolist() == ki[b, h, t].astype(int).tolist()
+                assert vq[b, h, j].tolist() == vi[b, h, t].astype(int).tolist()
+                assert ks[b, h, j] == np.float32(2.0 ** ke[b, h, t])
+                assert vs[b, h, j] == np.float32(2.0 ** ve[b, h, t])
+                assert sc[b, h, j] == new_sc[b, h, t]
+                assert pos[b, h, j] == 100 + t
+            rest = [j for j in range(C) if j not in ev[b, h]]
+            assert (kq[b, h, rest] == 3).all() and (vq[b, h, rest] == -3).all()
+            assert (ks[b, h, rest] == 7).all() and (vs[b, h, rest] == 9).all()
+            assert (sc[b, h, rest] == -1).all() and (pos[b, h, rest] == -1).all()
+
+
+def test_whole_q8_step_equals_the_unquantised_step_on_representable_rows():
+    # every K/V row (cache and chunk) is exactly representable, with per-row
+    # power-of-two scales drawn from different ranges for K and V: the 8-bit
+    # step must then equal the unquantised step bit for bit over a whole run
+    # (fill, partial overflow and eviction steps), and the stored codes and
+    # scales of every slot must be those of the token its position names
+    rng = np.random.default_rng(25)
+    B, Hq, Hkv, D, C, S, steps = 1, 4, 2, 16, 10, 4, 6
+    T = S * steps
+    kn_all, ki, ke = _representable_rows(rng, (B, Hkv, T, D), -5, 0)
+    vn_all, vi, ve = _representable_rows(rng, (B, Hkv, T, D), 0, 4)
+    q_all = rng.standard_normal((B, Hq, T, D)) * 0.02
+    kc = np.zeros((B, Hkv, C, D))
+    vc = np.zeros((B, Hkv, C, D))
+    kq = np.zeros((B, Hkv, C, D), np.int8)
+    vq = np.zeros((B, Hkv, C, D), np.int8)
+    ks = np.zeros((B, Hkv, C), np.float32)
+    vs = np.zeros((B, Hkv, C), np.float32)
+    sc = np.zeros((B, Hkv, C))
+    sc8 = np.zeros((B, Hkv, C))
+    pos = np.full((B, Hkv, C), -1, np.int64)
+    pos8 = pos.copy()
+    n = n8 = 0
+    for step in range(steps):
+        sl = slice(step * S, (step + 1) * S)
+        args = (q_all[:, :, sl], kn_all[:, :, sl], vn_all[:, :, sl], step * S)
+        r = oracle.h2o_step(kc, vc, sc, pos, n, *args)
+        r8 = oracle.h2o_step_q8(kq, ks, vq, vs, sc8, pos8, n8, *args)
+        for key in ("out", "lse", "wsum", "scores_acc", "new_scores", "evict_idx", "scores",
+                    "pos"):
+            np.testing.assert_array_equal(r8[key], r[key], err_msg=f"step {step} {key}")
+        assert r8["n_valid"] == r["n_valid"]
+        np.testing.assert_array_equal(oracle.dequantize_rows_int8(r8["kq"], r8["k_scale"]),
+                                      r["k_cache"])
+        np.testing.assert_array_equal(oracle.dequantize_rows_int8(r8["vq"], r8["v_scale"]),
+                                      r["v_cache"])
+        for b in range(B):
+            for h in range(Hkv):
+                for j in range(C):
+                    p = r8["pos"][b, h, j]
+                    if p < 0:
+                        continue
+                    assert r8["kq"][b, h, j].tolist() == ki[b, h, p].astype(int).tolist()
+                    assert r8["vq"][b, h, j].tolist() == vi[b, h, p].astype(int).tolist()
+                    assert r8["k_scale"][b, h, j] == np.float32(2.0 ** ke[b, h, p])
+                    assert r8["v_scale"][b, h, j] == np.float32(2.0 ** ve[b, h, p])
+        kc, vc, sc, pos, n = r["k_cache"], r["v_cache"], r["scores"], r["pos"], r["n_valid"]
+        kq, ks, vq, vs = r8["kq"], r8["k_scale"], r8["vq"], r8["v_scale"]
+        sc8, pos8, n8 = r8["scores"], r8["pos"], r8["n_valid"]
+    assert n == C   # the run reached eviction steps

@@ -135,3 +135,39 @@ def test_compacted_cache_attends_like_the_kept_keys(budget):
         vis[:, n + S:] = np.tril(np.ones((S2, S2), bool))
         want = _masked_attention(q2[0, a], keys, vals, vis, tau)
         np.testing.assert_allclose(got[0, a], want, rtol=1e-12, atol=1e-12)
+
+
+def test_compacted_rows_scores_and_positions_brute_force():
+    # the compacted cache written out by hand from a keep mask: the kept slots
+    # in slot order with their K, V, position and summed weight, then the
+    # window rows with their own columns; distinct weights per slot and head,
+    # so an index slip between slot and output row shows
+    rng = np.random.default_rng(16)
+    B, Hkv, C, D, S, n, budget, out_len = 2, 3, 20, 4, 3, 17, 6, 12
+    kc, vc = rng.standard_normal((B, Hkv, C, D)), rng.standard_normal((B, Hkv, C, D))
+    kn, vn = rng.standard_normal((B, Hkv, S, D)), rng.standard_normal((B, Hkv, S, D))
+    pos = rng.permutation(1000)[:B * Hkv * C].reshape(B, Hkv, C).astype(np.int64)
+    wsum = rng.permutation(B * Hkv * (C + S)).reshape(B, Hkv, C + S) * 0.5 + 0.125
+    keep = oracle.snapkv_keep(wsum, n, budget)
+    ko, vo, po, so = oracle.snapkv_compact(kc, vc, pos, kn, vn, wsum, keep, out_len, p0=500)
+    for b in range(B):
+        for h in range(Hkv):
+            # mask: the budget largest weights among the n valid slots
+            mask = np.zeros(C, bool)
+            mask[np.argsort(-wsum[b, h, :n])[:budget]] = True
+            rows = [j for j in range(C) if mask[j]]
+            assert len(rows) == budget
+            for i, j in enumerate(rows):
+                np.testing.assert_array_equal(ko[b, h, i], kc[b, h, j])
+                np.testing.assert_array_equal(vo[b, h, i], vc[b, h, j])
+                assert po[b, h, i] == pos[b, h, j]
+                assert so[b, h, i] == wsum[b, h, j]
+            for t in range(S):
+                i = budget + t
+                np.testing.assert_array_equal(ko[b, h, i], kn[b, h, t])
+                np.testing.assert_array_equal(vo[b, h, i], vn[b, h, t])
+                assert po[b, h, i] == 500 + t
+                assert so[b, h, i] == wsum[b, h, C + t]
+            tail = slice(budget + S, out_len)
+            assert (ko[b, h, tail] == 0).all() and (vo[b, h, tail] == 0).all()
+            assert (po[b, h, tail] == -1).all() and (so[b, h, tail] == 0).all()
