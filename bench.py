@@ -63,6 +63,11 @@ def parse():
     ap.add_argument("--backward", action="store_true",
                     help="time the attention backward (dQ, dK, dV with the slot layout "
                          "fixed) instead of the forward step")
+    ap.add_argument("--mfma-summary", nargs="+", metavar="PMC_DIR",
+                    help="print per-kernel SQ counters (MFMA ops and busy cycles, VALU and "
+                         "MFMA instructions, waits, LDS) of rocprofv3 --pmc runs of the "
+                         "default step, with the MFMA flops checked against the algorithmic "
+                         "count and the busy fraction against the SQ busy cycles")
     ap.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="print the copy-calibrated HBM bytes per dispatch of every h2o "
                          "kernel from a FETCH_SIZE and a WRITE_SIZE run (both with "
@@ -151,6 +156,61 @@ def traffic_summary(fetch_dir, write_dir):
             wb = write[k][0] * 1024.0 * w_scale
             print(f"{k:28s} fetch_bytes {fb:14.0f} write_bytes {wb:14.0f}   "
                   f"dispatches {fetch[k][1]}")
+
+
+def _pmc_avg(dirs):
+    """{kernel: {counter: average per dispatch}} over rocprofv3 --pmc csv runs
+    (counters summed over their instances within a dispatch)."""
+    import collections
+    import csv
+    import glob
+    out = collections.defaultdict(dict)
+    for d in dirs:
+        path = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)[0]
+        per = collections.defaultdict(lambda: collections.defaultdict(float))
+        for r in csv.DictReader(open(path)):
+            per[(_short(r["Kernel_Name"]), r["Counter_Name"])][int(r["Dispatch_Id"])] += \
+                float(r["Counter_Value"])
+        for (k, c), v in per.items():
+            out[k][c] = (sum(v.values()) / len(v), len(v))
+    return out
+
+
+def mfma_summary(dirs, workload="qwen3_4b_128k"):
+    """MFMA evidence of the attention kernels from SQ counters.
+
+    flop = SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512, against 4*D*pairs (pass 1) and
+    2*D*pairs (pass 2) of the steady layer-step; MFMA busy fraction =
+    SQ_VALU_MFMA_BUSY_CYCLES / (SQ_BUSY_CYCLES / shader engines x SIMDs),
+    i.e. over the cycles the kernel had waves resident, at the clock it ran."""
+    import synth
+    wl = synth.WORKLOADS[workload]
+    pairs = pairs_per_layer_step(wl.batch, wl.n_q_heads, wl.cache_len, wl.chunk_len,
+                                 wl.cache_len)
+    algo = {"attn_fwd_kernel<128>": 4 * wl.head_dim * pairs,
+            "attn_colsum_kernel<128>": 2 * wl.head_dim * pairs}
+    n_se, n_simd = 32, 1024    # 8 XCDs x 4 shader engines; 256 CUs x 4 SIMDs
+    data = _pmc_avg(dirs)
+    print(f"# SQ counters per dispatch, {workload} steady layer-step "
+          f"(pairs {pairs:.4e}); sources_sha1 {kernel_sources_sha1()}")
+    for k in sorted(data, key=lambda x: -data[x].get("SQ_BUSY_CYCLES", (0, 0))[0]):
+        if k.startswith("at::") or "elementwise" in k or "copyBuffer" in k:
+            continue
+        c = {n: v[0] for n, v in data[k].items()}
+        line = "  ".join(f"{n} {v:.0f}" for n, v in sorted(c.items()))
+        print(f"{k}: {line}")
+        if "SQ_INSTS_VALU_MFMA_MOPS_BF16" in c and c["SQ_INSTS_VALU_MFMA_MOPS_BF16"] > 0:
+            flop = c["SQ_INSTS_VALU_MFMA_MOPS_BF16"] * 512
+            msg = f"    mfma_flop {flop:.4e}"
+            if k in algo:
+                msg += f" = {flop / algo[k]:.4f} x algorithmic {algo[k]:.4e}"
+            if "SQ_VALU_MFMA_BUSY_CYCLES" in c and "SQ_BUSY_CYCLES" in c:
+                cyc = c["SQ_BUSY_CYCLES"] / n_se
+                msg += (f"; busy cycles per SE {cyc:.0f}; MFMA busy "
+                        f"{c['SQ_VALU_MFMA_BUSY_CYCLES'] / (cyc * n_simd):.3f} of SIMD-cycles")
+            if "SQ_INSTS_MFMA" in c and "SQ_INSTS_VALU" in c:
+                msg += f"; VALU/MFMA instructions {c['SQ_INSTS_VALU'] / c['SQ_INSTS_MFMA']:.2f}"
+            print(msg)
 
 
 def kernel_sources_sha1():
@@ -638,6 +698,9 @@ def main():
         return
     if args.traffic_summary:
         traffic_summary(*args.traffic_summary)
+        return
+    if args.mfma_summary:
+        mfma_summary(args.mfma_summary)
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
