@@ -27,13 +27,14 @@ from dataclasses import dataclass
 import torch
 
 from . import _lib
-from ._lib import H2OShape
+from ._lib import H2OShape, STATIC_SCRATCH_BYTES
 
 __all__ = ["Shape", "H2OError", "h2o_workspace_size", "h2o_attn_chunk",
            "h2o_score_accumulate", "h2o_evict_select", "kv_scatter",
            "h2o_attn_chunk_q8", "kv_scatter_q8", "h2o_quantize_rows_q8",
            "h2o_snapkv_select", "h2o_snapkv_compact", "h2o_attn_bwd_workspace_size", "h2o_attn_chunk_bwd",
            "h2o_timing_start", "h2o_timing_stop", "h2o_status_string", "H2OCache",
+           "h2o_attn_chunk_static", "STATIC_SCRATCH_BYTES",
            "load_library", "ATTN_KERNELS"]
 
 # the four kernels of h2o_attn_chunk, in launch order (h2o_timing_stop order)
@@ -132,6 +133,29 @@ def h2o_attn_chunk(shape: Shape, q, k_cache, v_cache, k_new, v_new, out, lse, ws
     _check(_lib.load().h2o_attn_chunk(ctypes.byref(sh), *args, ctypes.c_void_p(ws.data_ptr()),
                                       ctypes.c_size_t(nbytes), _stream(stream)),
            "h2o_attn_chunk")
+
+
+def h2o_attn_chunk_static(shape: Shape, q, k_cache, v_cache, k_new, v_new, out, lse, wsum,
+                          stream=None):
+    """h2o_attn_chunk with the library's static device scratch instead of a
+    caller workspace (for callers that cannot allocate); shapes whose
+    workspace exceeds STATIC_SCRATCH_BYTES are rejected."""
+    s = shape
+    B, Hq, Hkv, D, C, S = (s.batch, s.n_q_heads, s.n_kv_heads, s.head_dim,
+                           s.cache_len, s.chunk_len)
+    args = [
+        _ptr(q, "q", (B, Hq, S, D), _BF16),
+        _ptr(k_cache, "k_cache", (B, Hkv, C, D), _BF16),
+        _ptr(v_cache, "v_cache", (B, Hkv, C, D), _BF16),
+        _ptr(k_new, "k_new", (B, Hkv, S, D), _BF16),
+        _ptr(v_new, "v_new", (B, Hkv, S, D), _BF16),
+        _ptr(out, "out", (B, Hq, S, D), _F32),
+        ctypes.c_void_p(None) if lse is None else _ptr(lse, "lse", (B, Hq, S), _F32),
+        _ptr(wsum, "wsum", (B, Hkv, C + S), _F32),
+    ]
+    sh = s.c()
+    _check(_lib.load().h2o_attn_chunk_static(ctypes.byref(sh), *args, _stream(stream)),
+           "h2o_attn_chunk_static")
 
 
 def h2o_score_accumulate(shape: Shape, scores, new_scores, wsum, stream=None):

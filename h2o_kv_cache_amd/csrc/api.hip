@@ -10,9 +10,39 @@
 #include <math.h>
 #include <stdlib.h>
 
+#include <mutex>
 #include <vector>
 
+// Scratch of h2o_attn_chunk_static: one copy per device (the code object's
+// globals are instantiated on every device it is loaded on).  Host code
+// never uses this name as an address: it looks up each device's copy with
+// hipGetSymbolAddress and passes that pointer to the kernels.
+static __device__ __align__(256) unsigned char scratch[H2O_STATIC_SCRATCH_BYTES];
+
 namespace {
+
+// Device address of `scratch` on the current device, looked up once per
+// device (with that device current) and kept.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+hipError_t device_scratch(void** out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (!p || ((uintptr_t)p & 255u)) return hipErrorInvalidValue;
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return hipSuccess;
+}
 
 bool sync_debug() {
     static const bool on = [] {
@@ -93,6 +123,29 @@ h2o_status_t h2o_attn_chunk(const h2o_shape_t* s, const uint16_t* q, const uint1
     h2o::make_attn_plan(s->batch, s->n_q_heads, s->n_kv_heads, s->head_dim, s->cache_len,
                         s->chunk_len, s->n_valid, s->scale, &pl);
     if (!ws || ((uintptr_t)ws & 255u) || ws_bytes < pl.bytes) return H2O_ERR_WORKSPACE;
+    return from_hip(h2o::launch_attention(pl, q, k_cache, v_cache, k_new, v_new, out, lse,
+                                          wsum, ws, (hipStream_t)stream, sync_debug(),
+                                          timing_slot()));
+}
+
+h2o_status_t h2o_attn_chunk_static(const h2o_shape_t* s, const uint16_t* q,
+                                   const uint16_t* k_cache, const uint16_t* v_cache,
+                                   const uint16_t* k_new, const uint16_t* v_new, float* out,
+                                   float* lse, float* wsum, void* stream) {
+    h2o_status_t st = check_shape(s);
+    if (st != H2O_OK) return st;
+    if (!q || !k_cache || !v_cache || !k_new || !v_new || !out || !wsum)
+        return H2O_ERR_INVALID_ARG;
+    if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(k_new) ||
+        !aligned16(v_new) || !aligned16(out) || !aligned16(wsum) || (lse && !aligned16(lse)))
+        return H2O_ERR_INVALID_ARG;
+    h2o::AttnPlan pl;
+    h2o::make_attn_plan(s->batch, s->n_q_heads, s->n_kv_heads, s->head_dim, s->cache_len,
+                        s->chunk_len, s->n_valid, s->scale, &pl);
+    if (pl.bytes > H2O_STATIC_SCRATCH_BYTES) return H2O_ERR_WORKSPACE;
+    void* ws = nullptr;
+    st = from_hip(device_scratch(&ws));
+    if (st != H2O_OK) return st;
     return from_hip(h2o::launch_attention(pl, q, k_cache, v_cache, k_new, v_new, out, lse,
                                           wsum, ws, (hipStream_t)stream, sync_debug(),
                                           timing_slot()));

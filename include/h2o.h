@@ -282,6 +282,31 @@ h2o_status_t h2o_attn_chunk_bwd(const h2o_shape_t* shape, const uint16_t* q,
 h2o_status_t h2o_timing_start(int32_t max_calls);
 h2o_status_t h2o_timing_stop(double* ms, int32_t* calls);
 
+/* For callers that cannot allocate (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc): h2o_attn_chunk without a
+ * caller workspace.  The kernels' scratch (the key splits' partial outputs
+ * and row statistics, the row tiles' partial summed weights or the few-row
+ * path's stored logits) lives in a static device array of the library,
+ * H2O_STATIC_SCRATCH_BYTES on every GPU the library runs on, held until the
+ * process ends.  Nothing is allocated or freed by this call.
+ *   Arguments and results: as h2o_attn_chunk, without ws / ws_bytes.
+ *   Limit: shapes with h2o_workspace_size(shape) > H2O_STATIC_SCRATCH_BYTES
+ *          return H2O_ERR_WORKSPACE before anything is enqueued (the
+ *          Qwen3-4B-shaped 64k/128k layers, the 128-token chunks and 16-way
+ *          decode at 16384 slots all fit).
+ *   The first call on a device looks up that device's copy of the array
+ *   (hipGetSymbolAddress, with the device current); make it outside any
+ *   graph capture.  Every call on a GPU uses that GPU's one array and
+ *   leaves its contents behind: calls that overlap on one GPU (different
+ *   streams, or host threads without ordering) race and must be ordered by
+ *   the caller.  No element of the scratch has to start at zero: every
+ *   element a kernel reads was written earlier in the same call. */
+#define H2O_STATIC_SCRATCH_BYTES ((size_t)64 << 20)
+h2o_status_t h2o_attn_chunk_static(const h2o_shape_t* shape, const uint16_t* q,
+                                   const uint16_t* k_cache, const uint16_t* v_cache,
+                                   const uint16_t* k_new, const uint16_t* v_new,
+                                   float* out, float* lse, float* wsum, void* stream);
+
 /* Static, human-readable name of a status code. */
 const char* h2o_status_string(h2o_status_t status);
 

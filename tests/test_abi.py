@@ -218,3 +218,38 @@ def test_binding_argument_counts_match_the_header(lib):
         params = [p for p in m.group(1).split(",") if p.strip() and p.strip() != "void"]
         argtypes = getattr(lib, name).argtypes
         assert argtypes is not None and len(argtypes) == len(params), (name, len(params))
+
+
+def test_static_scratch_entry_point_checks(lib):
+    # argument and size checks of the no-workspace attention happen on the
+    # host before the device scratch is looked up or anything is enqueued
+    A = ctypes.c_void_p(4096)
+    M = ctypes.c_void_p(4098)
+    N = ctypes.c_void_p(None)
+    sh = _shape()
+    assert lib.h2o_workspace_size(ctypes.byref(sh)) <= _lib.STATIC_SCRATCH_BYTES
+    for k in range(8):
+        for bad in (N, M):
+            if k == 6 and bad is N:
+                continue  # lse may be NULL
+            args = [A] * 8
+            args[k] = bad
+            st = lib.h2o_attn_chunk_static(ctypes.byref(sh), *args, None)
+            assert st == _lib.H2O_ERR_INVALID_ARG, (k, bad)
+    for bad in (dict(batch=0), dict(n_valid=16385), dict(n_q_heads=12)):
+        assert lib.h2o_attn_chunk_static(ctypes.byref(_shape(**bad)), *([A] * 8),
+                                         None) == _lib.H2O_ERR_INVALID_ARG
+    assert lib.h2o_attn_chunk_static(ctypes.byref(_shape(head_dim=96)), *([A] * 8),
+                                     None) == _lib.H2O_ERR_UNSUPPORTED
+    # a shape whose workspace exceeds the static scratch (a 130048-slot cache
+    # with a 1024-token window) is refused
+    big = _shape(cache_len=130048, n_valid=130048)
+    assert lib.h2o_workspace_size(ctypes.byref(big)) > _lib.STATIC_SCRATCH_BYTES
+    assert lib.h2o_attn_chunk_static(ctypes.byref(big), *([A] * 8),
+                                     None) == _lib.H2O_ERR_WORKSPACE
+
+
+def test_static_scratch_size_matches_the_header():
+    text = open(HEADER).read()
+    m = re.search(r"#define H2O_STATIC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == _lib.STATIC_SCRATCH_BYTES
