@@ -57,6 +57,9 @@ def parse():
     ap.add_argument("--serial-policy", action="store_true",
                     help="issue the policy calls (accumulate, choice, scatter) on the same "
                          "stream as the attention instead of a second stream")
+    ap.add_argument("--separate-calls", action="store_true",
+                    help="with the policy calls on the attention stream, issue the four "
+                         "calls of a layer-step separately instead of h2o_step")
     ap.add_argument("--kv8", action="store_true",
                     help="8-bit KV cache (int8 codes + one fp32 scale per row): attention "
                          "over the int8 cache and the quantising scatter")
@@ -264,9 +267,10 @@ def measured_traffic(workload, kernel):
     summary (FETCH_SIZE + WRITE_SIZE, copy-calibrated), or None when there is
     none for this workload or the kernel source changed since it was taken."""
     import re
-    tag = {"qwen3_4b_128k": "qwen3_4b_128k"}.get(workload)
-    path = os.path.join(ROOT, "profiles", f"attn_fwd_{tag}_hbm_bytes.txt")
-    if tag is None or not os.path.exists(path):
+    name = {"qwen3_4b_128k": "attn_fwd_qwen3_4b_128k_hbm_bytes.txt",
+            "decode": "attn_fwd_small_decode_hbm_bytes.txt"}.get(workload)
+    path = os.path.join(ROOT, "profiles", name) if name else ""
+    if name is None or not os.path.exists(path):
         return None
     text = open(path).read()
     m = re.search(r"^sources_sha1 (\w+)", text, re.M)
@@ -562,8 +566,10 @@ def run_whole(args, wl):
             "fill_steps": len(fill), "eviction_steps": len(evict),
             "fill_step_ms_p10_p50_p90": pct(fill),
             "eviction_step_ms_p10_p50_p90": pct(evict),
-            "policy_stream": "same stream" if pstream is stream else
-                             "second stream, overlapped with the next layer's attention",
+            "policy_stream": ("same stream" if pstream is stream else
+                              "second stream, overlapped with the next layer's attention"),
+            "calls": "h2o_step (one call per layer-step)" if single_call else
+                     "h2o_attn_chunk, h2o_score_accumulate, h2o_evict_select, kv_scatter",
             "timing": "events around each step; inputs generated between steps",
         },
     }
@@ -651,6 +657,9 @@ def run_snapkv(args, wl):
 
     pairs = pairs_per_layer_step(B, Hq, C, S, C)
     per_layer = {k: v / calls for k, v in kernel_ms.items()}
+    if single_call and Hq // Hkv * S <= 32 and S == 1:
+        # h2o_step's decode path: the streaming pass, then one tail kernel
+        per_layer = {"attn_fwd": per_layer["attn_fwd"], "decode_tail": per_layer["attn_combine"]}
     per_layer.update(part_ms)
     fwd_ms = per_layer["attn_fwd"]
     fwd_flop = 4.0 * D * pairs
@@ -772,6 +781,10 @@ def main():
     ev_pol = [torch.cuda.Event() for _ in range(L)]
     p0_base = (C // S + 2) * S
 
+    # one stream and a bf16 cache: the whole layer-step in one call (for
+    # one-token chunks the work after the streaming pass is one kernel)
+    single_call = pstream is stream and not args.kv8 and not args.separate_calls
+
     def run_step(i, s_main=None):
         stream = s_main if s_main is not None else main_stream
         pstream = stream if policy_stream is main_stream else policy_stream
@@ -779,6 +792,10 @@ def main():
         for li, st in enumerate(layers):
             q, kn, vn = inputs[i][li]
             wsum, new_scores, evict = st["wsum"], st["new_scores"], st["evict"]
+            if single_call:
+                h2o.h2o_step(shape, q, st["k"], st["v"], kn, vn, out, lse, wsum, st["scores"],
+                             new_scores, evict, st["pos"], p0, ws, stream)
+                continue
             if pstream is not stream:
                 stream.wait_event(ev_pol[li])        # the cache after last step's scatter
             if args.kv8:
@@ -855,6 +872,9 @@ def main():
     pairs = pairs_per_layer_step(B, Hq, C, S, C)
     fwd_ms = kernel_ms["attn_fwd"] / calls
     per_layer = {k: v / calls for k, v in kernel_ms.items()}
+    if single_call and Hq // Hkv * S <= 32 and S == 1:
+        # h2o_step's decode path: the streaming pass, then one tail kernel
+        per_layer = {"attn_fwd": per_layer["attn_fwd"], "decode_tail": per_layer["attn_combine"]}
     # pass 1 reads every cached K/V row once plus the chunk's Q/K/V
     cache_row_bytes = (D + 4) if args.kv8 else 2 * D   # int8 codes + scale, or bf16
     fwd_bytes = (2.0 * B * Hkv * (C * cache_row_bytes + S * D * 2)) + B * Hq * S * D * 2
@@ -894,8 +914,10 @@ def main():
             "kv_cache": "int8 codes + fp32 row scales" if args.kv8 else "bf16",
             "phase": "steady state: cache full, S slots evicted per KV head per layer",
             "ms_per_layer_step": per_layer,
-            "policy_stream": "same stream" if pstream is stream else
-                             "second stream, overlapped with the next layer's attention",
+            "policy_stream": ("same stream" if pstream is stream else
+                              "second stream, overlapped with the next layer's attention"),
+            "calls": "h2o_step (one call per layer-step)" if single_call else
+                     "h2o_attn_chunk, h2o_score_accumulate, h2o_evict_select, kv_scatter",
             "executed_mfma_tflops_whole_step": step_tflops,
             "executed_mfma_frac_whole_step": step_tflops / PEAK_BF16_TFLOPS,
             "step_ms_p10_p50_p90": [float(np.percentile(step_ms, q)) for q in (10, 50, 90)],

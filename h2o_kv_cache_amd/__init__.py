@@ -34,7 +34,7 @@ __all__ = ["Shape", "H2OError", "h2o_workspace_size", "h2o_attn_chunk",
            "h2o_attn_chunk_q8", "kv_scatter_q8", "h2o_quantize_rows_q8",
            "h2o_snapkv_select", "h2o_snapkv_compact", "h2o_attn_bwd_workspace_size", "h2o_attn_chunk_bwd",
            "h2o_timing_start", "h2o_timing_stop", "h2o_status_string", "H2OCache",
-           "h2o_attn_chunk_static", "STATIC_SCRATCH_BYTES",
+           "h2o_attn_chunk_static", "STATIC_SCRATCH_BYTES", "h2o_step",
            "load_library", "ATTN_KERNELS"]
 
 # the four kernels of h2o_attn_chunk, in launch order (h2o_timing_stop order)
@@ -133,6 +133,37 @@ def h2o_attn_chunk(shape: Shape, q, k_cache, v_cache, k_new, v_new, out, lse, ws
     _check(_lib.load().h2o_attn_chunk(ctypes.byref(sh), *args, ctypes.c_void_p(ws.data_ptr()),
                                       ctypes.c_size_t(nbytes), _stream(stream)),
            "h2o_attn_chunk")
+
+
+def h2o_step(shape: Shape, q, k_cache, v_cache, k_new, v_new, out, lse, wsum, scores,
+             new_scores, evict_idx, pos, p0: int, ws, stream=None):
+    """The four calls of a step in one (attention, accumulation, choice,
+    scatter); one-token chunks on the few-row path run the work after the
+    streaming pass as one kernel."""
+    s = shape
+    B, Hq, Hkv, D, C, S = (s.batch, s.n_q_heads, s.n_kv_heads, s.head_dim,
+                           s.cache_len, s.chunk_len)
+    args = [
+        _ptr(q, "q", (B, Hq, S, D), _BF16),
+        _ptr(k_cache, "k_cache", (B, Hkv, C, D), _BF16),
+        _ptr(v_cache, "v_cache", (B, Hkv, C, D), _BF16),
+        _ptr(k_new, "k_new", (B, Hkv, S, D), _BF16),
+        _ptr(v_new, "v_new", (B, Hkv, S, D), _BF16),
+        _ptr(out, "out", (B, Hq, S, D), _F32),
+        ctypes.c_void_p(None) if lse is None else _ptr(lse, "lse", (B, Hq, S), _F32),
+        _ptr(wsum, "wsum", (B, Hkv, C + S), _F32),
+        _ptr(scores, "scores", (B, Hkv, C), _F32),
+        _ptr(new_scores, "new_scores", (B, Hkv, S), _F32),
+        _ptr(evict_idx, "evict_idx", (B, Hkv, S), (torch.int32,)),
+        ctypes.c_void_p(None) if pos is None else _ptr(pos, "pos", (B, Hkv, C), (torch.int64,)),
+    ]
+    if ws.device.type != "cuda" or not ws.is_contiguous():
+        raise ValueError("ws must be a contiguous device tensor")
+    nbytes = ws.numel() * ws.element_size()
+    sh = s.c()
+    _check(_lib.load().h2o_step(ctypes.byref(sh), *args, ctypes.c_int64(int(p0)),
+                                ctypes.c_void_p(ws.data_ptr()), ctypes.c_size_t(nbytes),
+                                _stream(stream)), "h2o_step")
 
 
 def h2o_attn_chunk_static(shape: Shape, q, k_cache, v_cache, k_new, v_new, out, lse, wsum,

@@ -19,7 +19,7 @@ EXPORTED = ("h2o_workspace_size", "h2o_attn_chunk", "h2o_score_accumulate",
             "h2o_quantize_rows_q8", "h2o_snapkv_select", "h2o_snapkv_compact",
             "h2o_attn_bwd_workspace_size",
             "h2o_attn_chunk_bwd", "h2o_timing_start", "h2o_timing_stop",
-            "h2o_attn_chunk_static", "h2o_status_string")
+            "h2o_attn_chunk_static", "h2o_step", "h2o_status_string")
 
 # bytes of the library's static scratch (H2O_STATIC_SCRATCH_BYTES in h2o.h)
 STATIC_SCRATCH_BYTES = 64 << 20
@@ -69,6 +69,8 @@ def _declare(lib):
     lib.h2o_timing_start.restype = ctypes.c_int
     lib.h2o_timing_stop.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int32)]
     lib.h2o_timing_stop.restype = ctypes.c_int
+    lib.h2o_step.argtypes = [S] + [P] * 12 + [ctypes.c_int64, P, ctypes.c_size_t, P]
+    lib.h2o_step.restype = ctypes.c_int
     lib.h2o_attn_chunk_static.argtypes = [S, P, P, P, P, P, P, P, P, P]
     lib.h2o_attn_chunk_static.restype = ctypes.c_int
     lib.h2o_status_string.argtypes = [ctypes.c_int]

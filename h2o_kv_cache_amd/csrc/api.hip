@@ -199,6 +199,44 @@ h2o_status_t kv_scatter(const h2o_shape_t* s, uint16_t* k_cache, uint16_t* v_cac
     return from_hip(e);
 }
 
+h2o_status_t h2o_step(const h2o_shape_t* s, const uint16_t* q, uint16_t* k_cache,
+                      uint16_t* v_cache, const uint16_t* k_new, const uint16_t* v_new, float* out,
+                      float* lse, float* wsum, float* scores, float* new_scores,
+                      int32_t* evict_idx, int64_t* pos, int64_t p0, void* ws, size_t ws_bytes,
+                      void* stream) {
+    h2o_status_t st = check_shape(s);
+    if (st != H2O_OK) return st;
+    const void* req[] = {q, k_cache, v_cache, k_new, v_new, out, wsum, scores, new_scores,
+                         evict_idx};
+    for (const void* p : req)
+        if (!p || !aligned16(p)) return H2O_ERR_INVALID_ARG;
+    if ((lse && !aligned16(lse)) || (pos && !aligned16(pos)) || p0 < 0)
+        return H2O_ERR_INVALID_ARG;
+    h2o::AttnPlan pl;
+    h2o::make_attn_plan(s->batch, s->n_q_heads, s->n_kv_heads, s->head_dim, s->cache_len,
+                        s->chunk_len, s->n_valid, s->scale, &pl);
+    if (!ws || ((uintptr_t)ws & 255u) || ws_bytes < pl.bytes) return H2O_ERR_WORKSPACE;
+    const hipStream_t str = (hipStream_t)stream;
+    if (h2o::decode_tail_applies(pl))
+        return from_hip(h2o::launch_decode_step(pl, q, k_cache, v_cache, k_new, v_new, out, lse,
+                                                wsum, scores, new_scores, evict_idx, pos, p0,
+                                                ws, str, sync_debug(), timing_slot()));
+    const int BH = s->batch * s->n_kv_heads;
+    hipError_t e = h2o::launch_attention(pl, q, k_cache, v_cache, k_new, v_new, out, lse, wsum,
+                                         ws, str, sync_debug(), timing_slot());
+    if (e == hipSuccess)
+        e = h2o::launch_score_accumulate(BH, s->cache_len, s->chunk_len, s->n_valid, scores,
+                                         new_scores, wsum, str);
+    if (e == hipSuccess)
+        e = h2o::launch_evict_select(BH, s->cache_len, s->chunk_len, s->n_valid, scores,
+                                     evict_idx, str);
+    if (e == hipSuccess)
+        e = h2o::launch_kv_scatter(BH, s->head_dim, s->cache_len, s->chunk_len, k_cache, v_cache,
+                                   scores, pos, k_new, v_new, new_scores, evict_idx, p0, str);
+    if (e == hipSuccess && sync_debug()) e = hipStreamSynchronize(str);
+    return from_hip(e);
+}
+
 h2o_status_t h2o_attn_chunk_q8(const h2o_shape_t* s, const uint16_t* q, const int8_t* k_cache,
                                const float* k_scale, const int8_t* v_cache,
                                const float* v_scale, const uint16_t* k_new,

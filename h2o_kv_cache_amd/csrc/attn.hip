@@ -748,22 +748,15 @@ merge:
         }
 }
 
-// Summed weights straight from the stored logits (few-row path): column j
-// sums 2^(u_rj - L2_r) over the rows that see it, in row order.  A thread
-// takes four consecutive columns, one 16-byte load per row (the logit rows
-// are padded to a multiple of 4 floats, so the quad stays inside the row).
-__global__ __launch_bounds__(256) void wsum_from_logits_kernel(
-    const AttnGeom g, const float* __restrict__ logits, const float* __restrict__ l2,
-    float* __restrict__ wsum) {
+// Summed weights of columns j0 .. j0+3 of one (b, kv head) straight from the
+// stored logits (few-row path): column j sums 2^(u_rj - L2_r) over the rows
+// that see it, in row order, one 16-byte load per row (the logit rows are
+// padded to a multiple of 4 floats, so the quad stays inside the row).
+// `lg` points at column j0 of row 0; `lb` at the rows' base-2 LSE.
+__device__ __forceinline__ void logit_quad_sums(const AttnGeom& g, const float* __restrict__ lg,
+                                                const float* lb, int j0, float (&s)[4]) {
     const int W = g.C + g.S;
-    const int nq = (W + 3) / 4;   // column quads per (b, kv head)
-    const long idx = (long)blockIdx.x * blockDim.x + threadIdx.x;
-    if (idx >= (long)g.B * g.Hkv * nq) return;
-    const int j0 = (int)(idx % nq) * 4;
-    const int bh = (int)(idx / nq);
     const int WL = logit_stride(g);
-    const float* lg = logits + (size_t)bh * g.R * WL + j0;
-    const float* lb = l2 + (size_t)bh * g.rows_pad;
     // column j0 + e is a valid cache slot or a chunk token, seen by rows
     // r >= r_lo[e] (row r sees chunk token t iff t*G <= r)
     bool col[4];
@@ -773,9 +766,9 @@ __global__ __launch_bounds__(256) void wsum_from_logits_kernel(
         const int jj = j0 + e;
         col[e] = jj < W && (jj < g.n || jj >= g.C);
         r_lo[e] = jj < g.C ? 0 : (jj - g.C) * g.G;
+        s[e] = 0.f;
     }
     // rows in order; the logits of 8 rows are loaded before they are summed
-    float s[4] = {0.f, 0.f, 0.f, 0.f};
     for (int r0 = 0; r0 < g.R; r0 += 8) {
         f32x4 x[8];
         float lr[8];
@@ -791,9 +784,99 @@ __global__ __launch_bounds__(256) void wsum_from_logits_kernel(
             for (int e = 0; e < 4; ++e)
                 if (r0 + u < g.R && col[e] && r0 + u >= r_lo[e]) s[e] += fast_exp2(x[u][e] - lr[u]);
     }
+}
+
+// Summed weights straight from the stored logits (few-row path): a thread
+// takes four consecutive columns.
+__global__ __launch_bounds__(256) void wsum_from_logits_kernel(
+    const AttnGeom g, const float* __restrict__ logits, const float* __restrict__ l2,
+    float* __restrict__ wsum) {
+    const int W = g.C + g.S;
+    const int nq = (W + 3) / 4;   // column quads per (b, kv head)
+    const long idx = (long)blockIdx.x * blockDim.x + threadIdx.x;
+    if (idx >= (long)g.B * g.Hkv * nq) return;
+    const int j0 = (int)(idx % nq) * 4;
+    const int bh = (int)(idx / nq);
+    float s[4];
+    logit_quad_sums(g, logits + (size_t)bh * g.R * logit_stride(g) + j0,
+                    l2 + (size_t)bh * g.rows_pad, j0, s);
 #pragma unroll
     for (int e = 0; e < 4; ++e)
         if (j0 + e < W) wsum[(size_t)bh * W + j0 + e] = s[e];
+}
+
+// ---------------------------------------------------------------------------
+// combine the key splits: O (normalised), natural LSE, base-2 L for pass 2
+// ---------------------------------------------------------------------------
+// Merge of the key splits of row r (dims 4*dc .. 4*dc+3): the largest split
+// reference M, the exact and the bf16-weight row sums L and Lt against M, and
+// the O sums.  Splits are combined in order; the loads of CB splits are
+// issued before any of them is used.
+template <int D>
+__device__ __forceinline__ void merge_splits(const AttnGeom& g, int nsplit,
+                                             const float* __restrict__ o_part,
+                                             const float* __restrict__ ml_part, int bh, int r,
+                                             int dc, float& M, float& L, float& Lt, f32x4& acc) {
+    const int BH = g.B * g.Hkv;
+    constexpr int CB = 8;
+    M = -INFINITY;
+    L = 0.f;
+    Lt = 0.f;
+    acc = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (nsplit <= 4) {   // few splits: one pass, all loads first
+        f32x4 ml[4], o[4];
+#pragma unroll
+        for (int sp = 0; sp < 4; ++sp) {
+            const size_t prow = ((size_t)sp * BH + bh) * g.rows_pad + r;
+            ml[sp] = sp < nsplit ? *(const f32x4*)(ml_part + prow * 4)
+                                 : f32x4{-INFINITY, 0.f, 0.f, 0.f};
+            o[sp] = sp < nsplit ? *(const f32x4*)(o_part + prow * D + dc * 4)
+                                : f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+#pragma unroll
+        for (int sp = 0; sp < 4; ++sp) M = fmaxf(M, ml[sp][0]);
+#pragma unroll
+        for (int sp = 0; sp < 4; ++sp) {
+            if (sp < nsplit) {
+                const float w = fast_exp2(ml[sp][0] - M);
+                L += w * ml[sp][1];
+                Lt += w * ml[sp][2];
+                acc += w * o[sp];
+            }
+        }
+        return;
+    }
+    for (int s0 = 0; s0 < nsplit; s0 += CB) {
+        float m[CB];
+#pragma unroll
+        for (int u = 0; u < CB; ++u) {
+            const int sp = s0 + u;
+            m[u] = sp < nsplit ? ml_part[(((size_t)sp * BH + bh) * g.rows_pad + r) * 4]
+                               : -INFINITY;
+        }
+#pragma unroll
+        for (int u = 0; u < CB; ++u) M = fmaxf(M, m[u]);
+    }
+    for (int s0 = 0; s0 < nsplit; s0 += CB) {
+        f32x4 ml[CB], o[CB];
+#pragma unroll
+        for (int u = 0; u < CB; ++u) {
+            const int sp = s0 + u;
+            const size_t prow = ((size_t)sp * BH + bh) * g.rows_pad + r;
+            ml[u] = sp < nsplit ? *(const f32x4*)(ml_part + prow * 4) : f32x4{0.f, 0.f, 0.f, 0.f};
+            o[u] = sp < nsplit ? *(const f32x4*)(o_part + prow * D + dc * 4)
+                               : f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+#pragma unroll
+        for (int u = 0; u < CB; ++u) {
+            if (s0 + u < nsplit) {
+                const float w = fast_exp2(ml[u][0] - M);
+                L += w * ml[u][1];
+                Lt += w * ml[u][2];
+                acc += w * o[u];
+            }
+        }
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -817,66 +900,9 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(
         if (dc == 0) l2[(size_t)bh * g.rows_pad + r] = INFINITY;
         return;
     }
-    // per split: (m, l, lt) with l the exact and lt the bf16-weight row sum.
-    // Splits are combined in order; the loads of CB splits are issued before
-    // any of them is used.
-    constexpr int CB = 8;
-    float M = -INFINITY;
-    float L = 0.f, Lt = 0.f;
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    if (nsplit <= 4) {   // few splits: one pass, all loads first
-        f32x4 ml[4], o[4];
-#pragma unroll
-        for (int sp = 0; sp < 4; ++sp) {
-            const size_t prow = ((size_t)sp * BH + bh) * g.rows_pad + r;
-            ml[sp] = sp < nsplit ? *(const f32x4*)(ml_part + prow * 4)
-                                 : f32x4{-INFINITY, 0.f, 0.f, 0.f};
-            o[sp] = sp < nsplit ? *(const f32x4*)(o_part + prow * D + dc * 4)
-                                : f32x4{0.f, 0.f, 0.f, 0.f};
-        }
-#pragma unroll
-        for (int sp = 0; sp < 4; ++sp) M = fmaxf(M, ml[sp][0]);
-#pragma unroll
-        for (int sp = 0; sp < 4; ++sp) {
-            if (sp < nsplit) {
-                const float w = fast_exp2(ml[sp][0] - M);
-                L += w * ml[sp][1];
-                Lt += w * ml[sp][2];
-                acc += w * o[sp];
-            }
-        }
-    }
-    for (int s0 = 0; nsplit > 4 && s0 < nsplit; s0 += CB) {
-        float m[CB];
-#pragma unroll
-        for (int u = 0; u < CB; ++u) {
-            const int sp = s0 + u;
-            m[u] = sp < nsplit ? ml_part[(((size_t)sp * BH + bh) * g.rows_pad + r) * 4]
-                               : -INFINITY;
-        }
-#pragma unroll
-        for (int u = 0; u < CB; ++u) M = fmaxf(M, m[u]);
-    }
-    for (int s0 = 0; nsplit > 4 && s0 < nsplit; s0 += CB) {
-        f32x4 ml[CB], o[CB];
-#pragma unroll
-        for (int u = 0; u < CB; ++u) {
-            const int sp = s0 + u;
-            const size_t prow = ((size_t)sp * BH + bh) * g.rows_pad + r;
-            ml[u] = sp < nsplit ? *(const f32x4*)(ml_part + prow * 4) : f32x4{0.f, 0.f, 0.f, 0.f};
-            o[u] = sp < nsplit ? *(const f32x4*)(o_part + prow * D + dc * 4)
-                               : f32x4{0.f, 0.f, 0.f, 0.f};
-        }
-#pragma unroll
-        for (int u = 0; u < CB; ++u) {
-            if (s0 + u < nsplit) {
-                const float w = fast_exp2(ml[u][0] - M);
-                L += w * ml[u][1];
-                Lt += w * ml[u][2];
-                acc += w * o[u];
-            }
-        }
-    }
+    float M, L, Lt;
+    f32x4 acc;
+    merge_splits<D>(g, nsplit, o_part, ml_part, bh, r, dc, M, L, Lt, acc);
     const float inv = 1.0f / Lt;
     const int b = bh / g.Hkv, h = bh % g.Hkv;
     const int i = r / g.G, a = h * g.G + r % g.G;
@@ -886,6 +912,140 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(
         const float L2 = M + fast_log2(L);
         l2[(size_t)bh * g.rows_pad + r] = L2;
         if (lse) lse[orow] = L2 * kLn2;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// One-token chunks on the few-row path: everything after the streaming pass
+// in one workgroup per (b, kv head) -- the split merge (O, LSE), the summed
+// weights from the stored logits, the score accumulation, the lexicographic
+// minimum of (score, slot) (or the first empty slot while the cache fills)
+// and the scatter of the token into that slot.  Each part does exactly the
+// arithmetic of its own kernel (combine, logits-to-weights, accumulation,
+// choice, scatter), so the results are those of the separate calls.
+// ---------------------------------------------------------------------------
+constexpr int TAIL_T = 1024;
+constexpr int TAIL_NQ = 4;   // column quads per thread in flight
+
+template <int D>
+__global__ __launch_bounds__(TAIL_T) void decode_tail_kernel(
+    const AttnGeom g, const int nsplit, const float* __restrict__ o_part,
+    const float* __restrict__ ml_part, const float* __restrict__ logits,
+    float* __restrict__ out, float* __restrict__ lse, float* __restrict__ wsum,
+    float* __restrict__ scores, float* __restrict__ new_scores,
+    int32_t* __restrict__ evict, uint16_t* __restrict__ kc, uint16_t* __restrict__ vc,
+    int64_t* __restrict__ pos, const uint16_t* __restrict__ kn,
+    const uint16_t* __restrict__ vn, int64_t p0) {
+    constexpr int CH = D / 4;
+    __shared__ float sh_l2[32];
+    __shared__ float sh_new;
+    __shared__ unsigned long long sh_min;
+    const int bh = blockIdx.x, tid = threadIdx.x;
+    const int W = g.C + 1;
+    // split merge: thread (r, dc) for the R <= 32 rows
+    if (tid < g.R * CH) {
+        const int r = tid / CH, dc = tid % CH;
+        float M, L, Lt;
+        f32x4 acc;
+        merge_splits<D>(g, nsplit, o_part, ml_part, bh, r, dc, M, L, Lt, acc);
+        const float inv = 1.0f / Lt;
+        const int b = bh / g.Hkv, h = bh % g.Hkv;
+        const int a = h * g.G + r;          // S = 1: row r is head h*G + r
+        const size_t orow = (size_t)b * g.Hq + a;
+        *(f32x4*)(out + orow * D + dc * 4) = acc * inv;
+        if (dc == 0) {
+            const float L2 = M + fast_log2(L);
+            sh_l2[r] = L2;
+            if (lse) lse[orow] = L2 * kLn2;
+        }
+    }
+    if (tid == 0) sh_min = ~0ull;
+    __syncthreads();
+    // summed weights, accumulated scores and the running minimum.  A thread
+    // takes TAIL_NQ column quads TAIL_T quads apart and issues all their
+    // loads (scores, then four logit rows at a time) before it uses any; per
+    // column the rows are summed in row order as in logit_quad_sums.
+    const float* lg = logits + (size_t)bh * g.R * logit_stride(g);
+    const int WL = logit_stride(g);
+    float* sc = scores + (size_t)bh * g.C;
+    float* wrow = wsum + (size_t)bh * W;
+    unsigned long long best = ~0ull;
+    for (int base = 4 * tid; base < W; base += 4 * TAIL_T * TAIL_NQ) {
+        float s[TAIL_NQ][4], old[TAIL_NQ][4];
+        int j0[TAIL_NQ];
+#pragma unroll
+        for (int k = 0; k < TAIL_NQ; ++k) {
+            j0[k] = base + 4 * TAIL_T * k;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                s[k][e] = 0.f;
+                const int j = j0[k] + e;
+                old[k][e] = j < g.n ? sc[j] : 0.f;
+            }
+        }
+        for (int r0 = 0; r0 < g.R; r0 += 4) {
+            f32x4 x[TAIL_NQ][4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int r = min(r0 + u, g.R - 1);
+#pragma unroll
+                for (int k = 0; k < TAIL_NQ; ++k)
+                    x[k][u] = j0[k] < W ? *(const f32x4*)(lg + (size_t)r * WL + j0[k])
+                                        : f32x4{0.f, 0.f, 0.f, 0.f};
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                if (r0 + u >= g.R) break;
+                const float lr = sh_l2[r0 + u];
+#pragma unroll
+                for (int k = 0; k < TAIL_NQ; ++k)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int j = j0[k] + e;
+                        if (j < g.n || j == g.C) s[k][e] += fast_exp2(x[k][u][e] - lr);
+                    }
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < TAIL_NQ; ++k)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int j = j0[k] + e;
+                if (j >= W) continue;
+                wrow[j] = s[k][e];
+                if (j < g.n) {
+                    const float acc = old[k][e] + s[k][e];
+                    sc[j] = acc;
+                    const unsigned long long kj =
+                        ((unsigned long long)score_key(acc) << 32) | (unsigned)j;
+                    best = kj < best ? kj : best;
+                } else if (j == g.C) {
+                    sh_new = s[k][e];
+                }
+            }
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+        const unsigned long long o = __shfl_xor(best, off, 64);
+        best = o < best ? o : best;
+    }
+    if ((tid & 63) == 0) atomicMin(&sh_min, best);
+    __syncthreads();
+    // the choice: the first empty slot while the cache fills, else the
+    // lexicographic minimum; then the scatter of the token into it
+    const int slot = g.n < g.C ? g.n : (int)(sh_min & 0xFFFFFFFFull);
+    constexpr int TPR = D / 8;   // threads per row (16 bytes each)
+    if (tid < 2 * TPR) {
+        const int which = tid / TPR, c = tid % TPR;
+        const uint16_t* src = (which ? vn : kn) + (size_t)bh * D + c * 8;
+        uint16_t* dst = (which ? vc : kc) + ((size_t)bh * g.C + slot) * D + c * 8;
+        *(u32x4*)dst = *(const u32x4*)src;
+        if (tid == 0) {
+            evict[bh] = slot;
+            new_scores[bh] = sh_new;
+            sc[slot] = sh_new;
+            if (pos) pos[(size_t)bh * g.C + slot] = p0;
+        }
     }
 }
 
@@ -1841,6 +2001,55 @@ hipError_t launch_attention(const AttnPlan& plan, const uint16_t* q, const uint1
                                              stream, sync_debug, ev5);
     return launch_attention_d<128, false>(plan, q, kc, vc, none, kn, vn, out, lse, wsum, ws,
                                           stream, sync_debug, ev5);
+}
+
+// One-token step on the few-row path: the streaming pass, then the tail
+// kernel (split merge, summed weights, accumulation, choice, scatter).
+template <int D>
+hipError_t launch_decode_step_d(const AttnPlan& pl, const uint16_t* q, uint16_t* kc,
+                                uint16_t* vc, const uint16_t* kn, const uint16_t* vn,
+                                float* out, float* lse, float* wsum, float* scores,
+                                float* new_scores, int32_t* evict, int64_t* pos, int64_t p0,
+                                void* ws, hipStream_t stream, bool sync_debug, hipEvent_t* ev) {
+    const AttnGeom& g = pl.g;
+    char* w = (char*)ws;
+    float* o_part = (float*)(w + pl.off_o);
+    float* ml_part = (float*)(w + pl.off_ml);
+    float* logits = (float*)(w + pl.off_wp);
+    const int BH = g.B * g.Hkv;
+    hipError_t err;
+    auto check = [&]() {
+        err = hipGetLastError();
+        if (err == hipSuccess && sync_debug) err = hipStreamSynchronize(stream);
+        return err;
+    };
+    auto event = [&](int i) { return ev ? hipEventRecord(ev[i], stream) : hipSuccess; };
+    if ((err = event(0)) != hipSuccess) return err;
+    hipLaunchKernelGGL(attn_fwd_small_kernel<D>, dim3(BH * pl.split1), dim3(NT_S), 0, stream, g,
+                       pl.split1, q, kc, vc, kn, vn, o_part, ml_part, logits);
+    if (check() != hipSuccess) return err;
+    if ((err = event(1)) != hipSuccess) return err;
+    hipLaunchKernelGGL(decode_tail_kernel<D>, dim3(BH), dim3(TAIL_T), 0, stream, g, pl.split1,
+                       o_part, ml_part, logits, out, lse, wsum, scores, new_scores, evict, kc,
+                       vc, pos, kn, vn, p0);
+    if (check() != hipSuccess) return err;
+    for (int i = 2; i < 5; ++i)
+        if ((err = event(i)) != hipSuccess) return err;
+    return hipSuccess;
+}
+
+bool decode_tail_applies(const AttnPlan& pl) { return pl.small && pl.g.S == 1; }
+
+hipError_t launch_decode_step(const AttnPlan& pl, const uint16_t* q, uint16_t* kc,
+                              uint16_t* vc, const uint16_t* kn, const uint16_t* vn, float* out,
+                              float* lse, float* wsum, float* scores, float* new_scores,
+                              int32_t* evict, int64_t* pos, int64_t p0, void* ws,
+                              hipStream_t stream, bool sync_debug, hipEvent_t* ev5) {
+    if (pl.g.D == 64)
+        return launch_decode_step_d<64>(pl, q, kc, vc, kn, vn, out, lse, wsum, scores,
+                                        new_scores, evict, pos, p0, ws, stream, sync_debug, ev5);
+    return launch_decode_step_d<128>(pl, q, kc, vc, kn, vn, out, lse, wsum, scores, new_scores,
+                                     evict, pos, p0, ws, stream, sync_debug, ev5);
 }
 
 hipError_t launch_attention_q8(const AttnPlan& plan, const uint16_t* q, const int8_t* kc,

@@ -55,4 +55,14 @@ __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) {
     return __builtin_bit_cast(bf16x8, v);
 }
 
+// Order-preserving map of a score onto uint32: -0.0 == +0.0, NaN above +inf.
+// Every mapped score is >= 0x007FFFFF (the image of -inf), so key 0 is free
+// for empty slots, which are taken first.
+__device__ __forceinline__ uint32_t score_key(float x) {
+    uint32_t u = __float_as_uint(x);
+    if (x != x) return 0xFFFFFFFFu;
+    if (u == 0x80000000u) u = 0u;
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
 }  // namespace h2o

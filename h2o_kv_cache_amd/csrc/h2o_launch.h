@@ -41,6 +41,19 @@ hipError_t launch_attention(const AttnPlan& plan, const uint16_t* q,
                             hipStream_t stream, bool sync_debug,
                             hipEvent_t* ev5 /* nullable: 5 timing events */);
 
+// A whole one-token step on the few-row path (decode_tail_applies): the
+// streaming attention pass, then one kernel for the split merge, the summed
+// weights, the score accumulation, the choice and the scatter.  Same results
+// as launch_attention + launch_score_accumulate + launch_evict_select +
+// launch_kv_scatter.
+bool decode_tail_applies(const AttnPlan& plan);
+hipError_t launch_decode_step(const AttnPlan& plan, const uint16_t* q, uint16_t* kc,
+                              uint16_t* vc, const uint16_t* kn, const uint16_t* vn, float* out,
+                              float* lse, float* wsum, float* scores, float* new_scores,
+                              int32_t* evict, int64_t* pos, int64_t p0, void* ws,
+                              hipStream_t stream, bool sync_debug,
+                              hipEvent_t* ev5 /* nullable: 5 timing events */);
+
 // The same attention over an 8-bit cache: int8 codes [B, Hkv, C, D] and one
 // float scale per row [B, Hkv, C] for K and V; same plan and workspace.
 hipError_t launch_attention_q8(const AttnPlan& plan, const uint16_t* q, const int8_t* kc,

@@ -33,16 +33,6 @@ __global__ __launch_bounds__(256) void score_accumulate_kernel(
 // ---------------------------------------------------------------------------
 // slot choice
 // ---------------------------------------------------------------------------
-// Order-preserving map of a score onto uint32: -0.0 == +0.0, NaN above +inf.
-// Every mapped score is >= 0x007FFFFF (the image of -inf), so key 0 is free
-// for empty slots, which are taken first.
-__device__ __forceinline__ uint32_t score_key(float x) {
-    uint32_t u = __float_as_uint(x);
-    if (x != x) return 0xFFFFFFFFu;
-    if (u == 0x80000000u) u = 0u;
-    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
-
 constexpr int SEL_T = 1024;   // threads per (b, kv head)
 
 __device__ __forceinline__ uint32_t slot_key(const float* __restrict__ sc, int j, int n) {

@@ -148,6 +148,24 @@ h2o_status_t kv_scatter(const h2o_shape_t* shape, uint16_t* k_cache,
                         const float* new_scores, const int32_t* evict_idx,
                         int64_t p0, void* stream);
 
+/* One whole step -- h2o_attn_chunk, h2o_score_accumulate, h2o_evict_select
+ * and kv_scatter in that order, on one stream, with the same arguments and
+ * results (the choice is written to evict_idx; scores ends as after
+ * kv_scatter).  For one-token chunks (chunk_len == 1) with at most 32 query
+ * heads per KV head -- the decode step, the few-queries-many-keys regime of
+ * [LtF] Chinese page §2 -- everything after the streaming attention pass
+ * (merging the key splits, the summed weights, the score update, the
+ * lowest (score, slot) choice and the one-row scatter) runs as a single
+ * kernel per (b, KV head) instead of five launches; its results are those of
+ * the separate calls bit for bit.
+ *   arguments as for the four calls; lse and pos may be NULL;
+ *   ws, ws_bytes: at least h2o_workspace_size(shape) bytes, 256-byte aligned. */
+h2o_status_t h2o_step(const h2o_shape_t* shape, const uint16_t* q, uint16_t* k_cache,
+                      uint16_t* v_cache, const uint16_t* k_new, const uint16_t* v_new,
+                      float* out, float* lse, float* wsum, float* scores,
+                      float* new_scores, int32_t* evict_idx, int64_t* pos, int64_t p0,
+                      void* ws, size_t ws_bytes, void* stream);
+
 /* 8-bit KV cache (Q-Hitter-like H2O).  ([LtF] Chinese page §2: cache
  * buffers can be quantised to 8 bits or fewer; Q-Hitter combines H2O with
  * such quantisation.)  Reading used here: every cached (token, KV head) row

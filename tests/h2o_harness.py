@@ -93,6 +93,32 @@ def gpu_step(shape: h2o.Shape, st: HostState, q_bits, k_bits, v_bits, p0, runs=1
     return results if runs > 1 else results[0]
 
 
+def gpu_step_fused(shape: h2o.Shape, st: HostState, q_bits, k_bits, v_bits, p0):
+    """One step through the single-call entry point h2o_step; host copies in
+    the layout of gpu_step (scores_acc is not observable here and is left
+    out)."""
+    B, Hq, Hkv, D, C, S = (shape.batch, shape.n_q_heads, shape.n_kv_heads, shape.head_dim,
+                           shape.cache_len, shape.chunk_len)
+    shape = shape.with_n(st.n_valid)
+    kc, vc = dev_bf16(st.k_bits), dev_bf16(st.v_bits)
+    scores = torch.from_numpy(st.scores.astype(np.float32)).cuda()
+    pos = torch.from_numpy(st.pos.astype(np.int64)).cuda()
+    q, kn, vn = dev_bf16(q_bits), dev_bf16(k_bits), dev_bf16(v_bits)
+    out = torch.full((B, Hq, S, D), float("nan"), device="cuda")
+    lse = torch.full((B, Hq, S), float("nan"), device="cuda")
+    wsum = torch.full((B, Hkv, C + S), float("nan"), device="cuda")
+    new_scores = torch.full((B, Hkv, S), float("nan"), device="cuda")
+    evict = torch.full((B, Hkv, S), -7, dtype=torch.int32, device="cuda")
+    ws = torch.full((max(h2o.h2o_workspace_size(shape), 256),), 0xFF, dtype=torch.uint8,
+                    device="cuda")
+    h2o.h2o_step(shape, q, kc, vc, kn, vn, out, lse, wsum, scores, new_scores, evict, pos, p0, ws)
+    torch.cuda.synchronize()
+    return dict(out=out.cpu().numpy(), lse=lse.cpu().numpy(), wsum=wsum.cpu().numpy(),
+                new_scores=new_scores.cpu().numpy(), evict_idx=evict.cpu().numpy(),
+                k_bits=host_bits(kc), v_bits=host_bits(vc), scores=scores.cpu().numpy(),
+                pos=pos.cpu().numpy())
+
+
 def oracle_step(st: HostState, q_bits, k_bits, v_bits, p0, scale=None, heads=None):
     """The oracle on the same inputs (float64).  ``heads`` restricts the
     comparison to a subset of KV heads (per-head work is independent)."""
