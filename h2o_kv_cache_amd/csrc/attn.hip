@@ -97,6 +97,19 @@ struct BufC {
     static constexpr int value = N;
 };
 
+// Per (b, kv head) state of the one-token step's tail (decode_tail_kernel,
+// decode_scatter_kernel), 16 bytes in the workspace: the running minimum
+// (score key << 32 | slot) over the tail's workgroups.  The streaming pass
+// (its split-0 workgroup) resets it before the tail runs.
+struct TailState {
+    unsigned long long min_key;
+    unsigned long long pad;
+};
+
+__device__ __forceinline__ void tail_state_init(TailState* ts, int bh) {
+    if (ts) ts[bh].min_key = ~0ull;
+}
+
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 constexpr bf16x2 kOnes2 = {(__bf16)1.0f, (__bf16)1.0f};
 
@@ -112,7 +125,7 @@ constexpr bf16x2 kOnes2 = {(__bf16)1.0f, (__bf16)1.0f};
 // of key j (vsc[lkb*32 + j]) multiplies P before its bf16 rounding, and O is
 // normalised by the exact row sum (lt_acc = l_acc).
 template <int D, bool MASKED, bool KSC = false, bool K8 = false, bool V8 = false,
-          bool TRACK = true>
+          bool TRACK = true, bool KREG = false>
 __device__ __forceinline__ void fwd_block(const uint16_t* Ks, const uint16_t* Vs,
                                           const LdsOffsets<D>& off,
                                           const bf16x8 (&qf)[RB][D / 16],
@@ -125,7 +138,8 @@ __device__ __forceinline__ void fwd_block(const uint16_t* Ks, const uint16_t* Vs
                                           const uint8_t* k8 = nullptr,
                                           const uint8_t* v8 = nullptr,
                                           const float* vsc = nullptr,
-                                          float* lg_stage = nullptr) {
+                                          float* lg_stage = nullptr,
+                                          const bf16x8* kreg = nullptr) {
     const int l32 = lane & 31, half = lane >> 5;
     {
         f32x16 s[RB];
@@ -142,6 +156,8 @@ __device__ __forceinline__ void fwd_block(const uint16_t* Ks, const uint16_t* Vs
             bf16x8 kf;
             if constexpr (K8)
                 kf = i8x8_to_bf16(*(const uint2*)(k8row + 16 * (ks ^ i8_swz<D>(krow))));
+            else if constexpr (KREG)
+                kf = kreg[ks];   // loaded from memory straight into registers
             else
                 kf = as_bf16x8(lds_read16(Ks, off.k[ks] + lkb * 64 * D));
 #pragma unroll
@@ -530,7 +546,8 @@ __global__ __launch_bounds__(NT_S, 1) void attn_fwd_small_kernel(
     const AttnGeom g, const int nsplit, const uint16_t* __restrict__ q,
     const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc,
     const uint16_t* __restrict__ kn, const uint16_t* __restrict__ vn,
-    float* __restrict__ o_part, float* __restrict__ ml_part, float* __restrict__ logits) {
+    float* __restrict__ o_part, float* __restrict__ ml_part, float* __restrict__ logits,
+    TailState* __restrict__ ts) {
     // stage b: K tile in KV[b], V tile in KV[STAGES_S + b]; reused for the final merge
     __shared__ __attribute__((aligned(16))) uint16_t KV[2 * STAGES_S][KT * D];
     // per wave: the base-2 logits of its key blocks of up to LGS_ROWS / R
@@ -548,13 +565,9 @@ __global__ __launch_bounds__(NT_S, 1) void attn_fwd_small_kernel(
     const int b = bh / g.Hkv, h = bh % g.Hkv;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform per wave
+    if (split == 0 && tid == 0) tail_state_init(ts, bh);   // for a tail that follows
     const int l32 = lane & 31, half = lane >> 5;
     const int W = g.C + g.S;
-
-    bf16x8 qf[RB][D / 16];
-    load_q<D>(qf, q, g, b, h, 0, l32, half);
-    const LdsOffsets<D> off(lane);
-    float* lg_row = (l32 < g.R) ? logits + ((size_t)bh * g.R + l32) * logit_stride(g) : nullptr;
 
     const TileRange tr = tile_range(g, 0);
     const int t_begin = (int)((long)split * tr.total / nsplit);
@@ -590,10 +603,25 @@ __global__ __launch_bounds__(NT_S, 1) void attn_fwd_small_kernel(
         issue_tile<D, true, 1, 32>(Vs[buf] + wave * 32 * D, chunk ? vn_bh : vc_bh,
                                    key0 + wave * 32, lim, 0, lane);
     };
+    // tiles t_begin .. t_begin+2 in flight
+    auto prologue = [&]() {
+        for (int i = 0; i < STAGES_S - 1 && t_begin + i < t_end; ++i) issue(t_begin + i, i);
+    };
+    // The main sweep's first copies go out before the query and diagonal-key
+    // loads below, so that their latency is not paid twice before the first
+    // tile can be used.
+    prologue();
+
+    bf16x8 qf[RB][D / 16];
+    load_q<D>(qf, q, g, b, h, 0, l32, half);
+    const LdsOffsets<D> off(lane);
+    float* lg_row = (l32 < g.R) ? logits + ((size_t)bh * g.R + l32) * logit_stride(g) : nullptr;
+
     float* const logits_bh = logits + (size_t)bh * g.R * logit_stride(g);
     // write_logits (wave-uniform): the main sweep stores the logits; the
-    // tracked sweeps do not (the logits do not depend on the reference)
-    auto sweep_tiles = [&](auto TRC, bool& overflow, bool write_logits) {
+    // tracked sweeps do not (the logits do not depend on the reference).
+    // issued: the prologue's copies are already in flight.
+    auto sweep_tiles = [&](auto TRC, bool& overflow, bool write_logits, bool issued) {
         constexpr bool TRACK = decltype(TRC)::value;
         float* const lg = write_logits ? lg_row : nullptr;
         // logits of full tiles batched in the LDS stage: nb tiles from key
@@ -612,8 +640,8 @@ __global__ __launch_bounds__(NT_S, 1) void attn_fwd_small_kernel(
             }
             nb = 0;
         };
-        // prologue: tiles t_begin .. t_begin+2 in flight, wait for the first
-        for (int i = 0; i < STAGES_S - 1 && t_begin + i < t_end; ++i) issue(t_begin + i, i);
+        if (!issued) prologue();
+        // wait for the first tile
         {
             const int later = min(STAGES_S - 2, t_end - 1 - t_begin);
             if (later >= 2)
@@ -687,7 +715,7 @@ __global__ __launch_bounds__(NT_S, 1) void attn_fwd_small_kernel(
         dot += xor32(dot);
         m_ref[0] = ok ? dot * g.c : 0.f;
         zero_state();
-        sweep_tiles(TrackC<false>{}, overflow, true);
+        sweep_tiles(TrackC<false>{}, overflow, true, true);
         overflow |= !(l_acc[0] <= kSumLimit);
         if (!__syncthreads_or(overflow)) goto merge;
     }
@@ -697,7 +725,7 @@ __global__ __launch_bounds__(NT_S, 1) void attn_fwd_small_kernel(
         bool overflow = false;
         m_ref[0] = (sweep == 0) ? -INFINITY : m_seen[0];
         zero_state();
-        sweep_tiles(TrackC<true>{}, overflow, false);
+        sweep_tiles(TrackC<true>{}, overflow, false, false);
         if (!__syncthreads_or(overflow)) break;
     }
 
@@ -746,6 +774,387 @@ merge:
             }
             *(f32x4*)(orow + db * 32 + 8 * gq + 4 * half) = acc;
         }
+}
+
+// ---------------------------------------------------------------------------
+// pass 1 for at most 16 rows (decode: the G <= 16 query heads of a group and
+// one token): the few-row kernel's structure on the 16x16x32 MFMA.
+//
+// S^T = K Q^T takes 16 keys x 16 rows per instruction, so the unused rows
+// cost a quarter of what they do on the 32x32 shape: lane l owns row l%16
+// and keys 4*(l/16) + [0, 4) of each 16-key half of the wave's 32-key block,
+// i.e. 8 logits per block to exponentiate instead of 16.  The PV product sums
+// the block's 32 keys in the order the lanes hold them: MFMA k-index
+// 8*(l/16) + e is key 4*(l/16) + e for e < 4 and 16 + 4*(l/16) + e - 4 for
+// e >= 4, so the bf16 P^T fragment of a lane is its own 8 weights (no
+// exchange between lanes) and V^T comes from two transposed LDS reads, one
+// per 4-key run.
+// ---------------------------------------------------------------------------
+constexpr int kFewRows = 16;
+
+// One 16x16x32 bf16 MFMA, fp32 accumulate.  Operand layout:
+//   A (16 x 32): lane l holds row l%16, k-values 8*(l/16) + [0, 8);
+//   B (32 x 16): lane l holds column l%16, k-values 8*(l/16) + [0, 8);
+//   C (16 x 16): lane l holds column l%16, rows 4*(l/16) + [0, 4).
+__device__ __forceinline__ f32x4 mfma16x16x32(const bf16x8 a, const bf16x8 b, const f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float xor16(float x) { return __shfl_xor(x, 16, 64); }
+
+// Per-lane LDS byte offsets of the 16-row path inside a tile, for key block 0
+// and 16-key half 0 (the block adds lkb*32 rows, the half 16 rows: constants
+// that fold into the instructions' immediate offsets, since the swizzles
+// depend only on key mod 16 and key mod 4).
+//   k[ks]: K fragment, key l%16, dims 32*ks + 8*(l/16) + [0, 8);
+//   v[db]: transposed V read of dims 16*db + [0, 16) over keys
+//          4*(l/16) + [0, 4): input lane j of a 16-lane group reads dims
+//          16*db + 4*(j%4) + [0, 4) of key 4*(l/16) + j/4, and the hardware
+//          hands output lane i dim 16*db + i of those 4 keys.
+template <int D>
+struct LdsOffsets16 {
+    uint32_t k[D / 32];
+    uint32_t v[D / 16];
+    __device__ __forceinline__ explicit LdsOffsets16(int lane) {
+        const int l16 = lane & 15, g = lane >> 4;
+#pragma unroll
+        for (int ks = 0; ks < D / 32; ++ks)
+            k[ks] = 2u * (uint32_t)tile_off<D, false>(l16, 4 * ks + g);
+        const int key = 4 * g + (l16 >> 2);
+#pragma unroll
+        for (int db = 0; db < D / 16; ++db) {
+            const int d = 16 * db + 4 * (l16 & 3);
+            v[db] = 2u * (uint32_t)(tile_off<D, true>(key, d >> 3) + (d & 7));
+        }
+    }
+};
+
+// One 32-key block of the 16-row pass 1 for one wave; the block's rows sit at
+// block lkb of the (per-wave) LDS tiles.  Same contract as fwd_block, with
+// one 16-row block per wave: MASKED handles the last partial cache tile and
+// the chunk tiles; lg_stage (full tiles) receives the block's base-2 logits
+// as [row][32 keys]; lg_row (masked tiles) receives them at logits columns
+// col0 + (key - key0) for the real keys.
+template <int D, bool MASKED, bool TRACK>
+__device__ __forceinline__ void fwd_block16(const uint16_t* Ks, const uint16_t* Vs,
+                                            const LdsOffsets16<D>& off,
+                                            const bf16x8 (&qf)[D / 32], f32x4 (&o_acc)[D / 16],
+                                            float& m_ref, float& m_seen, bool& overflow,
+                                            float& l_acc, float& lt_acc, float c, int kb,
+                                            int key0, int lim, bool chunk, int G, int lane,
+                                            float* lg_row, int col0, int lkb, float* lg_stage) {
+    const int l16 = lane & 15, g = lane >> 4;
+    const uint32_t blk = (uint32_t)lkb * 32 * D * 2;   // bytes to this block's rows
+    constexpr uint32_t HALF = 16 * D * 2;               // bytes to the second 16 keys
+    // S^T of the two 16-key halves; each sums its k-steps in two chains (even
+    // and odd k-steps), so that no MFMA waits for the one just issued
+    f32x4 s[2];
+    {
+        f32x4 acc[2][2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int p = 0; p < 2; ++p) acc[h][p] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < D / 32; ++ks)
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const bf16x8 kf = as_bf16x8(lds_read16(Ks, off.k[ks] + blk + h * HALF));
+                acc[h][ks & 1] = mfma16x16x32(kf, qf[ks], acc[h][ks & 1]);
+            }
+#pragma unroll
+        for (int h = 0; h < 2; ++h) s[h] = acc[h][0] + acc[h][1];
+    }
+    // element e of s[h] is key kb*32 + 16*h + 4*g + e of the tile, row l16
+    if (MASKED) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int key = key0 + kb * 32 + 16 * h + 4 * g + e;
+                const bool ok = key < lim && (!chunk || key * G <= l16);
+                s[h][e] = ok ? s[h][e] : -INFINITY;
+            }
+        if (lg_row) {
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int kl = kb * 32 + 16 * h + 4 * g + e;
+                    if (key0 + kl < lim) lg_row[col0 + kl] = s[h][e] * c;
+                }
+        }
+    } else if (lg_stage) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+            *(f32x4*)(lg_stage + l16 * 32 + 16 * h + 4 * g) = s[h] * c;
+    }
+    if constexpr (TRACK) {   // as in fwd_block: first-tile reference, every tile max kept
+        float mx = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
+                         fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
+        mx = fmaxf(mx, xor16(mx));
+        mx = fmaxf(mx, xor32(mx));   // the row's 4 lanes
+        const float mt = mx * c;
+        m_seen = fmaxf(m_seen, mt);
+        m_ref = (m_ref == -INFINITY) ? mt : m_ref;
+        overflow |= mt > m_ref + kHeadroom;
+    }
+    // P = 2^(s*c - m) and the row sums (l exact, lt over the bf16 weights)
+    const float m_use = (!TRACK || m_ref != -INFINITY) ? m_ref : 0.f;
+    bf16x8 pf;
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const float p = fast_exp2(fmaf(s[h][e], c, -m_use));
+            l_acc += p;
+            pf[4 * h + e] = (__bf16)p;
+        }
+#pragma unroll
+    for (int e = 0; e < 8; e += 2) {
+        const bf16x2 pair = {pf[e], pf[e + 1]};
+        lt_acc = __builtin_amdgcn_fdot2_f32_bf16(pair, kOnes2, lt_acc, false);
+    }
+    // O^T += V^T P^T over the block's 32 keys, in the lanes' key order
+#pragma unroll
+    for (int db = 0; db < D / 16; ++db) {
+        const u32x2 lo = lds_read_tr(Vs, off.v[db] + blk);
+        const u32x2 hi = lds_read_tr(Vs, off.v[db] + blk + HALF);
+        const bf16x8 vf = as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]});
+        o_acc[db] = mfma16x16x32(vf, pf, o_acc[db]);
+    }
+}
+
+// LDS stages of the 16-row kernel: 2 tiles in flight while one is read (the
+// fourth stage's LDS goes to the logits stage instead)
+constexpr int STAGES_F = 3;
+
+template <int D>
+__global__ __launch_bounds__(NT_S, 1) void attn_fwd_few_kernel(
+    const AttnGeom g, const int nsplit, const uint16_t* __restrict__ q,
+    const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc,
+    const uint16_t* __restrict__ kn, const uint16_t* __restrict__ vn,
+    float* __restrict__ o_part, float* __restrict__ ml_part, float* __restrict__ logits,
+    TailState* __restrict__ ts) {
+    // stage b: K tile in KV[b], V tile in KV[STAGES_F + b]; reused for the final merge
+    __shared__ __attribute__((aligned(16))) uint16_t KV[2 * STAGES_F][KT * D];
+    // per wave: the base-2 logits of its key blocks of up to LGS_ROWS / R
+    // consecutive full tiles, [tile][row][key], written out together (for a
+    // one-token step, R <= 4, the whole split's logits go out in one burst at
+    // its end)
+    constexpr int LGS_ROWS = 128;
+    __shared__ __attribute__((aligned(16))) float lgs[NW_S][LGS_ROWS * 32];
+    uint16_t (*Ks)[KT * D] = KV;
+    uint16_t (*Vs)[KT * D] = KV + STAGES_F;
+    constexpr int PER_TILE = 2 * KT * (D / 8) / NT_S;   // this wave's copies per tile
+
+    int qt, bh, split;
+    decode_block(1, nsplit, qt, bh, split);
+    const int BH = g.B * g.Hkv;
+    const int b = bh / g.Hkv, h = bh % g.Hkv;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform per wave
+    if (split == 0 && tid == 0) tail_state_init(ts, bh);   // for a tail that follows
+    const int l16 = lane & 15, grp = lane >> 4;
+
+    const TileRange tr = tile_range(g, 0);
+    const int t_begin = (int)((long)split * tr.total / nsplit);
+    const int t_end = (int)((long)(split + 1) * tr.total / nsplit);
+    const uint16_t* kc_bh = kc + (size_t)bh * g.C * D;
+    const uint16_t* vc_bh = vc + (size_t)bh * g.C * D;
+    const uint16_t* kn_bh = kn + (size_t)bh * g.S * D;
+    const uint16_t* vn_bh = vn + (size_t)bh * g.S * D;
+
+    // As in attn_fwd_small_kernel: each wave copies and reads only the 32 K
+    // and V rows of its own key block of a tile, so it waits for its own
+    // copies and needs no barrier per tile.
+    const TileCopy<D, false, 1, 32> kcopy(0, lane);
+    const TileCopy<D, true, 1, 32> vcopy(0, lane);
+    const int n_full_tiles = g.n / KT;
+    auto issue = [&](int t, int buf) {
+        if (t < n_full_tiles) {
+            const size_t row0 = (size_t)t * KT + wave * 32;
+            kcopy.issue(Ks[buf] + wave * 32 * D, kc_bh + row0 * D, 0);
+            vcopy.issue(Vs[buf] + wave * 32 * D, vc_bh + row0 * D, 0);
+            return;
+        }
+        const bool chunk = t >= tr.n_ct;
+        const int key0 = chunk ? (t - tr.n_ct) * KT : t * KT;
+        const int lim = chunk ? g.S : g.n;
+        issue_tile<D, false, 1, 32>(Ks[buf] + wave * 32 * D, chunk ? kn_bh : kc_bh,
+                                    key0 + wave * 32, lim, 0, lane);
+        issue_tile<D, true, 1, 32>(Vs[buf] + wave * 32 * D, chunk ? vn_bh : vc_bh,
+                                   key0 + wave * 32, lim, 0, lane);
+    };
+    auto prologue = [&]() {
+        for (int i = 0; i < STAGES_F - 1 && t_begin + i < t_end; ++i) issue(t_begin + i, i);
+    };
+    // the main sweep's first copies go out before the query loads
+    prologue();
+
+    // Q fragments (B operand of S^T = K Q^T): row l16, dims 32*ks + 8*grp + [0, 8)
+    const bool row_ok = l16 < g.R;
+    bf16x8 qf[D / 32];
+    {
+        const uint16_t* qrow =
+            q + (((size_t)b * g.Hq + (size_t)h * g.G + (l16 % g.G)) * g.S + l16 / g.G) * D +
+            8 * grp;
+#pragma unroll
+        for (int ks = 0; ks < D / 32; ++ks) {
+            u32x4 v = {0u, 0u, 0u, 0u};
+            if (row_ok) v = *(const u32x4*)(qrow + 32 * ks);
+            qf[ks] = as_bf16x8(v);
+        }
+    }
+    const LdsOffsets16<D> off(lane);
+    float* lg_row = row_ok ? logits + ((size_t)bh * g.R + l16) * logit_stride(g) : nullptr;
+    float* const logits_bh = logits + (size_t)bh * g.R * logit_stride(g);
+
+    float m_ref = 0.f, m_seen = -INFINITY, l_acc = 0.f, lt_acc = 0.f;
+    f32x4 o_acc[D / 16];
+    auto zero_state = [&]() {
+        l_acc = 0.f;
+        lt_acc = 0.f;
+#pragma unroll
+        for (int db = 0; db < D / 16; ++db) o_acc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+    };
+    // write_logits (wave-uniform): the main sweep stores the logits, the
+    // tracked sweeps do not; issued: the prologue's copies are in flight
+    auto sweep_tiles = [&](auto TRC, bool& overflow, bool write_logits, bool issued) {
+        constexpr bool TRACK = decltype(TRC)::value;
+        float* const lg = write_logits ? lg_row : nullptr;
+        const int tf = LGS_ROWS / g.R;
+        int nb = 0, b_key0 = 0;
+        auto flush = [&]() {
+            const int per = g.R * 8;   // 16-byte pieces per tile
+            for (int cix = lane; cix < nb * per; cix += 64) {
+                const int slot = cix / per, rem = cix - slot * per;
+                const int row = rem >> 3, k4 = rem & 7;
+                const f32x4 v = *(const f32x4*)&lgs[wave][(slot * g.R + row) * 32 + 4 * k4];
+                *(f32x4*)(logits_bh + (size_t)row * logit_stride(g) + b_key0 + slot * KT +
+                          wave * 32 + 4 * k4) = v;
+            }
+            nb = 0;
+        };
+        if (!issued) prologue();
+        {
+            const int later = min(STAGES_F - 2, t_end - 1 - t_begin);
+            if (later >= 2)
+                wait_vm<2 * PER_TILE>();
+            else if (later == 1)
+                wait_vm<PER_TILE>();
+            else
+                wait_tiles();
+        }
+        for (int t = t_begin; t < t_end; ++t) {
+            const int buf = (t - t_begin) % STAGES_F;
+            const bool chunk = t >= tr.n_ct;
+            const int key0 = chunk ? (t - tr.n_ct) * KT : t * KT;
+            const int lim = chunk ? g.S : g.n;
+            const int col0 = chunk ? g.C + key0 : key0;
+            // the stage of tile t+2 was last read, by this wave, for tile t-1
+            if (t + STAGES_F - 1 < t_end) issue(t + STAGES_F - 1, (buf + STAGES_F - 1) % STAGES_F);
+            if (!chunk && key0 + KT <= g.n) {
+                if (nb == 0) b_key0 = key0;
+                float* const stage =
+                    (write_logits && row_ok) ? &lgs[wave][nb * g.R * 32] : nullptr;
+                fwd_block16<D, false, TRACK>(Ks[buf], Vs[buf], off, qf, o_acc, m_ref, m_seen,
+                                             overflow, l_acc, lt_acc, g.c, wave, key0, lim,
+                                             false, 0, lane, nullptr, col0, wave, stage);
+                if (write_logits && ++nb == tf) flush();
+            } else {
+                if (nb > 0) flush();
+                fwd_block16<D, true, TRACK>(Ks[buf], Vs[buf], off, qf, o_acc, m_ref, m_seen,
+                                            overflow, l_acc, lt_acc, g.c, wave, key0, lim, chunk,
+                                            g.G, lane, lg, col0, wave, nullptr);
+            }
+            const int later = min(STAGES_F - 2, t_end - 1 - (t + 1));
+            if (later >= 2)
+                wait_vm<2 * PER_TILE>();
+            else if (later == 1)
+                wait_vm<PER_TILE>();
+            else
+                wait_tiles();
+        }
+        if (nb > 0) flush();
+    };
+    // the row sum of a lane's row: its 4 lanes (l16 + 16*grp)
+    auto row_sum = [&](float x) {
+        x += xor16(x);
+        return x + xor32(x);
+    };
+
+    // Main sweep with each row's reference at its own logit against its
+    // diagonal chunk key (no per-tile max); row sums above 2^kHeadroom send
+    // the workgroup to the tracked sweeps.
+    {
+        bool overflow = false;
+        const uint16_t* kself = kn_bh + (size_t)(row_ok ? l16 / g.G : 0) * D + 8 * grp;
+        float dot = 0.f;
+#pragma unroll
+        for (int ks = 0; ks < D / 32; ++ks) {
+            const bf16x8 kv = as_bf16x8(*(const u32x4*)(kself + 32 * ks));
+#pragma unroll
+            for (int e = 0; e < 8; ++e) dot = fmaf((float)qf[ks][e], (float)kv[e], dot);
+        }
+        dot = row_sum(dot);
+        m_ref = row_ok ? dot * g.c : 0.f;
+        zero_state();
+        sweep_tiles(TrackC<false>{}, overflow, true, true);
+        overflow |= !(row_sum(l_acc) <= kSumLimit);
+        if (!__syncthreads_or(overflow)) goto merge;
+    }
+    // tracked sweeps (rare): first-tile reference with every tile max
+    // recorded, then, if still overshot, the exact row max
+    for (int sweep = 0; sweep < 2; ++sweep) {
+        bool overflow = false;
+        m_ref = (sweep == 0) ? -INFINITY : m_seen;
+        zero_state();
+        sweep_tiles(TrackC<true>{}, overflow, false, false);
+        if (!__syncthreads_or(overflow)) break;
+    }
+
+merge:
+    // merge the waves' (m, l, lt, O) through LDS (the tiles are free now)
+    {
+        const float l = row_sum(l_acc);
+        const float lt = row_sum(lt_acc);
+        constexpr int XS = D / 4 + 4;   // [NW_S][64 lanes][XS] floats
+        static_assert(NW_S * 64 * XS * 4 <= (int)sizeof(KV), "merge area exceeds the tiles");
+        float* xch = (float*)&KV[0][0];
+        float* mine = xch + ((size_t)wave * 64 + lane) * XS;
+#pragma unroll
+        for (int db = 0; db < D / 16; ++db) *(f32x4*)(mine + 4 * db) = o_acc[db];
+        mine[D / 4 + 0] = m_ref;
+        mine[D / 4 + 1] = l;
+        mine[D / 4 + 2] = lt;
+        __syncthreads();
+        if (wave != 0) return;
+        float M = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < NW_S; ++w) M = fmaxf(M, xch[((size_t)w * 64 + lane) * XS + D / 4]);
+        float wt[NW_S], L = 0.f, Lt = 0.f;
+#pragma unroll
+        for (int w = 0; w < NW_S; ++w) {
+            const float* o = xch + ((size_t)w * 64 + lane) * XS;
+            wt[w] = (M == -INFINITY) ? 0.f : fast_exp2(o[D / 4] - M);
+            L += wt[w] * o[D / 4 + 1];
+            Lt += wt[w] * o[D / 4 + 2];
+        }
+        if (!row_ok) return;
+        const size_t prow = ((size_t)split * BH + bh) * g.rows_pad + l16;
+        if (grp == 0) *(f32x4*)(ml_part + prow * 4) = f32x4{M, L, Lt, 0.f};
+        float* orow = o_part + prow * D;
+        // lane holds dims 16*db + 4*grp + [0, 4) of its row
+#pragma unroll
+        for (int db = 0; db < D / 16; ++db) {
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int w = 0; w < NW_S; ++w)
+                acc += wt[w] * *(const f32x4*)(xch + ((size_t)w * 64 + lane) * XS + 4 * db);
+            *(f32x4*)(orow + 16 * db + 4 * grp) = acc;
+        }
+    }
 }
 
 // Summed weights of columns j0 .. j0+3 of one (b, kv head) straight from the
@@ -924,74 +1333,115 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(
 // arithmetic of its own kernel (combine, logits-to-weights, accumulation,
 // choice, scatter), so the results are those of the separate calls.
 // ---------------------------------------------------------------------------
-constexpr int TAIL_T = 1024;
+// The tail of a one-token step, in two kernels.  decode_tail_kernel splits
+// each (b, kv head) over TAIL_P workgroups of TAIL_T threads by cache
+// columns, so that it fills the chip: split merge, summed weights, score
+// update and the running minimum (a device-scope atomic on the TailState).
+// decode_scatter_kernel then makes the choice and writes the token into the
+// chosen slot; the kernel boundary orders its score write after the
+// columns' (a workgroup of the first kernel may have written that slot's
+// score from another XCD's L2).
+constexpr int TAIL_T = 256;
 constexpr int TAIL_NQ = 4;   // column quads per thread in flight
+constexpr int TAIL_P = 4;    // workgroups per (b, kv head)
 
 template <int D>
 __global__ __launch_bounds__(TAIL_T) void decode_tail_kernel(
     const AttnGeom g, const int nsplit, const float* __restrict__ o_part,
     const float* __restrict__ ml_part, const float* __restrict__ logits,
-    float* __restrict__ out, float* __restrict__ lse, float* __restrict__ wsum,
-    float* __restrict__ scores, float* __restrict__ new_scores,
-    int32_t* __restrict__ evict, uint16_t* __restrict__ kc, uint16_t* __restrict__ vc,
-    int64_t* __restrict__ pos, const uint16_t* __restrict__ kn,
-    const uint16_t* __restrict__ vn, int64_t p0) {
+    TailState* __restrict__ ts, float* __restrict__ out, float* __restrict__ lse,
+    float* __restrict__ wsum, float* __restrict__ scores, float* __restrict__ new_scores) {
     constexpr int CH = D / 4;
     __shared__ float sh_l2[32];
-    __shared__ float sh_new;
+    __shared__ float sh_pc[32];   // part 0: weight of the token's own column, per row
     __shared__ unsigned long long sh_min;
-    const int bh = blockIdx.x, tid = threadIdx.x;
+    const int bh = blockIdx.x / TAIL_P, part = blockIdx.x % TAIL_P;
+    const int tid = threadIdx.x;
     const int W = g.C + 1;
-    // split merge: thread (r, dc) for the R <= 32 rows
-    if (tid < g.R * CH) {
-        const int r = tid / CH, dc = tid % CH;
-        float M, L, Lt;
-        f32x4 acc;
-        merge_splits<D>(g, nsplit, o_part, ml_part, bh, r, dc, M, L, Lt, acc);
-        const float inv = 1.0f / Lt;
-        const int b = bh / g.Hkv, h = bh % g.Hkv;
-        const int a = h * g.G + r;          // S = 1: row r is head h*G + r
-        const size_t orow = (size_t)b * g.Hq + a;
-        *(f32x4*)(out + orow * D + dc * 4) = acc * inv;
-        if (dc == 0) {
-            const float L2 = M + fast_log2(L);
-            sh_l2[r] = L2;
-            if (lse) lse[orow] = L2 * kLn2;
-        }
-    }
-    if (tid == 0) sh_min = ~0ull;
-    __syncthreads();
-    // summed weights, accumulated scores and the running minimum.  A thread
-    // takes TAIL_NQ column quads TAIL_T quads apart and issues all their
-    // loads (scores, then four logit rows at a time) before it uses any; per
-    // column the rows are summed in row order as in logit_quad_sums.
     const float* lg = logits + (size_t)bh * g.R * logit_stride(g);
     const int WL = logit_stride(g);
     float* sc = scores + (size_t)bh * g.C;
     float* wrow = wsum + (size_t)bh * W;
-    unsigned long long best = ~0ull;
-    for (int base = 4 * tid; base < W; base += 4 * TAIL_T * TAIL_NQ) {
-        float s[TAIL_NQ][4], old[TAIL_NQ][4];
-        int j0[TAIL_NQ];
-#pragma unroll
-        for (int k = 0; k < TAIL_NQ; ++k) {
-            j0[k] = base + 4 * TAIL_T * k;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                s[k][e] = 0.f;
-                const int j = j0[k] + e;
-                old[k][e] = j < g.n ? sc[j] : 0.f;
+    // this part's column quads [q_lo, q_hi); a thread takes quads TAIL_T apart
+    const int nq = (g.C + 3) / 4;
+    const int qp = (nq + TAIL_P - 1) / TAIL_P;
+    const int q_lo = part * qp, q_hi = min(nq, q_lo + qp);
+    constexpr int QSTEP = TAIL_T * TAIL_NQ;
+
+    // The logits do not depend on the rows' final log-sum-exp: the first pass
+    // of this thread's column quads (rows 0..3) is loaded before the merge,
+    // so that both share one memory round trip.
+    f32x4 x[TAIL_NQ][4];
+    float old[TAIL_NQ][4];
+#define H2O_TAIL_LOAD_ROWS(q0, r0)                                              \
+    _Pragma("unroll") for (int u = 0; u < 4; ++u) {                             \
+        const int r = min((r0) + u, g.R - 1);                                   \
+        _Pragma("unroll") for (int k = 0; k < TAIL_NQ; ++k) {                   \
+            const int q = (q0) + TAIL_T * k;                                    \
+            x[k][u] = q < q_hi ? *(const f32x4*)(lg + (size_t)r * WL + 4 * q)   \
+                               : f32x4{0.f, 0.f, 0.f, 0.f};                     \
+        }                                                                       \
+    }
+    H2O_TAIL_LOAD_ROWS(q_lo + tid, 0)
+
+    // the rows' base-2 log-sum-exp from the key splits (thread r < R); part 0
+    // instead merges all of O (threads (r, dc)) and takes the weight of the
+    // token's own column (column C, summed over the rows in order)
+    if (part == 0) {
+        for (int idx = tid; idx < g.R * CH; idx += TAIL_T) {
+            const int r = idx / CH, dc = idx % CH;
+            const float xc = dc == 0 ? lg[(size_t)r * WL + g.C] : 0.f;
+            float M, L, Lt;
+            f32x4 acc;
+            merge_splits<D>(g, nsplit, o_part, ml_part, bh, r, dc, M, L, Lt, acc);
+            const float inv = 1.0f / Lt;
+            const int b = bh / g.Hkv, h = bh % g.Hkv;
+            const size_t orow = (size_t)b * g.Hq + h * g.G + r;   // S = 1: row r is head h*G + r
+            *(f32x4*)(out + orow * D + dc * 4) = acc * inv;
+            if (dc == 0) {
+                const float L2 = M + fast_log2(L);
+                sh_l2[r] = L2;
+                sh_pc[r] = fast_exp2(xc - L2);
+                if (lse) lse[orow] = L2 * kLn2;
             }
         }
+    } else if (tid < g.R) {
+        float M, L, Lt;
+        f32x4 acc;
+        merge_splits<D>(g, nsplit, o_part, ml_part, bh, tid, 0, M, L, Lt, acc);
+        sh_l2[tid] = M + fast_log2(L);
+    }
+    if (tid == 0) sh_min = ~0ull;
+    __syncthreads();
+    if (part == 0 && tid == 0) {
+        float s_new = 0.f;   // rows in order
+        for (int r = 0; r < g.R; ++r) s_new += sh_pc[r];
+        wrow[g.C] = s_new;
+        new_scores[bh] = s_new;
+    }
+    // summed weights of the cache columns, accumulated scores and the running
+    // minimum; per column the rows are summed in row order as in
+    // logit_quad_sums
+    unsigned long long best = ~0ull;
+    for (int q0 = q_lo + tid; q0 < q_hi; q0 += QSTEP) {
+#pragma unroll
+        for (int k = 0; k < TAIL_NQ; ++k)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int j = 4 * (q0 + TAIL_T * k) + e;
+                old[k][e] = j < g.n ? sc[j] : 0.f;
+            }
+        if (q0 != q_lo + tid) {
+            H2O_TAIL_LOAD_ROWS(q0, 0)
+        }
+        float s[TAIL_NQ][4];
+#pragma unroll
+        for (int k = 0; k < TAIL_NQ; ++k)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) s[k][e] = 0.f;
         for (int r0 = 0; r0 < g.R; r0 += 4) {
-            f32x4 x[TAIL_NQ][4];
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const int r = min(r0 + u, g.R - 1);
-#pragma unroll
-                for (int k = 0; k < TAIL_NQ; ++k)
-                    x[k][u] = j0[k] < W ? *(const f32x4*)(lg + (size_t)r * WL + j0[k])
-                                        : f32x4{0.f, 0.f, 0.f, 0.f};
+            if (r0 > 0) {
+                H2O_TAIL_LOAD_ROWS(q0, r0)
             }
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
@@ -1001,17 +1451,18 @@ __global__ __launch_bounds__(TAIL_T) void decode_tail_kernel(
                 for (int k = 0; k < TAIL_NQ; ++k)
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
-                        const int j = j0[k] + e;
-                        if (j < g.n || j == g.C) s[k][e] += fast_exp2(x[k][u][e] - lr);
+                        const int j = 4 * (q0 + TAIL_T * k) + e;
+                        if (j < g.n) s[k][e] += fast_exp2(x[k][u][e] - lr);
                     }
             }
         }
 #pragma unroll
-        for (int k = 0; k < TAIL_NQ; ++k)
+        for (int k = 0; k < TAIL_NQ; ++k) {
+            if (q0 + TAIL_T * k >= q_hi) continue;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const int j = j0[k] + e;
-                if (j >= W) continue;
+                const int j = 4 * (q0 + TAIL_T * k) + e;
+                if (j >= g.C) continue;
                 wrow[j] = s[k][e];
                 if (j < g.n) {
                     const float acc = old[k][e] + s[k][e];
@@ -1019,11 +1470,11 @@ __global__ __launch_bounds__(TAIL_T) void decode_tail_kernel(
                     const unsigned long long kj =
                         ((unsigned long long)score_key(acc) << 32) | (unsigned)j;
                     best = kj < best ? kj : best;
-                } else if (j == g.C) {
-                    sh_new = s[k][e];
                 }
             }
+        }
     }
+#undef H2O_TAIL_LOAD_ROWS
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) {
         const unsigned long long o = __shfl_xor(best, off, 64);
@@ -1031,21 +1482,30 @@ __global__ __launch_bounds__(TAIL_T) void decode_tail_kernel(
     }
     if ((tid & 63) == 0) atomicMin(&sh_min, best);
     __syncthreads();
-    // the choice: the first empty slot while the cache fills, else the
-    // lexicographic minimum; then the scatter of the token into it
-    const int slot = g.n < g.C ? g.n : (int)(sh_min & 0xFFFFFFFFull);
+    if (tid == 0) atomicMin(&ts[bh].min_key, sh_min);
+}
+
+// The choice and the scatter of a one-token step, one workgroup per (b, kv
+// head): the first empty slot while the cache fills, else the lexicographic
+// minimum the tail kernel left in the TailState; the token's K/V row, score
+// and position go into that slot.
+template <int D>
+__global__ __launch_bounds__(64) void decode_scatter_kernel(
+    const AttnGeom g, const TailState* __restrict__ ts, float* __restrict__ scores,
+    const float* __restrict__ new_scores, int32_t* __restrict__ evict,
+    uint16_t* __restrict__ kc, uint16_t* __restrict__ vc, int64_t* __restrict__ pos,
+    const uint16_t* __restrict__ kn, const uint16_t* __restrict__ vn, int64_t p0) {
     constexpr int TPR = D / 8;   // threads per row (16 bytes each)
+    const int bh = blockIdx.x, tid = threadIdx.x;
+    const int slot = g.n < g.C ? g.n : (int)(ts[bh].min_key & 0xFFFFFFFFull);
     if (tid < 2 * TPR) {
-        const int which = tid / TPR, c = tid % TPR;
-        const uint16_t* src = (which ? vn : kn) + (size_t)bh * D + c * 8;
-        uint16_t* dst = (which ? vc : kc) + ((size_t)bh * g.C + slot) * D + c * 8;
-        *(u32x4*)dst = *(const u32x4*)src;
-        if (tid == 0) {
-            evict[bh] = slot;
-            new_scores[bh] = sh_new;
-            sc[slot] = sh_new;
-            if (pos) pos[(size_t)bh * g.C + slot] = p0;
-        }
+        const u32x4 v = *(const u32x4*)((tid < TPR ? kn : vn) + (size_t)bh * D + (tid % TPR) * 8);
+        *(u32x4*)((tid < TPR ? kc : vc) + ((size_t)bh * g.C + slot) * D + (tid % TPR) * 8) = v;
+    }
+    if (tid == 0) {
+        evict[bh] = slot;
+        scores[(size_t)bh * g.C + slot] = new_scores[bh];
+        if (pos) pos[(size_t)bh * g.C + slot] = p0;
     }
 }
 
@@ -1914,9 +2374,14 @@ hipError_t launch_attention_d(const AttnPlan& pl, const uint16_t* q,
             hipLaunchKernelGGL(attn_fwd_q8_kernel<D>, dim3(g.n_qt * BH * pl.split1), dim3(NT),
                                0, stream, g, pl.split1, q, qc, kn, vn, o_part, ml_part);
     } else {
-        if (pl.small)
+        if (pl.small && g.R <= kFewRows)
+            hipLaunchKernelGGL(attn_fwd_few_kernel<D>, dim3(BH * pl.split1), dim3(NT_S), 0,
+                               stream, g, pl.split1, q, kc, vc, kn, vn, o_part, ml_part, wpart,
+                               nullptr);
+        else if (pl.small)
             hipLaunchKernelGGL(attn_fwd_small_kernel<D>, dim3(BH * pl.split1), dim3(NT_S), 0,
-                               stream, g, pl.split1, q, kc, vc, kn, vn, o_part, ml_part, wpart);
+                               stream, g, pl.split1, q, kc, vc, kn, vn, o_part, ml_part, wpart,
+                               nullptr);
         else
             hipLaunchKernelGGL(attn_fwd_kernel<D>, dim3(g.n_qt * BH * pl.split1), dim3(NT), 0,
                                stream, g, pl.split1, q, kc, vc, kn, vn, o_part, ml_part);
@@ -1987,6 +2452,8 @@ bool make_attn_plan(int B, int Hq, int Hkv, int D, int C, int S, int n, float sc
     pl->off_wp = off;   // row-tile partial sums, or the logits of the few-row path
     off = align(off + (size_t)(pl->small ? g.R * logit_stride(g) : g.n_qt * (C + S)) * BH *
                           sizeof(float));
+    pl->off_tail = off;
+    off = align(off + (size_t)BH * 16);
     pl->bytes = off;
     return true;
 }
@@ -2025,13 +2492,22 @@ hipError_t launch_decode_step_d(const AttnPlan& pl, const uint16_t* q, uint16_t*
     };
     auto event = [&](int i) { return ev ? hipEventRecord(ev[i], stream) : hipSuccess; };
     if ((err = event(0)) != hipSuccess) return err;
-    hipLaunchKernelGGL(attn_fwd_small_kernel<D>, dim3(BH * pl.split1), dim3(NT_S), 0, stream, g,
-                       pl.split1, q, kc, vc, kn, vn, o_part, ml_part, logits);
+    TailState* tstate = (TailState*)(w + pl.off_tail);
+    if (g.R <= kFewRows)
+        hipLaunchKernelGGL(attn_fwd_few_kernel<D>, dim3(BH * pl.split1), dim3(NT_S), 0, stream,
+                           g, pl.split1, q, kc, vc, kn, vn, o_part, ml_part, logits, tstate);
+    else
+        hipLaunchKernelGGL(attn_fwd_small_kernel<D>, dim3(BH * pl.split1), dim3(NT_S), 0,
+                           stream, g, pl.split1, q, kc, vc, kn, vn, o_part, ml_part, logits,
+                           tstate);
     if (check() != hipSuccess) return err;
     if ((err = event(1)) != hipSuccess) return err;
-    hipLaunchKernelGGL(decode_tail_kernel<D>, dim3(BH), dim3(TAIL_T), 0, stream, g, pl.split1,
-                       o_part, ml_part, logits, out, lse, wsum, scores, new_scores, evict, kc,
-                       vc, pos, kn, vn, p0);
+    hipLaunchKernelGGL(decode_tail_kernel<D>, dim3(BH * TAIL_P), dim3(TAIL_T), 0, stream, g,
+                       pl.split1, o_part, ml_part, logits, tstate, out, lse, wsum, scores,
+                       new_scores);
+    if (check() != hipSuccess) return err;
+    hipLaunchKernelGGL(decode_scatter_kernel<D>, dim3(BH), dim3(64), 0, stream, g, tstate,
+                       scores, new_scores, evict, kc, vc, pos, kn, vn, p0);
     if (check() != hipSuccess) return err;
     for (int i = 2; i < 5; ++i)
         if ((err = event(i)) != hipSuccess) return err;

@@ -28,7 +28,9 @@ struct AttnPlan {
     bool small;     // G * S <= 32: one row block, logits stored for the weights
     int split1;     // key splits of pass 1 (log-sum-exp and output)
     int split2;     // key splits of pass 2 (summed weights)
-    size_t off_o, off_ml, off_l2, off_wp, bytes;
+    // off_tail: per (b, kv head) state of the one-token step's tail (running
+    // minimum and finished-part count; 16 bytes each)
+    size_t off_o, off_ml, off_l2, off_wp, off_tail, bytes;
 };
 
 bool make_attn_plan(int B, int Hq, int Hkv, int D, int C, int S, int n,

@@ -139,6 +139,9 @@ EDGE = [
     # few query rows per KV head (G * S <= 32): the logits path
     ("few_rows_causal", 2, 12, 3, 128, 300, 8, 40, 1.0, 0.05),
     ("few_rows_ragged", 1, 6, 2, 64, 97, 5, 25, 1.0, 0.05),
+    # the 16-row kernel at its limit (R = 16) and the 32-row one just above it
+    ("rows_16_decode", 2, 16, 1, 128, 230, 1, 40, 1.0, 0.05),
+    ("rows_17_g1", 1, 1, 1, 64, 150, 17, 12, 1.0, 0.05),
 ]
 
 
