@@ -585,8 +585,8 @@ __global__ __launch_bounds__(NT_S, 1) void attn_fwd_small_kernel(
     // its own copies (loads complete in issue order) and needs no barrier
     // per tile.  A stage is rewritten by the wave that read it, after its
     // reads of it have returned.
-    const TileCopy<D, false, 1, 32> kcopy(0, lane);
-    const TileCopy<D, true, 1, 32> vcopy(0, lane);
+    const TileCopy<D, false, 1, 32, true> kcopy(0, lane);   // rows read once
+    const TileCopy<D, true, 1, 32, true> vcopy(0, lane);
     const int n_full_tiles = g.n / KT;
     auto issue = [&](int t, int buf) {
         if (t < n_full_tiles) {   // every row exists: scalar base, fixed lane offsets
@@ -968,8 +968,8 @@ __global__ __launch_bounds__(NT_S, 1) void attn_fwd_few_kernel(
     // As in attn_fwd_small_kernel: each wave copies and reads only the 32 K
     // and V rows of its own key block of a tile, so it waits for its own
     // copies and needs no barrier per tile.
-    const TileCopy<D, false, 1, 32> kcopy(0, lane);
-    const TileCopy<D, true, 1, 32> vcopy(0, lane);
+    const TileCopy<D, false, 1, 32, true> kcopy(0, lane);   // rows read once
+    const TileCopy<D, true, 1, 32, true> vcopy(0, lane);
     const int n_full_tiles = g.n / KT;
     auto issue = [&](int t, int buf) {
         if (t < n_full_tiles) {

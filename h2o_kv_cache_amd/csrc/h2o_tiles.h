@@ -109,6 +109,17 @@ __device__ __forceinline__ void dma16_s(const void* sbase, uint32_t voff, uint32
                  : "memory", "m0");
 }
 
+// dma16_s with the non-temporal hint, for rows that are read exactly once
+// (the few-row passes stream every K/V row once): the stream then does not
+// displace cached lines that are reused -- in the one-token step, the
+// logits the tail reads back.  Same contract as dma16.
+__device__ __forceinline__ void dma16_s_nt(const void* sbase, uint32_t voff, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2 nt"
+                 :
+                 : "s"(lds), "v"(voff), "s"(sbase)
+                 : "memory", "m0");
+}
+
 __device__ __forceinline__ const uint16_t* uniform_ptr(const uint16_t* p) {
     const uint64_t v = (uint64_t)(uintptr_t)p;
     const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
@@ -118,8 +129,9 @@ __device__ __forceinline__ const uint16_t* uniform_ptr(const uint16_t* p) {
 
 // The copy of issue_tile for a tile whose ROWS rows all exist: the lanes'
 // byte offsets inside a tile are fixed, so they are formed once, and each
-// tile only moves the scalar base (row key0 of the source).
-template <int D, bool VT, int NW = kWaves, int ROWS = kKeyTile>
+// tile only moves the scalar base (row key0 of the source).  NT: the copies
+// carry the non-temporal hint (rows read once).
+template <int D, bool VT, int NW = kWaves, int ROWS = kKeyTile, bool NT = false>
 struct TileCopy {
     static constexpr int CPR = D / 8;
     static constexpr int ITER = ROWS * CPR / (NW * 64);
@@ -139,7 +151,12 @@ struct TileCopy {
         const uint32_t base = __builtin_amdgcn_readfirstlane(lds_addr(tile));
         const uint16_t* sb = uniform_ptr(rows);
 #pragma unroll
-        for (int it = 0; it < ITER; ++it) dma16_s(sb, voff[it], base + (it * NW + wave) * 1024);
+        for (int it = 0; it < ITER; ++it) {
+            if constexpr (NT)
+                dma16_s_nt(sb, voff[it], base + (it * NW + wave) * 1024);
+            else
+                dma16_s(sb, voff[it], base + (it * NW + wave) * 1024);
+        }
     }
 };
 
