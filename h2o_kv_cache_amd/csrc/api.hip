@@ -222,17 +222,25 @@ h2o_status_t h2o_step(const h2o_shape_t* s, const uint16_t* q, uint16_t* k_cache
                                                 wsum, scores, new_scores, evict_idx, pos, p0,
                                                 ws, str, sync_debug(), timing_slot()));
     const int BH = s->batch * s->n_kv_heads;
+    // the kernel that writes the summed weights also accumulates the scores;
+    // the choice and the scatter share one kernel where the keys fit in
+    // registers
     hipError_t e = h2o::launch_attention(pl, q, k_cache, v_cache, k_new, v_new, out, lse, wsum,
-                                         ws, str, sync_debug(), timing_slot());
-    if (e == hipSuccess)
-        e = h2o::launch_score_accumulate(BH, s->cache_len, s->chunk_len, s->n_valid, scores,
-                                         new_scores, wsum, str);
-    if (e == hipSuccess)
-        e = h2o::launch_evict_select(BH, s->cache_len, s->chunk_len, s->n_valid, scores,
-                                     evict_idx, str);
-    if (e == hipSuccess)
-        e = h2o::launch_kv_scatter(BH, s->head_dim, s->cache_len, s->chunk_len, k_cache, v_cache,
-                                   scores, pos, k_new, v_new, new_scores, evict_idx, p0, str);
+                                         ws, str, sync_debug(), timing_slot(), scores,
+                                         new_scores);
+    if (e == hipSuccess && h2o::select_scatter_fuses(s->cache_len)) {
+        e = h2o::launch_select_scatter(BH, s->head_dim, s->cache_len, s->chunk_len, s->n_valid,
+                                       scores, evict_idx, k_cache, v_cache, pos, k_new, v_new,
+                                       new_scores, p0, str);
+    } else {
+        if (e == hipSuccess)
+            e = h2o::launch_evict_select(BH, s->cache_len, s->chunk_len, s->n_valid, scores,
+                                         evict_idx, str);
+        if (e == hipSuccess)
+            e = h2o::launch_kv_scatter(BH, s->head_dim, s->cache_len, s->chunk_len, k_cache,
+                                       v_cache, scores, pos, k_new, v_new, new_scores, evict_idx,
+                                       p0, str);
+    }
     if (e == hipSuccess && sync_debug()) e = hipStreamSynchronize(str);
     return from_hip(e);
 }

@@ -1197,9 +1197,11 @@ __device__ __forceinline__ void logit_quad_sums(const AttnGeom& g, const float* 
 
 // Summed weights straight from the stored logits (few-row path): a thread
 // takes four consecutive columns.
+// With non-null `scores` the kernel also accumulates: scores[j] += wsum[j]
+// (j < n), new_scores[t] = wsum[C + t].
 __global__ __launch_bounds__(256) void wsum_from_logits_kernel(
     const AttnGeom g, const float* __restrict__ logits, const float* __restrict__ l2,
-    float* __restrict__ wsum) {
+    float* __restrict__ wsum, float* __restrict__ scores, float* __restrict__ new_scores) {
     const int W = g.C + g.S;
     const int nq = (W + 3) / 4;   // column quads per (b, kv head)
     const long idx = (long)blockIdx.x * blockDim.x + threadIdx.x;
@@ -1210,8 +1212,17 @@ __global__ __launch_bounds__(256) void wsum_from_logits_kernel(
     logit_quad_sums(g, logits + (size_t)bh * g.R * logit_stride(g) + j0,
                     l2 + (size_t)bh * g.rows_pad, j0, s);
 #pragma unroll
-    for (int e = 0; e < 4; ++e)
-        if (j0 + e < W) wsum[(size_t)bh * W + j0 + e] = s[e];
+    for (int e = 0; e < 4; ++e) {
+        const int j = j0 + e;
+        if (j >= W) continue;
+        wsum[(size_t)bh * W + j] = s[e];
+        if (scores) {
+            if (j < g.n)
+                scores[(size_t)bh * g.C + j] += s[e];
+            else if (j >= g.C)
+                new_scores[(size_t)bh * g.S + (j - g.C)] = s[e];
+        }
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -2298,8 +2309,10 @@ merge:
 // ---------------------------------------------------------------------------
 // sum the row-tile partials in tile order
 // ---------------------------------------------------------------------------
+// With non-null `scores` the kernel also accumulates, as wsum_from_logits_kernel.
 __global__ __launch_bounds__(256) void wsum_reduce_kernel(
-    const AttnGeom g, const float* __restrict__ wpart, float* __restrict__ wsum) {
+    const AttnGeom g, const float* __restrict__ wpart, float* __restrict__ wsum,
+    float* __restrict__ scores, float* __restrict__ new_scores) {
     const int BH = g.B * g.Hkv;
     const int W = g.C + g.S;
     const long idx = (long)blockIdx.x * blockDim.x + threadIdx.x;
@@ -2325,6 +2338,12 @@ __global__ __launch_bounds__(256) void wsum_reduce_kernel(
         }
     }
     wsum[idx] = s;
+    if (scores) {
+        if (j < g.n)
+            scores[(size_t)bh * g.C + j] += s;
+        else if (j >= g.C)
+            new_scores[(size_t)bh * g.S + (j - g.C)] = s;
+    }
 }
 
 int pick_split(int base_blocks, int max_tiles, int target) {
@@ -2342,7 +2361,8 @@ hipError_t launch_attention_d(const AttnPlan& pl, const uint16_t* q,
                               const uint16_t* kc, const uint16_t* vc, const Q8Cache& qc,
                               const uint16_t* kn, const uint16_t* vn, float* out,
                               float* lse, float* wsum, void* ws,
-                              hipStream_t stream, bool sync_debug, hipEvent_t* ev) {
+                              hipStream_t stream, bool sync_debug, hipEvent_t* ev,
+                              float* scores = nullptr, float* new_scores = nullptr) {
     const AttnGeom& g = pl.g;
     char* w = (char*)ws;
     float* o_part = (float*)(w + pl.off_o);
@@ -2400,7 +2420,7 @@ hipError_t launch_attention_d(const AttnPlan& pl, const uint16_t* q,
     if (pl.small) {
         const long qtotal = (long)BH * ((g.C + g.S + 3) / 4);
         hipLaunchKernelGGL(wsum_from_logits_kernel, dim3((unsigned)((qtotal + 255) / 256)),
-                           dim3(256), 0, stream, g, wpart, l2, wsum);
+                           dim3(256), 0, stream, g, wpart, l2, wsum, scores, new_scores);
         H2O_CHECK();
         H2O_EVENT(3);
     } else {
@@ -2413,7 +2433,7 @@ hipError_t launch_attention_d(const AttnPlan& pl, const uint16_t* q,
         H2O_CHECK();
         H2O_EVENT(3);
         hipLaunchKernelGGL(wsum_reduce_kernel, dim3((unsigned)((wtotal + 255) / 256)),
-                           dim3(256), 0, stream, g, wpart, wsum);
+                           dim3(256), 0, stream, g, wpart, wsum, scores, new_scores);
         H2O_CHECK();
     }
     H2O_EVENT(4);
@@ -2461,17 +2481,19 @@ bool make_attn_plan(int B, int Hq, int Hkv, int D, int C, int S, int n, float sc
 hipError_t launch_attention(const AttnPlan& plan, const uint16_t* q, const uint16_t* kc,
                             const uint16_t* vc, const uint16_t* kn, const uint16_t* vn,
                             float* out, float* lse, float* wsum, void* ws,
-                            hipStream_t stream, bool sync_debug, hipEvent_t* ev5) {
+                            hipStream_t stream, bool sync_debug, hipEvent_t* ev5,
+                            float* scores, float* new_scores) {
     const Q8Cache none{nullptr, nullptr, nullptr, nullptr};
     if (plan.g.D == 64)
         return launch_attention_d<64, false>(plan, q, kc, vc, none, kn, vn, out, lse, wsum, ws,
-                                             stream, sync_debug, ev5);
+                                             stream, sync_debug, ev5, scores, new_scores);
     return launch_attention_d<128, false>(plan, q, kc, vc, none, kn, vn, out, lse, wsum, ws,
-                                          stream, sync_debug, ev5);
+                                          stream, sync_debug, ev5, scores, new_scores);
 }
 
 // One-token step on the few-row path: the streaming pass, then the tail
-// kernel (split merge, summed weights, accumulation, choice, scatter).
+// kernels (split merge, summed weights, accumulation and the running
+// minimum; then the choice and the scatter).
 template <int D>
 hipError_t launch_decode_step_d(const AttnPlan& pl, const uint16_t* q, uint16_t* kc,
                                 uint16_t* vc, const uint16_t* kn, const uint16_t* vn,

@@ -28,26 +28,30 @@ struct AttnPlan {
     bool small;     // G * S <= 32: one row block, logits stored for the weights
     int split1;     // key splits of pass 1 (log-sum-exp and output)
     int split2;     // key splits of pass 2 (summed weights)
-    // off_tail: per (b, kv head) state of the one-token step's tail (running
-    // minimum and finished-part count; 16 bytes each)
+    // off_tail: per (b, kv head) state of the one-token step's tail (the
+    // running minimum; 16 bytes each)
     size_t off_o, off_ml, off_l2, off_wp, off_tail, bytes;
 };
 
 bool make_attn_plan(int B, int Hq, int Hkv, int D, int C, int S, int n,
                     float scale, AttnPlan* plan);
 
+// With non-null `scores` the kernel that writes the summed weights also does
+// the score accumulation (scores[j] += wsum[j] for j < n, new_scores[t] =
+// wsum[C + t]), with the results of launch_score_accumulate.
 hipError_t launch_attention(const AttnPlan& plan, const uint16_t* q,
                             const uint16_t* kc, const uint16_t* vc,
                             const uint16_t* kn, const uint16_t* vn, float* out,
                             float* lse, float* wsum, void* ws,
                             hipStream_t stream, bool sync_debug,
-                            hipEvent_t* ev5 /* nullable: 5 timing events */);
+                            hipEvent_t* ev5 /* nullable: 5 timing events */,
+                            float* scores = nullptr, float* new_scores = nullptr);
 
 // A whole one-token step on the few-row path (decode_tail_applies): the
-// streaming attention pass, then one kernel for the split merge, the summed
-// weights, the score accumulation, the choice and the scatter.  Same results
-// as launch_attention + launch_score_accumulate + launch_evict_select +
-// launch_kv_scatter.
+// streaming attention pass, one kernel for the split merge, the summed
+// weights, the score accumulation and the running minimum, and one for the
+// choice and the scatter.  Same results as launch_attention +
+// launch_score_accumulate + launch_evict_select + launch_kv_scatter.
 bool decode_tail_applies(const AttnPlan& plan);
 hipError_t launch_decode_step(const AttnPlan& plan, const uint16_t* q, uint16_t* kc,
                               uint16_t* vc, const uint16_t* kn, const uint16_t* vn, float* out,
@@ -88,6 +92,14 @@ hipError_t launch_score_accumulate(int BH, int C, int S, int n, float* scores,
 hipError_t launch_evict_select(int BH, int C, int S, int n,
                                const float* scores, int32_t* evict_idx,
                                hipStream_t stream);
+
+// launch_evict_select followed by launch_kv_scatter in one kernel (same
+// results), for rows whose keys fit in registers (select_scatter_fuses(C)).
+bool select_scatter_fuses(int C);
+hipError_t launch_select_scatter(int BH, int D, int C, int S, int n, float* scores,
+                                 int32_t* evict_idx, uint16_t* kc, uint16_t* vc, int64_t* pos,
+                                 const uint16_t* kn, const uint16_t* vn,
+                                 const float* new_scores, int64_t p0, hipStream_t stream);
 
 hipError_t launch_kv_scatter(int BH, int D, int C, int S, uint16_t* kc,
                              uint16_t* vc, float* scores, int64_t* pos,

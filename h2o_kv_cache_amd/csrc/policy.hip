@@ -34,6 +34,7 @@ __global__ __launch_bounds__(256) void score_accumulate_kernel(
 // slot choice
 // ---------------------------------------------------------------------------
 constexpr int SEL_T = 1024;   // threads per (b, kv head)
+constexpr int SEL_SLOTS = 4096;   // choices kept in LDS for the fused scatter
 
 __device__ __forceinline__ uint32_t slot_key(const float* __restrict__ sc, int j, int n) {
     return (j < n) ? score_key(sc[j]) : 0u;
@@ -60,33 +61,6 @@ __device__ __forceinline__ void load_keys(uint32_t (&key)[SU], const float* __re
         const int j = base + 64 * u + lane;
         key[u] = (j < n && j <= last) ? score_key(x[u]) : 0u;
     }
-}
-
-// Exclusive prefix sum over the block (1024 threads, 16 waves).
-__device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t x, uint32_t* sh_wave) {
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    uint32_t inc = x;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const uint32_t y = __shfl_up(inc, off, 64);
-        if (lane >= off) inc += y;
-    }
-    if (lane == 63) sh_wave[wave] = inc;
-    __syncthreads();
-    if (wave == 0) {
-        uint32_t t = (lane < SEL_T / 64) ? sh_wave[lane] : 0u;
-        uint32_t ti = t;
-#pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-            const uint32_t y = __shfl_up(ti, off, 64);
-            if (lane >= off) ti += y;
-        }
-        if (lane < SEL_T / 64) sh_wave[lane] = ti - t;   // exclusive wave offsets
-    }
-    __syncthreads();
-    const uint32_t res = sh_wave[wave] + inc - x;
-    __syncthreads();
-    return res;
 }
 
 // Add 1 to hist[bin] for every active lane.  Lanes of the wave whose bin
@@ -134,25 +108,145 @@ __device__ __forceinline__ void find_bin(const uint32_t* hist, uint32_t k, uint3
     }
 }
 
+// Every wave computes the same result as find_bin from the shared histogram
+// (no broadcast through LDS, hence no barrier after it): the digit of the bin
+// that holds rank k and the rank inside that bin.  k must not exceed the
+// histogram's total.
+__device__ __forceinline__ void find_bin_wave(const uint32_t* hist, uint32_t k,
+                                              uint32_t& digit, uint32_t& k_in) {
+    const int lane = threadIdx.x & 63;
+    uint32_t h4[4], s4 = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        h4[e] = hist[lane * 4 + e];
+        s4 += h4[e];
+    }
+    uint32_t inc = s4;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const uint32_t y = __shfl_up(inc, off, 64);
+        if (lane >= off) inc += y;
+    }
+    uint32_t before = inc - s4, d = 0, kk = 0;
+    const bool here = before < k && k <= inc;
+    if (here) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            if (before < k && k <= before + h4[e]) {
+                d = (uint32_t)(lane * 4 + e);
+                kk = k - before;
+            }
+            before += h4[e];
+        }
+    }
+    const unsigned long long m = __ballot(here);
+    const int src = m ? __builtin_ctzll(m) : 0;
+    digit = __builtin_amdgcn_readlane(d, src);
+    k_in = __builtin_amdgcn_readlane(kk, src);
+}
+
+// Exclusive prefix sums of two counts over the block (1024 threads).
+__device__ __forceinline__ void block_exclusive_scan2(uint32_t x, uint32_t y, uint32_t* sh,
+                                                      uint32_t& xb, uint32_t& yb) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    uint32_t ix = x, iy = y;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const uint32_t a = __shfl_up(ix, off, 64), c = __shfl_up(iy, off, 64);
+        if (lane >= off) {
+            ix += a;
+            iy += c;
+        }
+    }
+    if (lane == 63) {
+        sh[wave] = ix;
+        sh[SEL_T / 64 + wave] = iy;
+    }
+    __syncthreads();
+    uint32_t ox = 0, oy = 0;
+    for (int w = 0; w < wave; ++w) {   // wave-uniform loop over the earlier waves' totals
+        ox += sh[w];
+        oy += sh[SEL_T / 64 + w];
+    }
+    xb = ox + ix - x;
+    yb = oy + iy - y;
+}
+
 // One workgroup per (b, kv head).  Each thread holds the keys of a
 // contiguous run of KPT slots in registers.  Radix select (4 passes of 8
 // bits) finds the key T of the S-th smallest (key, slot) pair and how many
 // slots with key T are taken; a slot-ordered compaction (block prefix sums
 // over the threads' runs) then writes the chosen slots in increasing order.
-template <int KPT>
+// The histograms rotate over three LDS buffers, so that a pass needs one
+// barrier: pass p fills buffer p % 3 and clears buffer (p + 1) % 3, which
+// the waves last read in pass p - 2 (before pass p - 1's barrier).  Passes
+// over leading bytes that every key shares are skipped.
+// DS > 0: the kernel also scatters the chunk into the chosen slots (the
+// work of kv_scatter_kernel for head dim DS), after the choice is in `evict`.
+template <int KPT, int DS>
 __global__ __launch_bounds__(SEL_T) void evict_select_kernel(
-    int C, int S, int n, const float* __restrict__ scores, int32_t* __restrict__ evict) {
-    __shared__ uint32_t hist[256];
-    __shared__ uint32_t sh_wave[SEL_T / 64];
-    __shared__ uint32_t sh_digit, sh_k;
+    int C, int S, int n, float* __restrict__ scores, int32_t* __restrict__ evict,
+    uint16_t* __restrict__ kc, uint16_t* __restrict__ vc, int64_t* __restrict__ pos,
+    const uint16_t* __restrict__ kn, const uint16_t* __restrict__ vn,
+    const float* __restrict__ new_scores, int64_t p0) {
+    __shared__ uint32_t hist[3][256];
+    __shared__ uint32_t sh_scan[2 * (SEL_T / 64)];
     __shared__ unsigned long long sh_min;
+    __shared__ uint32_t sh_kmin, sh_kmax;
+    __shared__ int32_t sh_slot[DS > 0 ? SEL_SLOTS : 1];   // the choice, for the scatter
 
     const int bh = blockIdx.x, tid = threadIdx.x;
-    const float* sc = scores + (size_t)bh * C;
+    float* sc = scores + (size_t)bh * C;
     int32_t* out = evict + (size_t)bh * S;
 
+    // the scatter of chunk token t into slot out[t] (from sh_slot when S <=
+    // SEL_SLOTS, else from `out`), once the choice is complete (written by
+    // this workgroup before the barrier that precedes the call); a thread
+    // moves up to 4 pieces of 16 bytes, all loaded before any is stored
+    auto scatter = [&]() {
+        if constexpr (DS > 0) {
+            constexpr int TPR = DS / 8;   // 16-byte pieces per row
+            constexpr int U = 4;
+            const int total = S * 2 * TPR;
+            for (int i0 = tid; i0 < total; i0 += U * SEL_T) {
+                u32x4 v[U];
+                int slot[U];
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    const int i = i0 + u * SEL_T;
+                    slot[u] = -1;
+                    if (i >= total) continue;
+                    const int t = i / (2 * TPR), which = (i / TPR) & 1, c = i % TPR;
+                    slot[u] = S <= SEL_SLOTS ? sh_slot[t] : out[t];
+                    v[u] = *(const u32x4*)((which ? vn : kn) + ((size_t)bh * S + t) * DS + c * 8);
+                }
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    const int i = i0 + u * SEL_T;
+                    if (slot[u] < 0 || slot[u] >= C) continue;
+                    const int t = i / (2 * TPR), which = (i / TPR) & 1, c = i % TPR;
+                    *(u32x4*)((which ? vc : kc) + ((size_t)bh * C + slot[u]) * DS + c * 8) = v[u];
+                    if (which == 0 && c == 0) {
+                        sc[slot[u]] = new_scores[(size_t)bh * S + t];
+                        if (pos) pos[(size_t)bh * C + slot[u]] = p0 + t;
+                    }
+                }
+            }
+        }
+    };
+    // record the choice of output position o (the scatter reads it back)
+    auto put = [&](int o, int slot) {
+        out[o] = slot;
+        if constexpr (DS > 0)
+            if (S <= SEL_SLOTS) sh_slot[o] = slot;
+    };
+
     if (n + S <= C) {   // fill phase: append
-        for (int t = tid; t < S; t += SEL_T) out[t] = n + t;
+        for (int t = tid; t < S; t += SEL_T) put(t, n + t);
+        if constexpr (DS > 0) {
+            __syncthreads();
+            scatter();
+        }
         return;
     }
     if (S == 1) {   // cache full (n == C): lexicographic min of (key, slot)
@@ -181,34 +275,86 @@ __global__ __launch_bounds__(SEL_T) void evict_select_kernel(
         __syncthreads();
         if ((tid & 63) == 0) atomicMin(&sh_min, best);
         __syncthreads();
-        if (tid == 0) out[0] = (int32_t)(sh_min & 0xFFFFFFFFull);
+        if (tid == 0) put(0, (int)(sh_min & 0xFFFFFFFFull));
+        if constexpr (DS > 0) {
+            __syncthreads();
+            scatter();
+        }
         return;
     }
     const int j0 = tid * KPT;
     uint32_t key[KPT];
+    if ((C & 3) == 0) {   // 16-byte aligned rows: the run in 16-byte loads
+        float4 x[KPT / 4];
 #pragma unroll
-    for (int e = 0; e < KPT; ++e) {
-        const int j = j0 + e;
-        key[e] = (j < C) ? slot_key(sc, j, n) : 0xFFFFFFFFu;
+        for (int e4 = 0; e4 < KPT / 4; ++e4)
+            x[e4] = j0 + 4 * e4 < C ? *(const float4*)(sc + j0 + 4 * e4)
+                                    : float4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int e4 = 0; e4 < KPT / 4; ++e4) {
+            const float f[4] = {x[e4].x, x[e4].y, x[e4].z, x[e4].w};
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int j = j0 + 4 * e4 + u;
+                key[4 * e4 + u] = j >= C ? 0xFFFFFFFFu : (j < n ? score_key(f[u]) : 0u);
+            }
+        }
+    } else {
+#pragma unroll
+        for (int e = 0; e < KPT; ++e) {
+            const int j = j0 + e;
+            key[e] = (j < C) ? slot_key(sc, j, n) : 0xFFFFFFFFu;
+        }
     }
     // slots past C carry key ~0 and must never be counted or taken
     const int cnt = max(0, min(KPT, C - j0));
 
-    uint32_t prefix = 0u, mask = 0u, k = (uint32_t)S;   // k: 1-based rank
+    // The leading bytes that every key shares need no pass: the smallest and
+    // the largest key give them (and their pass would keep k).
+    uint32_t lo = 0xFFFFFFFFu, hi = 0u;
+#pragma unroll
+    for (int e = 0; e < KPT; ++e)
+        if (e < cnt) {
+            lo = min(lo, key[e]);
+            hi = max(hi, key[e]);
+        }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+        lo = min(lo, (uint32_t)__shfl_xor(lo, off, 64));
+        hi = max(hi, (uint32_t)__shfl_xor(hi, off, 64));
+    }
+    if (tid == 0) {
+        sh_kmin = 0xFFFFFFFFu;
+        sh_kmax = 0u;
+    }
+    // all three buffers start cleared: the first pass that runs may be any
+    for (int i = tid; i < 3 * 256; i += SEL_T) hist[i / 256][i % 256] = 0u;
+    __syncthreads();
+    if ((tid & 63) == 0) {
+        atomicMin(&sh_kmin, lo);
+        atomicMax(&sh_kmax, hi);
+    }
+    __syncthreads();
+    const uint32_t kmin = sh_kmin, diff = kmin ^ sh_kmax;
+    const int first = diff == 0u ? 4 : __builtin_clz(diff) / 8;   // passes 0..first-1 skipped
+    uint32_t mask = first >= 4 ? 0xFFFFFFFFu : (first == 0 ? 0u : ~0u << (32 - 8 * first));
+    uint32_t prefix = kmin & mask, k = (uint32_t)S;   // k: 1-based rank
+#pragma unroll
     for (int pass = 0; pass < 4; ++pass) {
+        if (pass < first) continue;   // workgroup-uniform
         const int shift = 24 - 8 * pass;
-        for (int i = tid; i < 256; i += SEL_T) hist[i] = 0u;
-        __syncthreads();
+        uint32_t* h = hist[pass % 3];
+        if (pass < 3)
+            for (int i = tid; i < 256; i += SEL_T) hist[(pass + 1) % 3][i] = 0u;
 #pragma unroll
         for (int e = 0; e < KPT; ++e)
-            hist_add(hist, (key[e] >> shift) & 255u, e < cnt && (key[e] & mask) == prefix);
+            hist_add(h, (key[e] >> shift) & 255u, e < cnt && (key[e] & mask) == prefix);
         __syncthreads();
-        if (tid < 64) find_bin(hist, k, &sh_digit, &sh_k);
-        __syncthreads();
-        prefix |= sh_digit << shift;
+        uint32_t digit, k_in;
+        find_bin_wave(h, k, digit, k_in);
+        prefix |= digit << shift;
         mask |= 255u << shift;
-        k = sh_k;
-        __syncthreads();
+        k = k_in;
     }
     const uint32_t T = prefix;
 
@@ -218,10 +364,14 @@ __global__ __launch_bounds__(SEL_T) void evict_select_kernel(
         n_eq += (e < cnt && key[e] == T);
         n_lt += (e < cnt && key[e] < T);
     }
-    const uint32_t eq_before = block_exclusive_scan(n_eq, sh_wave);
-    const uint32_t eq_take = (k > eq_before) ? min(k - eq_before, n_eq) : 0u;
-    const uint32_t out_before = block_exclusive_scan(n_lt + eq_take, sh_wave);
-    uint32_t o = out_before, eq_seen = 0;
+    // ties are taken in slot order: the threads before this one take
+    // eq_prev = min(k, eq_before) of them, this one the next eq_take
+    uint32_t eq_before, lt_before;
+    block_exclusive_scan2(n_eq, n_lt, sh_scan, eq_before, lt_before);
+    const uint32_t eq_prev = eq_before < k ? eq_before : k;
+    const uint32_t eq_room = k - eq_prev;   // no wrap: eq_prev <= k
+    const uint32_t eq_take = eq_room < n_eq ? eq_room : n_eq;
+    uint32_t o = lt_before + eq_prev, eq_seen = 0;
 #pragma unroll
     for (int e = 0; e < KPT; ++e) {
         if (e >= cnt) break;
@@ -231,9 +381,13 @@ __global__ __launch_bounds__(SEL_T) void evict_select_kernel(
             ++eq_seen;
         }
         if (take) {
-            if (o < (uint32_t)S) out[o] = j0 + e;   // never past the row, whatever the counts
+            if (o < (uint32_t)S) put((int)o, j0 + e);   // never past the row, whatever the counts
             ++o;
         }
+    }
+    if constexpr (DS > 0) {
+        __syncthreads();
+        scatter();
     }
 }
 
@@ -569,18 +723,50 @@ hipError_t launch_evict_select(int BH, int C, int S, int n, const float* scores,
                                int32_t* evict_idx, hipStream_t stream) {
     // keys per thread: the smallest supported run that covers C
     const int kpt = (C + SEL_T - 1) / SEL_T;
+    float* sc = const_cast<float*>(scores);   // read only without a scatter
+#define H2O_SEL(KPT)                                                                    \
+    hipLaunchKernelGGL((evict_select_kernel<KPT, 0>), dim3(BH), dim3(SEL_T), 0, stream, C, S, \
+                       n, sc, evict_idx, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, \
+                       (int64_t)0)
     if (kpt > 64)
         hipLaunchKernelGGL(select_stream_kernel<false>, dim3(BH), dim3(SEL_T), 0, stream, C, S,
                            n, scores, (long)C, evict_idx, (long)S);
     else if (kpt <= 4)
-        hipLaunchKernelGGL(evict_select_kernel<4>, dim3(BH), dim3(SEL_T), 0, stream, C, S, n,
-                           scores, evict_idx);
+        H2O_SEL(4);
     else if (kpt <= 16)
-        hipLaunchKernelGGL(evict_select_kernel<16>, dim3(BH), dim3(SEL_T), 0, stream, C, S, n,
-                           scores, evict_idx);
-    else if (kpt <= 64)
-        hipLaunchKernelGGL(evict_select_kernel<64>, dim3(BH), dim3(SEL_T), 0, stream, C, S, n,
-                           scores, evict_idx);
+        H2O_SEL(16);
+    else
+        H2O_SEL(64);
+#undef H2O_SEL
+    return hipGetLastError();
+}
+
+bool select_scatter_fuses(int C) { return (C + SEL_T - 1) / SEL_T <= 64; }
+
+hipError_t launch_select_scatter(int BH, int D, int C, int S, int n, float* scores,
+                                 int32_t* evict_idx, uint16_t* kc, uint16_t* vc, int64_t* pos,
+                                 const uint16_t* kn, const uint16_t* vn,
+                                 const float* new_scores, int64_t p0, hipStream_t stream) {
+    const int kpt = (C + SEL_T - 1) / SEL_T;
+#define H2O_SEL(KPT, DS)                                                                   \
+    hipLaunchKernelGGL((evict_select_kernel<KPT, DS>), dim3(BH), dim3(SEL_T), 0, stream, C, S, \
+                       n, scores, evict_idx, kc, vc, pos, kn, vn, new_scores, p0)
+    if (D == 64) {
+        if (kpt <= 4)
+            H2O_SEL(4, 64);
+        else if (kpt <= 16)
+            H2O_SEL(16, 64);
+        else
+            H2O_SEL(64, 64);
+    } else {
+        if (kpt <= 4)
+            H2O_SEL(4, 128);
+        else if (kpt <= 16)
+            H2O_SEL(16, 128);
+        else
+            H2O_SEL(64, 128);
+    }
+#undef H2O_SEL
     return hipGetLastError();
 }
 
