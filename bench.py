@@ -275,7 +275,7 @@ def measured_traffic(workload, kernel):
     none for this workload or the kernel source changed since it was taken."""
     import re
     name = {"qwen3_4b_128k": "attn_fwd_qwen3_4b_128k_hbm_bytes.txt",
-            "decode": "attn_fwd_small_decode_hbm_bytes.txt"}.get(workload)
+            "decode": "attn_fwd_few_decode_hbm_bytes.txt"}.get(workload)
     path = os.path.join(ROOT, "profiles", name) if name else ""
     if name is None or not os.path.exists(path):
         return None
@@ -665,7 +665,8 @@ def run_snapkv(args, wl):
     pairs = pairs_per_layer_step(B, Hq, C, S, C)
     per_layer = {k: v / calls for k, v in kernel_ms.items()}
     if single_call and Hq // Hkv * S <= 32 and S == 1:
-        # h2o_step's decode path: the streaming pass, then one tail kernel
+        # h2o_step's decode path: the streaming pass, then the tail kernels
+        # (weights, scores and running minimum; choice and scatter)
         per_layer = {"attn_fwd": per_layer["attn_fwd"], "decode_tail": per_layer["attn_combine"]}
     per_layer.update(part_ms)
     fwd_ms = per_layer["attn_fwd"]
@@ -880,7 +881,8 @@ def main():
     fwd_ms = kernel_ms["attn_fwd"] / calls
     per_layer = {k: v / calls for k, v in kernel_ms.items()}
     if single_call and Hq // Hkv * S <= 32 and S == 1:
-        # h2o_step's decode path: the streaming pass, then one tail kernel
+        # h2o_step's decode path: the streaming pass, then the tail kernels
+        # (weights, scores and running minimum; choice and scatter)
         per_layer = {"attn_fwd": per_layer["attn_fwd"], "decode_tail": per_layer["attn_combine"]}
     # pass 1 reads every cached K/V row once plus the chunk's Q/K/V
     cache_row_bytes = (D + 4) if args.kv8 else 2 * D   # int8 codes + scale, or bf16
@@ -893,10 +895,13 @@ def main():
         roof = {"bound": "hbm", "achieved": fwd_bytes / (fwd_ms * 1e-3) / 1e9,
                 "peak": PEAK_HBM_GBS, "unit": "GB/s", "per_launch_bytes": fwd_bytes}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    small = Hq // Hkv * S <= 32
-    fwd_kernel = (("attn_fwd_small_q8_kernel<%d>" if small else "attn_fwd_q8_kernel<%d>") % D
-                  if args.kv8 else
-                  ("attn_fwd_small_kernel<%d>" if small else "attn_fwd_kernel<%d>") % D)
+    rows = Hq // Hkv * S   # packed query rows per (b, kv head)
+    small = rows <= 32
+    if args.kv8:
+        fwd_kernel = ("attn_fwd_small_q8_kernel<%d>" if small else "attn_fwd_q8_kernel<%d>") % D
+    else:
+        fwd_kernel = ("attn_fwd_few_kernel<%d>" if rows <= 16 else
+                      "attn_fwd_small_kernel<%d>" if small else "attn_fwd_kernel<%d>") % D
     traffic = None if args.kv8 else measured_traffic(wl.name, fwd_kernel)
     per_layer["policy_and_gaps"] = ms_per_step / L - sum(per_layer.values())
     total_flop_exec = 6.0 * D * pairs

@@ -224,11 +224,11 @@ h2o_status_t h2o_step(const h2o_shape_t* s, const uint16_t* q, uint16_t* k_cache
     const int BH = s->batch * s->n_kv_heads;
     // the kernel that writes the summed weights also accumulates the scores;
     // the choice and the scatter share one kernel where the keys fit in
-    // registers
+    // registers and the chunk is short
     hipError_t e = h2o::launch_attention(pl, q, k_cache, v_cache, k_new, v_new, out, lse, wsum,
                                          ws, str, sync_debug(), timing_slot(), scores,
                                          new_scores);
-    if (e == hipSuccess && h2o::select_scatter_fuses(s->cache_len)) {
+    if (e == hipSuccess && h2o::select_scatter_fuses(s->cache_len, s->chunk_len, s->head_dim)) {
         e = h2o::launch_select_scatter(BH, s->head_dim, s->cache_len, s->chunk_len, s->n_valid,
                                        scores, evict_idx, k_cache, v_cache, pos, k_new, v_new,
                                        new_scores, p0, str);

@@ -94,8 +94,9 @@ hipError_t launch_evict_select(int BH, int C, int S, int n,
                                hipStream_t stream);
 
 // launch_evict_select followed by launch_kv_scatter in one kernel (same
-// results), for rows whose keys fit in registers (select_scatter_fuses(C)).
-bool select_scatter_fuses(int C);
+// results), for rows whose keys fit in registers and short chunks
+// (select_scatter_fuses).
+bool select_scatter_fuses(int C, int S, int D);
 hipError_t launch_select_scatter(int BH, int D, int C, int S, int n, float* scores,
                                  int32_t* evict_idx, uint16_t* kc, uint16_t* vc, int64_t* pos,
                                  const uint16_t* kn, const uint16_t* vn,

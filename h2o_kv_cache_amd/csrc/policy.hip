@@ -741,7 +741,12 @@ hipError_t launch_evict_select(int BH, int C, int S, int n, const float* scores,
     return hipGetLastError();
 }
 
-bool select_scatter_fuses(int C) { return (C + SEL_T - 1) / SEL_T <= 64; }
+// The fused kernel moves the chunk with one workgroup per (b, kv head): worth
+// it for a short chunk (up to four 16-byte pieces per thread; S <= 128 at
+// D = 128), while a long chunk moves faster in kv_scatter_kernel's grid.
+bool select_scatter_fuses(int C, int S, int D) {
+    return (C + SEL_T - 1) / SEL_T <= 64 && S * 2 * (D / 8) <= 4 * SEL_T;
+}
 
 hipError_t launch_select_scatter(int BH, int D, int C, int S, int n, float* scores,
                                  int32_t* evict_idx, uint16_t* kc, uint16_t* vc, int64_t* pos,
