@@ -436,16 +436,26 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_kernel(
             full_tile(BufC<0>{}, t);
             if (t + 1 < t_mid) full_tile(BufC<1>{}, t + 1);
         }
+        // the rest: the partial cache tile and the chunk tiles; a chunk tile
+        // whose keys all exist and precede this wave's first query (query
+        // rbase / G) needs no mask, only the tiles on the diagonal do
+        const int wave_q0 = rbase / g.G;
         for (int t = t_mid; t < t_end; ++t) {
             const int buf = (t - t_begin) & 1;
             const bool chunk = t >= tr.n_ct;
             const int key0 = chunk ? (t - tr.n_ct) * KT : t * KT;
             const int lim = chunk ? g.S : g.n;
             if (t + 1 < t_end) issue(t + 1, buf ^ 1);
-            if (live > 0)
-                fwd_tile<D, true, false, false>(Ks[buf], Vs[buf], off, qf, o_acc, m_ref, m_seen,
-                                                overflow, l_acc, lt_acc, g.c, key0, lim, chunk,
-                                                g.G, rbase, lane);
+            if (live > 0) {
+                if (chunk && key0 + KT <= g.S && key0 + KT - 1 <= wave_q0)
+                    fwd_tile<D, false, false, false>(Ks[buf], Vs[buf], off, qf, o_acc, m_ref,
+                                                     m_seen, overflow, l_acc, lt_acc, g.c, 0, 0,
+                                                     false, 0, rbase, lane);
+                else
+                    fwd_tile<D, true, false, false>(Ks[buf], Vs[buf], off, qf, o_acc, m_ref,
+                                                    m_seen, overflow, l_acc, lt_acc, g.c, key0,
+                                                    lim, chunk, g.G, rbase, lane);
+            }
             wait_tiles();
             __syncthreads();
         }
@@ -1671,7 +1681,10 @@ __global__ __launch_bounds__(NT, 2) void attn_colsum_kernel(
 #pragma unroll
                 for (int kb = 0; kb < KT2 / 32; ++kb) colp[buf][wave][kb * 32 + l32] = 0.f;
             }
-        } else if (!chunk && key0 + KT2 <= g.n) {
+        } else if (chunk ? key0 + KT2 <= g.S && key0 + KT2 - 1 <= rbase / g.G
+                         : key0 + KT2 <= g.n) {
+            // a full cache tile, or a chunk tile whose keys all exist and
+            // precede this wave's first query: no mask
             colsum_tile<D, false, false, KT2>(Ks[buf], off, colp[buf][wave], qf, l2v, g.c, 0, 0,
                                               0, rbase, l32, half);
         } else {
