@@ -412,14 +412,18 @@ def run_backward(args, wl):
     elapsed_ms = t_start.elapsed_time(t_stop)
     ms_per_step = elapsed_ms / args.steps
     pairs = pairs_per_layer_step(B, Hq, C, S, C)
-    names = ("bwd_prep", "bwd_dkdv", "bwd_dq")
+    # D = 128: dK/dV and dQ share one grid (bwd_dkdv_dq_kernel), then the
+    # split reduction of dQ; D = 64: dK/dV, then dQ and its reduction
+    names = (("bwd_prep", "bwd_dkdv_dq", "bwd_dq_reduce") if D == 128 else
+             ("bwd_prep", "bwd_dkdv", "bwd_dq"))
     per_layer = {n: kernel_ms[k] / calls for n, k in zip(names, h2o.ATTN_KERNELS)}
-    dkdv_ms = per_layer["bwd_dkdv"]
+    dkdv_ms = per_layer[names[1]]
     # algorithmic, 2*D flop per pair each: dP = dO V^T, dV = P^T dO and
-    # dK = dS^T Q (the key-major kernel), dQ = dS K (the query-major one).
-    # Executed: the key-major kernel also recomputes S (8*D per pair), the
-    # query-major one S and dP (6*D per pair)
-    dkdv_flop = 6.0 * D * pairs
+    # dK = dS^T Q (the key-major part), dQ = dS K (the query-major one).
+    # Executed: the key-major part also recomputes S (8*D per pair), the
+    # query-major one S and dP (6*D per pair).  At D = 128 the roofline
+    # kernel runs both parts: 8*D algorithmic flop per pair
+    dkdv_flop = (8.0 if D == 128 else 6.0) * D * pairs
     roof = {"bound": "mfma", "achieved": dkdv_flop / (dkdv_ms * 1e-3) / 1e12,
             "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "per_launch_flop": dkdv_flop}
     roof["frac"] = roof["achieved"] / roof["peak"]
@@ -443,7 +447,8 @@ def run_backward(args, wl):
             "algorithmic_flop_per_layer_step": 8.0 * D * pairs,
             "algorithmic_tflops_whole_step": 8.0 * D * pairs * L / (ms_per_step * 1e-3) / 1e12,
         },
-        "roofline": dict(kernel=("bwd_dkdv_pair_kernel<128> (S, P, dP, dV, dK)" if D == 128
+        "roofline": dict(kernel=("bwd_dkdv_dq_kernel<128> (dK/dV key tiles: S, P, dP, dV, dK; "
+                                 "dQ row tiles: S, P, dP, dQ)" if D == 128
                                  else "bwd_dkdv_kernel<%d> (S, P, dP, dV, dK)" % D), traffic=None,
                          avg_launch_ms=dkdv_ms, launches=calls, **roof),
     }

@@ -14,7 +14,7 @@
 //   dQ = scale dS K,   dK = scale dS^T Q,   dV = P^T dO.
 // Kernels:
 //   bwd_prep_kernel       per packed row: L2 and D.
-//   bwd_dkdv_pair_kernel  key-major, D = 128.  Two waves of one SIMD share a
+//   dkdv_pair_body        key-major, D = 128.  Two waves of one SIMD share a
 //                         32-key block of one KV head: one keeps the K
 //                         fragments and dV^T accumulators (S, P, dV), the
 //                         other the V fragments and dK^T accumulators (dP,
@@ -25,9 +25,12 @@
 //                         LDS.
 //   bwd_dkdv_kernel       key-major, D = 64: one wave owns two 32-key blocks
 //                         with both sets of fragments and accumulators.
-//   bwd_dq_kernel         row-major, shaped like the forward's pass 1:
+//   dq_body               row-major, shaped like the forward's pass 1:
 //                         S^T = K Q^T and dP^T = V dO^T (a lane owns a row),
-//                         then dQ^T += K^T dS^T.
+//                         then dQ^T += K^T dS^T (bwd_dq_kernel at D = 64).
+//   bwd_dkdv_dq_kernel    D = 128: the dK/dV key tiles and the dQ row tiles
+//                         in one grid, so that the dQ workgroups fill the
+//                         last, partial round of key tiles.
 // Rows are packed as in the forward: row r of a (b, kv head h) is query r / G
 // of head h*G + r % G.  Every reduction has a fixed order.
 #include "h2o_device.h"
@@ -351,13 +354,16 @@ __device__ __forceinline__ u32x2 lds_ld_tr(uint32_t addr) {
     return __builtin_bit_cast(u32x2, v);
 }
 
+// The body of one dK/dV workgroup (key tile `blk` of the (b, kv head)-major
+// list), run by bwd_dkdv_dq_kernel.
 template <int D>
-__global__ __launch_bounds__(PQ_NT, 1) void bwd_dkdv_pair_kernel(
-    const BwdGeom g, const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc,
-    const uint16_t* __restrict__ vc, const uint16_t* __restrict__ kn,
-    const uint16_t* __restrict__ vn, const uint16_t* __restrict__ dout,
-    const float* __restrict__ l2, const float* __restrict__ drow, float* __restrict__ dkc,
-    float* __restrict__ dvc, float* __restrict__ dkn, float* __restrict__ dvn) {
+__device__ __forceinline__ void dkdv_pair_body(
+    const int blk, const BwdGeom& g, const uint16_t* __restrict__ q,
+    const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc,
+    const uint16_t* __restrict__ kn, const uint16_t* __restrict__ vn,
+    const uint16_t* __restrict__ dout, const float* __restrict__ l2,
+    const float* __restrict__ drow, float* __restrict__ dkc, float* __restrict__ dvc,
+    float* __restrict__ dkn, float* __restrict__ dvn) {
     constexpr int TILE = BR * D;
     constexpr int NDB = D / 32;
     constexpr int CPR = D / 8;                       // 16-byte chunks per row
@@ -374,7 +380,7 @@ __global__ __launch_bounds__(PQ_NT, 1) void bwd_dkdv_pair_kernel(
 
     const int n_ct = (g.C + PQ_KEYS - 1) / PQ_KEYS;
     const int n_kt = n_ct + (g.S + PQ_KEYS - 1) / PQ_KEYS;
-    const int bh = blockIdx.x / n_kt, kt = blockIdx.x % n_kt;
+    const int bh = blk / n_kt, kt = blk % n_kt;
     const int b = bh / g.Hkv, h = bh % g.Hkv;
     const bool chunk = kt >= n_ct;
     const int key0 = (chunk ? kt - n_ct : kt) * PQ_KEYS;
@@ -593,6 +599,7 @@ __global__ __launch_bounds__(PQ_NT, 1) void bwd_dkdv_pair_kernel(
         }
 }
 
+
 // ---------------------------------------------------------------------------
 // dQ: row-major
 // ---------------------------------------------------------------------------
@@ -601,13 +608,16 @@ constexpr int Q_NT = Q_WAVES * 64;
 constexpr int Q_ROWS = Q_WAVES * BR;        // rows per workgroup
 constexpr int Q_KT = 64;                    // keys per tile
 
+// The body of dQ workgroup `blk` of `nblk`, shared by bwd_dq_kernel and
+// bwd_dkdv_dq_kernel.
 template <int D>
-__global__ __launch_bounds__(Q_NT, 1) void bwd_dq_kernel(
-    const BwdGeom g, const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc,
-    const uint16_t* __restrict__ vc, const uint16_t* __restrict__ kn,
-    const uint16_t* __restrict__ vn, const uint16_t* __restrict__ dout,
-    const float* __restrict__ l2, const float* __restrict__ drow, const int nsplit,
-    float* __restrict__ dq, float* __restrict__ dq_part) {
+__device__ __forceinline__ void dq_body(
+    const int blk, const int nblk, const BwdGeom& g, const uint16_t* __restrict__ q,
+    const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc,
+    const uint16_t* __restrict__ kn, const uint16_t* __restrict__ vn,
+    const uint16_t* __restrict__ dout, const float* __restrict__ l2,
+    const float* __restrict__ drow, const int nsplit, float* __restrict__ dq,
+    float* __restrict__ dq_part) {
     constexpr int TILE = Q_KT * D;
     constexpr int CPR = D / 8;
     constexpr int NDB = D / 32;
@@ -618,7 +628,7 @@ __global__ __launch_bounds__(Q_NT, 1) void bwd_dq_kernel(
 
     const int n_rt = (g.R + Q_ROWS - 1) / Q_ROWS;
     int rt, bh, split;
-    decode_block(n_rt, nsplit, rt, bh, split);
+    decode_block_at(blk, nblk, n_rt, nsplit, rt, bh, split);
     const int b = bh / g.Hkv, h = bh % g.Hkv;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -799,6 +809,40 @@ __global__ __launch_bounds__(Q_NT, 1) void bwd_dq_kernel(
         }
 }
 
+template <int D>
+__global__ __launch_bounds__(Q_NT, 1) void bwd_dq_kernel(
+    const BwdGeom g, const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc,
+    const uint16_t* __restrict__ vc, const uint16_t* __restrict__ kn,
+    const uint16_t* __restrict__ vn, const uint16_t* __restrict__ dout,
+    const float* __restrict__ l2, const float* __restrict__ drow, const int nsplit,
+    float* __restrict__ dq, float* __restrict__ dq_part) {
+    dq_body<D>(blockIdx.x, gridDim.x, g, q, kc, vc, kn, vn, dout, l2, drow, nsplit, dq, dq_part);
+}
+
+// dK/dV and dQ in one grid: the first n_dkdv workgroups are dK/dV key tiles,
+// the rest dQ workgroups.  The two are independent, and the dQ workgroups,
+// dispatched after every dK/dV one, fill the CUs that the last, partial
+// round of dK/dV key tiles leaves idle (at the 128k shape 1088 key tiles
+// make 4.25 rounds of 256).  Both halves take 8 waves and about 205 VGPRs
+// per lane, so the fused kernel keeps one workgroup per CU.
+template <int D>
+__global__ __launch_bounds__(PQ_NT, 1) void bwd_dkdv_dq_kernel(
+    const BwdGeom g, const int n_dkdv, const uint16_t* __restrict__ q,
+    const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc,
+    const uint16_t* __restrict__ kn, const uint16_t* __restrict__ vn,
+    const uint16_t* __restrict__ dout, const float* __restrict__ l2,
+    const float* __restrict__ drow, float* __restrict__ dkc, float* __restrict__ dvc,
+    float* __restrict__ dkn, float* __restrict__ dvn, const int nsplit,
+    float* __restrict__ dq, float* __restrict__ dq_part) {
+    static_assert(PQ_NT == Q_NT, "one block size for both halves");
+    const int L = blockIdx.x;
+    if (L < n_dkdv)
+        dkdv_pair_body<D>(L, g, q, kc, vc, kn, vn, dout, l2, drow, dkc, dvc, dkn, dvn);
+    else
+        dq_body<D>(L - n_dkdv, (int)gridDim.x - n_dkdv, g, q, kc, vc, kn, vn, dout, l2, drow,
+                   nsplit, dq, dq_part);
+}
+
 // dQ = scale * (sum of the key splits' partials, in split order)
 __global__ __launch_bounds__(256) void bwd_dq_reduce_kernel(const float* __restrict__ part,
                                                            int nsplit, long n4, float tau,
@@ -852,34 +896,36 @@ hipError_t launch_bwd_d(const BwdGeom& g, const uint16_t* q, const uint16_t* kc,
         H2O_CHECK();
     }
     H2O_EVENT(1);
+    const int n_rt = (g.R + Q_ROWS - 1) / Q_ROWS;
+    const int nsplit = bwd_dq_splits(g);
+    float* part = drow + bwd_rows_padded(g);
     if constexpr (D == 128) {
+        // dK/dV and dQ in one grid (the dQ workgroups fill the dK/dV tail)
         const int n_kt = (g.C + PQ_KEYS - 1) / PQ_KEYS + (g.S + PQ_KEYS - 1) / PQ_KEYS;
-        hipLaunchKernelGGL(bwd_dkdv_pair_kernel<D>, dim3(BH * n_kt), dim3(PQ_NT), 0, stream, g,
-                           q, kc, vc, kn, vn, dout, l2, drow, dkc, dvc, dkn, dvn);
+        const int n_dkdv = BH * n_kt;
+        hipLaunchKernelGGL(bwd_dkdv_dq_kernel<D>, dim3(n_dkdv + BH * n_rt * nsplit), dim3(PQ_NT),
+                           0, stream, g, n_dkdv, q, kc, vc, kn, vn, dout, l2, drow, dkc, dvc,
+                           dkn, dvn, nsplit, dq, part);
         H2O_CHECK();
+        H2O_EVENT(2);
     } else {
         constexpr int KV_KEYS = kv_keys<D>();
         const int n_kt = (g.C + KV_KEYS - 1) / KV_KEYS + (g.S + KV_KEYS - 1) / KV_KEYS;
         hipLaunchKernelGGL(bwd_dkdv_kernel<D>, dim3(BH * n_kt), dim3(KV_NT), 0, stream, g, q, kc,
                            vc, kn, vn, dout, l2, drow, dkc, dvc, dkn, dvn);
         H2O_CHECK();
-    }
-    H2O_EVENT(2);
-    {
-        const int n_rt = (g.R + Q_ROWS - 1) / Q_ROWS;
-        const int nsplit = bwd_dq_splits(g);
-        float* part = drow + bwd_rows_padded(g);
+        H2O_EVENT(2);
         hipLaunchKernelGGL(bwd_dq_kernel<D>, dim3(BH * n_rt * nsplit), dim3(Q_NT), 0, stream, g,
                            q, kc, vc, kn, vn, dout, l2, drow, nsplit, dq, part);
         H2O_CHECK();
-        if (nsplit > 1) {
-            const long n4 = (long)g.B * g.Hq * g.S * D / 4;
-            long blocks = (n4 + 255) / 256;
-            if (blocks > 8192) blocks = 8192;
-            hipLaunchKernelGGL(bwd_dq_reduce_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
-                               part, nsplit, n4, g.tau, dq);
-            H2O_CHECK();
-        }
+    }
+    if (nsplit > 1) {
+        const long n4 = (long)g.B * g.Hq * g.S * D / 4;
+        long blocks = (n4 + 255) / 256;
+        if (blocks > 8192) blocks = 8192;
+        hipLaunchKernelGGL(bwd_dq_reduce_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
+                           part, nsplit, n4, g.tau, dq);
+        H2O_CHECK();
     }
     H2O_EVENT(3);
     H2O_EVENT(4);

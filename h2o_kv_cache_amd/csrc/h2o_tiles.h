@@ -13,15 +13,20 @@ namespace {
 // XCD L % 8).  Re-index so that each XCD receives one contiguous run of the
 // (bh, split, qt) work list: the row tiles that read the same K/V tiles then
 // share one XCD's L2.
-__device__ __forceinline__ void decode_block(int n_qt, int nsplit, int& qt, int& bh,
-                                             int& split) {
-    const int L = blockIdx.x, N = gridDim.x;
+// decode_block for workgroup L of N (a part of a larger grid).
+__device__ __forceinline__ void decode_block_at(int L, int N, int n_qt, int nsplit, int& qt,
+                                                int& bh, int& split) {
     const int q8 = N >> 3, r8 = N & 7, x = L & 7, j = L >> 3;
     const int lam = x * q8 + min(x, r8) + j;
     qt = lam % n_qt;
     const int rest = lam / n_qt;
     split = rest % nsplit;
     bh = rest / nsplit;
+}
+
+__device__ __forceinline__ void decode_block(int n_qt, int nsplit, int& qt, int& bh,
+                                             int& split) {
+    decode_block_at(blockIdx.x, gridDim.x, n_qt, nsplit, qt, bh, split);
 }
 
 // LDS tiles are ROWS x D bf16, row-major, with the 16-byte chunks of each row
