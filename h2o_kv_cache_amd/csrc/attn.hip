@@ -2147,9 +2147,11 @@ __global__ __launch_bounds__(NT_S, 3) void attn_fwd_small_q8_kernel(
     // wave that read it, after its reads of it have returned.
     auto issue = [&](int t, int sb) {
         const int k0 = t * KT + wave * 32;
-        issue_tile_i8<D, 1, 32, 1>(stg[sb] + wave * 32 * D, qc.kc + row0 * D, k0, g.n, 0, lane);
-        issue_tile_i8<D, 1, 32, 2>(stg[sb] + KT * D + wave * 32 * D, qc.vc + row0 * D, k0, g.n, 0,
-                                   lane);
+        // rows read once: non-temporal copies
+        issue_tile_i8<D, 1, 32, 1, true>(stg[sb] + wave * 32 * D, qc.kc + row0 * D, k0, g.n, 0,
+                                         lane);
+        issue_tile_i8<D, 1, 32, 2, true>(stg[sb] + KT * D + wave * 32 * D, qc.vc + row0 * D, k0,
+                                         g.n, 0, lane);
         const int gkey = min(k0 + l32, g.n - 1);
         dma4((half ? qc.vs : qc.ks) + row0 + gkey,
              __builtin_amdgcn_readfirstlane(lds_addr(&ssc[sb][wave][0])));

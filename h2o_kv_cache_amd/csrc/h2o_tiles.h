@@ -67,6 +67,14 @@ __device__ __forceinline__ void dma16(const uint16_t* gptr, uint32_t lds) {
                  : "memory", "m0");
 }
 
+// dma16 with the non-temporal hint (rows read once; see dma16_s_nt).
+__device__ __forceinline__ void dma16_nt(const uint16_t* gptr, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off nt"
+                 :
+                 : "s"(lds), "v"(gptr)
+                 : "memory", "m0");
+}
+
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
     return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
@@ -185,8 +193,9 @@ __device__ __forceinline__ int i8_swz_v(int key) {
     return D >= 128 ? ((key & 3) | ((key >> 1) & 4)) : (key & 3);
 }
 
-// SWZ: 0 none, 1 i8_swz (K tiles), 2 i8_swz_v (V tiles)
-template <int D, int NW, int ROWS = kKeyTile, int SWZ = 0>
+// SWZ: 0 none, 1 i8_swz (K tiles), 2 i8_swz_v (V tiles); NT: non-temporal
+// copies (rows read once)
+template <int D, int NW, int ROWS = kKeyTile, int SWZ = 0, bool NT = false>
 __device__ __forceinline__ void issue_tile_i8(uint8_t* tile, const int8_t* __restrict__ src,
                                               int key0, int lim, int wave, int lane) {
     constexpr int CPR = D / 16;                  // 16-byte chunks per row
@@ -200,7 +209,11 @@ __device__ __forceinline__ void issue_tile_i8(uint8_t* tile, const int8_t* __res
             const int key = p / CPR;
             const int c = (p % CPR) ^ (SWZ == 1 ? i8_swz<D>(key) : SWZ == 2 ? i8_swz_v<D>(key) : 0);
             const int gkey = min(key0 + key, lim - 1);
-            dma16((const uint16_t*)(src + (size_t)gkey * D + c * 16), base + blk * 1024);
+            const uint16_t* g = (const uint16_t*)(src + (size_t)gkey * D + c * 16);
+            if constexpr (NT)
+                dma16_nt(g, base + blk * 1024);
+            else
+                dma16(g, base + blk * 1024);
         }
     }
 }
