@@ -18,13 +18,14 @@
 //                               the PV MFMA straight from the accumulators.
 //   combine                     merges the key splits: O, L (natural log for
 //                               the caller, base 2 for pass 2).
-//   pass 2 (attn_colsum_kernel) S = Q K^T on MFMA (the other orientation: a
-//                               lane owns one key and 16 query rows), so the
-//                               column sums of P = exp2(S*c - L2) reduce
-//                               in-lane, then across the two wave halves, then
-//                               across the 4 waves through LDS in a fixed
-//                               order.  Writes one partial row of column sums
-//                               per 128-row tile.
+//   pass 2 (attn_colsum_kernel) S = Q K^T on the 16x16x32 MFMA (the other
+//                               orientation: a lane owns one key and 8 query
+//                               rows of a 16-key block), so the column sums
+//                               of P = exp2(S*c - L2) reduce in-lane, then
+//                               across the four 16-lane groups, then across
+//                               the 8 waves through LDS in a fixed order.
+//                               Writes one partial row of column sums per
+//                               256-row tile.
 //   wsum reduce                 sums the row-tile partials in tile order.
 //
 // Rows of a (b, kv head) pack the G query heads of its group: row r is query
@@ -1592,6 +1593,117 @@ __device__ __forceinline__ void colsum_tile(const uint16_t* Ks, const LdsOffsets
     }
 }
 
+// Pass 2 on the 16x16x32 MFMA.  S = Q K^T per 16-key block: a lane holds key
+// l%16 of the block and rows 4*(l/16) + [0, 4) of each of the wave's two
+// 16-row blocks, so a block needs 8 accumulator registers and the products
+// of the next block are issued before this block's exponentials (the two
+// streams of one wave overlap on the SIMD).  Each lane sums its 8 rows per
+// block; the four 16-lane groups are then reduced in a reduce-scatter, so
+// that lane l ends with the totals of NB/4 blocks.
+//   qf[rb][ks]: row rbase + 16*rb + l%16, dims 32*ks + 8*(l/16) + [0, 8)
+//   l2v[rb][e]: base-2 LSE of row rbase + 16*rb + 4*(l/16) + e
+//   koff[ks]:   K fragment of key l%16, dims 32*ks + 8*(l/16) + [0, 8)
+template <int D>
+__device__ __forceinline__ void load_q16(bf16x8 (&qf)[2][D / 32], const uint16_t* __restrict__ q,
+                                         const AttnGeom& g, int b, int h, int rbase, int l16,
+                                         int grp) {
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+        const int r = rbase + rb * 16 + l16;
+        const bool ok = r < g.R;
+        const uint16_t* qrow =
+            q + (((size_t)b * g.Hq + (size_t)h * g.G + (r % g.G)) * g.S + r / g.G) * D;
+#pragma unroll
+        for (int ks = 0; ks < D / 32; ++ks) {
+            u32x4 v = {0u, 0u, 0u, 0u};
+            if (ok) v = *(const u32x4*)(qrow + ks * 32 + grp * 8);
+            qf[rb][ks] = as_bf16x8(v);
+        }
+    }
+}
+
+template <int D, bool MASKED, int KTT>
+__device__ __forceinline__ void colsum_tile16(const uint16_t* Ks, const uint32_t (&koff)[D / 32],
+                                              float* colp, const bf16x8 (&qf)[2][D / 32],
+                                              const float (&l2v)[2][4], float c, int key0,
+                                              int lim, int G, int rbase, int lane) {
+    constexpr int NB = KTT / 16;
+    static_assert(NB % 4 == 0, "tile of 64-key multiples");
+    const int l16 = lane & 15, grp = lane >> 4;
+    // software pipeline, one stage per 16-key block: the K fragments of
+    // block i+1 are read and its products issued while the weights of block
+    // i are formed; the scheduling fence between stages keeps the compiler
+    // from hoisting every read of the tile (register pressure)
+    auto read_k = [&](int blk, bf16x8 (&kf)[D / 32]) {
+#pragma unroll
+        for (int ks = 0; ks < D / 32; ++ks)
+            kf[ks] = as_bf16x8(lds_read16(Ks, koff[ks] + blk * 16 * D * 2));
+    };
+    auto products = [&](const bf16x8 (&kf)[D / 32], f32x4 (&s)[2]) {
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) s[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < D / 32; ++ks)
+#pragma unroll
+            for (int rb = 0; rb < 2; ++rb) s[rb] = mfma16x16x32(qf[rb][ks], kf[ks], s[rb]);
+    };
+    auto weights = [&](int blk, const f32x4 (&s)[2]) {
+        float p[8];
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                float x = fast_exp2(fmaf(s[rb][e], c, -l2v[rb][e]));
+                if (MASKED) {
+                    const int key = key0 + blk * 16 + l16;
+                    const int r = rbase + rb * 16 + 4 * grp + e;
+                    x = (key < lim && key * G <= r) ? x : 0.f;
+                }
+                p[rb * 4 + e] = x;
+            }
+        return ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+    };
+    float part[NB];
+    f32x4 sv[2][2];
+    {
+        bf16x8 kf[D / 32];
+        read_k(0, kf);
+        products(kf, sv[0]);
+    }
+#pragma unroll
+    for (int blk = 0; blk < NB; ++blk) {
+        __builtin_amdgcn_sched_barrier(0);
+        if (blk + 1 < NB) {
+            bf16x8 kf[D / 32];
+            read_k(blk + 1, kf);
+            products(kf, sv[(blk + 1) & 1]);
+        }
+        part[blk] = weights(blk, sv[blk & 1]);
+        // pinned here: the sums are used only after the loop, and would
+        // otherwise sink below the later stages' products
+        asm volatile("" : "+v"(part[blk]));
+    }
+    // reduce-scatter over the four 16-lane groups: groups 0,1 keep the first
+    // half of the blocks and 2,3 the second, then 0,2 the first quarter of
+    // their half and 1,3 the second
+    const bool up2 = (grp & 2) != 0, up1 = (grp & 1) != 0;
+    float h2[NB / 2];
+#pragma unroll
+    for (int i = 0; i < NB / 2; ++i) {
+        const float keep = up2 ? part[i + NB / 2] : part[i];
+        const float send = up2 ? part[i] : part[i + NB / 2];
+        h2[i] = keep + xor32(send);
+    }
+#pragma unroll
+    for (int i = 0; i < NB / 4; ++i) {
+        const float keep = up1 ? h2[i + NB / 4] : h2[i];
+        const float send = up1 ? h2[i] : h2[i + NB / 4];
+        const float tot = keep + xor16(send);
+        const int blk = (up2 ? NB / 2 : 0) + (up1 ? NB / 4 : 0) + i;
+        colp[blk * 16 + l16] = tot;
+    }
+}
+
 // ---------------------------------------------------------------------------
 // pass 2: column sums of P per row tile
 // ---------------------------------------------------------------------------
@@ -1600,7 +1712,7 @@ __device__ __forceinline__ void colsum_tile(const uint16_t* Ks, const LdsOffsets
 constexpr int KT2 = 2 * KT;
 
 template <int D>
-__global__ __launch_bounds__(NT, 2) void attn_colsum_kernel(
+__global__ __launch_bounds__(NT, 4) void attn_colsum_kernel(
     const AttnGeom g, const int nsplit, const uint16_t* __restrict__ q,
     const uint16_t* __restrict__ kc, const uint16_t* __restrict__ kn,
     const float* __restrict__ l2, float* __restrict__ wpart) {
@@ -1617,18 +1729,21 @@ __global__ __launch_bounds__(NT, 2) void attn_colsum_kernel(
     const int W = g.C + g.S;
     const int rbase = qt * kRowsPerBlock + wave * kRowsPerWave;
     const int live = min(RB, max(0, (g.R - rbase + 31) / 32));
+    const int l16 = lane & 15, grp = lane >> 4;
 
-    bf16x8 qf[RB][D / 16];
-    load_q<D>(qf, q, g, b, h, rbase, l32, half);
-    const LdsOffsets<D> off(lane);
+    bf16x8 qf[2][D / 32];
+    load_q16<D>(qf, q, g, b, h, rbase, l16, grp);
+    uint32_t koff[D / 32];
+#pragma unroll
+    for (int ks = 0; ks < D / 32; ++ks) koff[ks] = 2u * (uint32_t)tile_off<D, false>(l16, 4 * ks + grp);
     // base-2 LSE of the rows this lane holds in the S accumulators
     // (padding rows carry +inf, so their weights are 0)
-    float l2v[RB][16];
+    float l2v[2][4];
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb)
+    for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
-        for (int v = 0; v < 16; ++v)
-            l2v[rb][v] = l2[(size_t)bh * g.rows_pad + rbase + rb * 32 + acc_row(v, half)];
+        for (int e = 0; e < 4; ++e)
+            l2v[rb][e] = l2[(size_t)bh * g.rows_pad + rbase + rb * 16 + 4 * grp + e];
 
     const TileRange tr = tile_range<KT2>(g, qt);
     const int t_begin = (int)((long)split * tr.total / nsplit);
@@ -1685,11 +1800,11 @@ __global__ __launch_bounds__(NT, 2) void attn_colsum_kernel(
                          : key0 + KT2 <= g.n) {
             // a full cache tile, or a chunk tile whose keys all exist and
             // precede this wave's first query: no mask
-            colsum_tile<D, false, false, KT2>(Ks[buf], off, colp[buf][wave], qf, l2v, g.c, 0, 0,
-                                              0, rbase, l32, half);
+            colsum_tile16<D, false, KT2>(Ks[buf], koff, colp[buf][wave], qf, l2v, g.c, 0, 0, 0,
+                                         rbase, lane);
         } else {
-            colsum_tile<D, true, false, KT2>(Ks[buf], off, colp[buf][wave], qf, l2v, g.c, key0,
-                                             lim, chunk ? g.G : 0, rbase, l32, half);
+            colsum_tile16<D, true, KT2>(Ks[buf], koff, colp[buf][wave], qf, l2v, g.c, key0, lim,
+                                        chunk ? g.G : 0, rbase, lane);
         }
         wait_tiles();
         __syncthreads();
