@@ -64,6 +64,17 @@ __device__ __forceinline__ TileRange tile_range(const AttnGeom& g, int qt) {
     return t;
 }
 
+// First tile of key split `sp` of a row tile (sp = nsplit gives tr.total):
+// the splits take contiguous ranges of equal estimated cost, a chunk tile
+// counting 7/4 of a cache tile (the chunk tiles of a row tile take longer:
+// per-workgroup timestamps of pass 1 show the split that holds them ending
+// last by about 0.7 cache tiles per chunk tile).
+__device__ __forceinline__ int split_tile(const TileRange& tr, int sp, int nsplit) {
+    const long cache_cost = 4L * tr.n_ct;
+    const long c = (long)sp * (cache_cost + 7L * (tr.total - tr.n_ct)) / nsplit;
+    return c <= cache_cost ? (int)(c / 4) : tr.n_ct + (int)((c - cache_cost) / 7);
+}
+
 // Q fragments of this lane: row rbase + rb*32 + l32, dims 16*ks + 8*half + [0, 8).
 // Serve as the B operand of S^T = K Q^T and the A operand of S = Q K^T.
 template <int D>
@@ -356,8 +367,8 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_kernel(
     const LdsOffsets<D> off(lane);
 
     const TileRange tr = tile_range(g, qt);
-    const int t_begin = (int)((long)split * tr.total / nsplit);
-    const int t_end = (int)((long)(split + 1) * tr.total / nsplit);
+    const int t_begin = split_tile(tr, split, nsplit);
+    const int t_end = split_tile(tr, split + 1, nsplit);
     const uint16_t* kc_bh = kc + (size_t)bh * g.C * D;
     const uint16_t* vc_bh = vc + (size_t)bh * g.C * D;
     const uint16_t* kn_bh = kn + (size_t)bh * g.S * D;
