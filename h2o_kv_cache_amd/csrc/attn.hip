@@ -1746,7 +1746,8 @@ __global__ __launch_bounds__(NT, 4) void attn_colsum_kernel(
     load_q16<D>(qf, q, g, b, h, rbase, l16, grp);
     uint32_t koff[D / 32];
 #pragma unroll
-    for (int ks = 0; ks < D / 32; ++ks) koff[ks] = 2u * (uint32_t)tile_off<D, false>(l16, 4 * ks + grp);
+    for (int ks = 0; ks < D / 32; ++ks)
+        koff[ks] = 2u * (uint32_t)tile_off<D, false>(l16, 4 * ks + grp);
     // base-2 LSE of the rows this lane holds in the S accumulators
     // (padding rows carry +inf, so their weights are 0)
     float l2v[2][4];
