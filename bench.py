@@ -318,7 +318,7 @@ def _host_info():
             "host_cpus": os.cpu_count(), "affinity_cpus": len(os.sched_getaffinity(0))}
 
 
-def cpu_baseline(wl, min_seconds=10.0, max_heads=24, q8=False):
+def cpu_baseline(wl, min_seconds=10.0, max_heads=4096, q8=False):
     """The oracle as it stands, run in float32 (its ``dtype`` argument), on
     single-KV-head slices of steady layer-steps, repeated until about
     ``min_seconds`` of CPU work; scaled to tokens/s of the whole workload.
@@ -580,8 +580,7 @@ def run_whole(args, wl):
             "eviction_step_ms_p10_p50_p90": pct(evict),
             "policy_stream": ("same stream" if pstream is stream else
                               "second stream, overlapped with the next layer's attention"),
-            "calls": "h2o_step (one call per layer-step)" if single_call else
-                     "h2o_attn_chunk, h2o_score_accumulate, h2o_evict_select, kv_scatter",
+            "calls": "h2o_attn_chunk, h2o_score_accumulate, h2o_evict_select, kv_scatter",
             "timing": "events around each step; inputs generated between steps",
         },
     }
@@ -669,10 +668,6 @@ def run_snapkv(args, wl):
 
     pairs = pairs_per_layer_step(B, Hq, C, S, C)
     per_layer = {k: v / calls for k, v in kernel_ms.items()}
-    if single_call and Hq // Hkv * S <= 32 and S == 1:
-        # h2o_step's decode path: the streaming pass, then the tail kernels
-        # (weights, scores and running minimum; choice and scatter)
-        per_layer = {"attn_fwd": per_layer["attn_fwd"], "decode_tail": per_layer["attn_combine"]}
     per_layer.update(part_ms)
     fwd_ms = per_layer["attn_fwd"]
     fwd_flop = 4.0 * D * pairs
