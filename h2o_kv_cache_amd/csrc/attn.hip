@@ -137,7 +137,7 @@ constexpr bf16x2 kOnes2 = {(__bf16)1.0f, (__bf16)1.0f};
 // of key j (vsc[lkb*32 + j]) multiplies P before its bf16 rounding, and O is
 // normalised by the exact row sum (lt_acc = l_acc).
 template <int D, bool MASKED, bool KSC = false, bool K8 = false, bool V8 = false,
-          bool TRACK = true, bool KREG = false>
+          bool TRACK = true>
 __device__ __forceinline__ void fwd_block(const uint16_t* Ks, const uint16_t* Vs,
                                           const LdsOffsets<D>& off,
                                           const bf16x8 (&qf)[RB][D / 16],
@@ -150,8 +150,7 @@ __device__ __forceinline__ void fwd_block(const uint16_t* Ks, const uint16_t* Vs
                                           const uint8_t* k8 = nullptr,
                                           const uint8_t* v8 = nullptr,
                                           const float* vsc = nullptr,
-                                          float* lg_stage = nullptr,
-                                          const bf16x8* kreg = nullptr) {
+                                          float* lg_stage = nullptr) {
     const int l32 = lane & 31, half = lane >> 5;
     {
         f32x16 s[RB];
@@ -168,8 +167,6 @@ __device__ __forceinline__ void fwd_block(const uint16_t* Ks, const uint16_t* Vs
             bf16x8 kf;
             if constexpr (K8)
                 kf = i8x8_to_bf16(*(const uint2*)(k8row + 16 * (ks ^ i8_swz<D>(krow))));
-            else if constexpr (KREG)
-                kf = kreg[ks];   // loaded from memory straight into registers
             else
                 kf = as_bf16x8(lds_read16(Ks, off.k[ks] + lkb * 64 * D));
 #pragma unroll
