@@ -586,7 +586,6 @@ __global__ __launch_bounds__(NT_S, 1) void attn_fwd_small_kernel(
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform per wave
     if (split == 0 && tid == 0) tail_state_init(ts, bh);   // for a tail that follows
     const int l32 = lane & 31, half = lane >> 5;
-    const int W = g.C + g.S;
 
     const TileRange tr = tile_range(g, 0);
     const int t_begin = (int)((long)split * tr.total / nsplit);
@@ -2221,8 +2220,11 @@ __device__ __forceinline__ void wait_later(int later) {
         wait_tiles();
 }
 
+// One wave per SIMD is what the kernel holds: at D = 128 its registers with
+// the accumulators exceed 256 (a higher occupancy target only made the
+// compiler spill at D = 64).
 template <int D>
-__global__ __launch_bounds__(NT_S, 3) void attn_fwd_small_q8_kernel(
+__global__ __launch_bounds__(NT_S, 1) void attn_fwd_small_q8_kernel(
     const AttnGeom g, const int nsplit, const uint16_t* __restrict__ q, const Q8Cache qc,
     const uint16_t* __restrict__ kn, const uint16_t* __restrict__ vn,
     float* __restrict__ o_part, float* __restrict__ ml_part, float* __restrict__ logits) {

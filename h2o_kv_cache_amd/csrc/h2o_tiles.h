@@ -60,6 +60,11 @@ __device__ __forceinline__ int tile_off(int key, int chunk) {
 // each transposed LDS read).  The asm has no register outputs; completion is
 // awaited explicitly with wait_tiles() before the barrier that publishes the
 // tile, and before the workgroup exits.
+// The asm sets M0 (the LDS address of the copy).  The compiler treats M0 as
+// reserved and warns about the clobber; that is safe only while no code the
+// compiler generates for these kernels keeps a value in M0, which holds for
+// every kernel of this library (their gfx950 assembly has no M0 operand
+// outside these asm blocks: no v_movrel indexing, no LDS-direct loads).
 __device__ __forceinline__ void dma16(const uint16_t* gptr, uint32_t lds) {
     asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
                  :
