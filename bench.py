@@ -898,7 +898,8 @@ def main():
     rows = Hq // Hkv * S   # packed query rows per (b, kv head)
     small = rows <= 32
     if args.kv8:
-        fwd_kernel = ("attn_fwd_small_q8_kernel<%d>" if small else "attn_fwd_q8_kernel<%d>") % D
+        fwd_kernel = ("attn_fwd_few_q8_kernel<%d>" if rows <= 16 else
+                      "attn_fwd_small_q8_kernel<%d>" if small else "attn_fwd_q8_kernel<%d>") % D
     else:
         fwd_kernel = ("attn_fwd_few_kernel<%d>" if rows <= 16 else
                       "attn_fwd_small_kernel<%d>" if small else "attn_fwd_kernel<%d>") % D

@@ -2448,6 +2448,360 @@ merge:
 }
 
 // ---------------------------------------------------------------------------
+// pass 1 over the 8-bit cache with at most 16 rows (e.g. one decode token per
+// sequence): the 16-row pass of attn_fwd_few_kernel with the codes read
+// straight from LDS and converted in registers.
+// ---------------------------------------------------------------------------
+// One 32-key block of a cache tile for one wave.  kt / vt hold the K / V
+// codes of the wave's 32 rows (swizzled by i8_swz_k16 / i8_swz_v16), ksc /
+// vsc their scales.  As fwd_block16, with the K fragments converted exactly
+// from the codes and each logit multiplied by its key's scale; P times the
+// key's V scale is rounded to bf16 for the PV product (V^T from the 8-bit
+// transposed read, in the lanes' key order), and O is normalised by the exact
+// row sum (lt = l), as in the 32-row 8-bit pass.  MASKED: the last partial
+// cache tile.
+template <int D, bool MASKED, bool TRACK>
+__device__ __forceinline__ void fwd_block16_q8(const uint8_t* kt, const uint8_t* vt,
+                                               const float* ksc, const float* vsc,
+                                               const bf16x8 (&qf)[D / 32],
+                                               f32x4 (&o_acc)[D / 16], float& m_ref,
+                                               float& m_seen, bool& overflow, float& l_acc,
+                                               float& lt_acc, float c, int kb, int key0, int lim,
+                                               int lane, float* lg_row, int col0,
+                                               float* lg_stage) {
+    const int l16 = lane & 15, g = lane >> 4;
+    // S^T of the two 16-key halves (key 16*h + l16 of the block is the A row),
+    // each over two chains of k-steps
+    f32x4 s[2];
+    {
+        f32x4 acc[2][2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int p = 0; p < 2; ++p) acc[h][p] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < D / 32; ++ks)
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int key = 16 * h + l16;
+                const int ch = 2 * ks + (g >> 1);   // dims 32*ks + 8*g + [0, 8)
+                const bf16x8 kf = i8x8_to_bf16(*(const uint2*)(
+                    kt + key * D + 16 * (ch ^ i8_swz_k16<D>(key)) + 8 * (g & 1)));
+                acc[h][ks & 1] = mfma16x16x32(kf, qf[ks], acc[h][ks & 1]);
+            }
+#pragma unroll
+        for (int h = 0; h < 2; ++h) s[h] = acc[h][0] + acc[h][1];
+    }
+    // element e of s[h] is key 16*h + 4*g + e of the block: its K scale
+    // multiplies the logit, its V scale the weight
+    f32x4 vs4[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        s[h] = s[h] * *(const f32x4*)(ksc + 16 * h + 4 * g);
+        vs4[h] = *(const f32x4*)(vsc + 16 * h + 4 * g);
+    }
+    if (MASKED) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int key = key0 + kb * 32 + 16 * h + 4 * g + e;
+                s[h][e] = key < lim ? s[h][e] : -INFINITY;
+            }
+        if (lg_row) {
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int kl = kb * 32 + 16 * h + 4 * g + e;
+                    if (key0 + kl < lim) lg_row[col0 + kl] = s[h][e] * c;
+                }
+        }
+    } else if (lg_stage) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+            *(f32x4*)(lg_stage + l16 * 32 + 16 * h + 4 * g) = s[h] * c;
+    }
+    if constexpr (TRACK) {   // as in fwd_block16
+        float mx = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
+                         fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
+        mx = fmaxf(mx, xor16(mx));
+        mx = fmaxf(mx, xor32(mx));
+        const float mt = mx * c;
+        m_seen = fmaxf(m_seen, mt);
+        m_ref = (m_ref == -INFINITY) ? mt : m_ref;
+        overflow |= mt > m_ref + kHeadroom;
+    }
+    const float m_use = (!TRACK || m_ref != -INFINITY) ? m_ref : 0.f;
+    bf16x8 pf;
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const float p = fast_exp2(fmaf(s[h][e], c, -m_use));
+            l_acc += p;
+            pf[4 * h + e] = (__bf16)(p * vs4[h][e]);
+        }
+    lt_acc = l_acc;
+    // O^T += V^T P^T: input lane j of a 16-lane group points at row vkey
+    // (b = j / 2: 4*g + b, or 16 + 4*g + b - 4) and half j % 2 of chunk db;
+    // output lane i then holds dims 16*db + i of those 8 rows as its k-values
+    const int b8 = l16 >> 1;
+    const int vkey = b8 < 4 ? 4 * g + b8 : 16 + 4 * g + b8 - 4;
+    const uint8_t* vrow = vt + vkey * D + 8 * (l16 & 1);
+    const int vsw = i8_swz_v16<D>(vkey);
+#pragma unroll
+    for (int db = 0; db < D / 16; ++db) {
+        const bf16x8 vf = i8x8_to_bf16(lds_read_tr8(vrow + 16 * (db ^ vsw)));
+        o_acc[db] = mfma16x16x32(vf, pf, o_acc[db]);
+    }
+}
+
+// Per-wave stages of the 16-row 8-bit pass (three tiles in flight while one
+// is read; a stage of one wave is 8 KiB at D = 128, so two workgroups fit a CU)
+constexpr int STAGES_FQ = 4;
+
+template <int D>
+__global__ __launch_bounds__(NT_S, 1) void attn_fwd_few_q8_kernel(
+    const AttnGeom g, const int nsplit, const uint16_t* __restrict__ q, const Q8Cache qc,
+    const uint16_t* __restrict__ kn, const uint16_t* __restrict__ vn,
+    float* __restrict__ o_part, float* __restrict__ ml_part, float* __restrict__ logits) {
+    // per wave and stage: the K codes then the V codes of its 32 rows; the
+    // first two stages of a wave take its bf16 chunk tile at the end
+    __shared__ __attribute__((aligned(16))) uint8_t stg[NW_S][STAGES_FQ][2 * 32 * D];
+    // per wave and stage: the K scales then the V scales of its 32 rows
+    __shared__ __attribute__((aligned(16))) float ssc[NW_S][STAGES_FQ][64];
+    // per wave: the base-2 logits of its key blocks of up to LGS_ROWS / R
+    // consecutive full tiles, [tile][row][key], written out together
+    constexpr int LGS_ROWS = 32;
+    __shared__ __attribute__((aligned(16))) float lgs[NW_S][LGS_ROWS * 32];
+    constexpr int PER_TILE = 2 * (32 * D / 16 / 64) + 1;   // this wave's copies per tile
+    static_assert(STAGES_FQ >= 2 && STAGES_FQ - 2 <= 3, "waits cover up to three later tiles");
+
+    int qt, bh, split;
+    decode_block(1, nsplit, qt, bh, split);
+    const int BH = g.B * g.Hkv;
+    const int b = bh / g.Hkv, h = bh % g.Hkv;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform per wave
+    const int l16 = lane & 15, grp = lane >> 4;
+
+    const TileRange tr = tile_range(g, 0);
+    const int t_begin = (int)((long)split * tr.total / nsplit);
+    const int t_end = (int)((long)(split + 1) * tr.total / nsplit);
+    const int c_end = min(t_end, tr.n_ct);   // cache tiles of this split: [t_begin, c_end)
+    const size_t row0 = (size_t)bh * g.C;
+    const uint16_t* kn_bh = kn + (size_t)bh * g.S * D;
+    const uint16_t* vn_bh = vn + (size_t)bh * g.S * D;
+
+    // Each wave copies the codes and scales of the 32 rows of its own key
+    // block of a tile and reads only those (no barrier per tile); rows past
+    // n re-read row n - 1 and are masked.  Rows read once: non-temporal.
+    auto issue = [&](int t, int sb) {
+        const int k0 = t * KT + wave * 32;
+        uint8_t* st = stg[wave][sb];
+        issue_tile_i8<D, 1, 32, 3, true>(st, qc.kc + row0 * D, k0, g.n, 0, lane);
+        issue_tile_i8<D, 1, 32, 4, true>(st + 32 * D, qc.vc + row0 * D, k0, g.n, 0, lane);
+        const int gkey = min(k0 + (lane & 31), g.n - 1);
+        dma4((lane >= 32 ? qc.vs : qc.ks) + row0 + gkey,
+             __builtin_amdgcn_readfirstlane(lds_addr(&ssc[wave][sb][0])));
+    };
+    auto prologue = [&]() {
+        for (int i = 0; i < STAGES_FQ - 1 && t_begin + i < c_end; ++i) issue(t_begin + i, i);
+    };
+    // waits until the copies of all but the `later` tiles issued last landed
+    auto wait_later_q = [&](int later) {
+        if (later >= 3)
+            wait_vm<3 * PER_TILE>();
+        else if (later == 2)
+            wait_vm<2 * PER_TILE>();
+        else if (later == 1)
+            wait_vm<PER_TILE>();
+        else
+            wait_tiles();
+    };
+    // the main sweep's first copies go out before the query loads
+    prologue();
+
+    // Q fragments (B operand of S^T = K Q^T): row l16, dims 32*ks + 8*grp + [0, 8)
+    const bool row_ok = l16 < g.R;
+    bf16x8 qf[D / 32];
+    {
+        const uint16_t* qrow =
+            q + (((size_t)b * g.Hq + (size_t)h * g.G + (l16 % g.G)) * g.S + l16 / g.G) * D +
+            8 * grp;
+#pragma unroll
+        for (int ks = 0; ks < D / 32; ++ks) {
+            u32x4 v = {0u, 0u, 0u, 0u};
+            if (row_ok) v = *(const u32x4*)(qrow + 32 * ks);
+            qf[ks] = as_bf16x8(v);
+        }
+    }
+    const LdsOffsets16<D> off(lane);   // the bf16 chunk tile
+    float* lg_row = row_ok ? logits + ((size_t)bh * g.R + l16) * logit_stride(g) : nullptr;
+    float* const logits_bh = logits + (size_t)bh * g.R * logit_stride(g);
+
+    float m_ref = 0.f, m_seen = -INFINITY, l_acc = 0.f, lt_acc = 0.f;
+    f32x4 o_acc[D / 16];
+    auto zero_state = [&]() {
+        l_acc = 0.f;
+        lt_acc = 0.f;
+#pragma unroll
+        for (int db = 0; db < D / 16; ++db) o_acc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+    };
+    // write_logits (wave-uniform): the main sweep stores the logits, the
+    // tracked sweeps do not; issued: the prologue's copies are in flight
+    auto sweep_tiles = [&](auto TRC, bool& overflow, bool write_logits, bool issued) {
+        constexpr bool TRACK = decltype(TRC)::value;
+        float* const lg = write_logits ? lg_row : nullptr;
+        const int tf = LGS_ROWS / g.R;
+        int nb = 0, b_key0 = 0;
+        auto flush = [&]() {
+            const int per = g.R * 8;   // 16-byte pieces per tile
+            for (int cix = lane; cix < nb * per; cix += 64) {
+                const int slot = cix / per, rem = cix - slot * per;
+                const int row = rem >> 3, k4 = rem & 7;
+                const f32x4 v = *(const f32x4*)&lgs[wave][(slot * g.R + row) * 32 + 4 * k4];
+                *(f32x4*)(logits_bh + (size_t)row * logit_stride(g) + b_key0 + slot * KT +
+                          wave * 32 + 4 * k4) = v;
+            }
+            nb = 0;
+        };
+        if (!issued) prologue();
+        wait_later_q(min(STAGES_FQ - 2, c_end - 1 - t_begin));
+        for (int t = t_begin; t < c_end; ++t) {
+            const int sb = (t - t_begin) % STAGES_FQ;
+            const int key0 = t * KT;
+            // the stage of tile t + STAGES_FQ - 1 was last read, by this
+            // wave, for tile t - 1
+            if (t + STAGES_FQ - 1 < c_end)
+                issue(t + STAGES_FQ - 1, (sb + STAGES_FQ - 1) % STAGES_FQ);
+            const uint8_t* st = stg[wave][sb];
+            const float* sc = &ssc[wave][sb][0];
+            if (key0 + KT <= g.n) {
+                if (nb == 0) b_key0 = key0;
+                float* const stage =
+                    (write_logits && row_ok) ? &lgs[wave][nb * g.R * 32] : nullptr;
+                fwd_block16_q8<D, false, TRACK>(st, st + 32 * D, sc, sc + 32, qf, o_acc, m_ref,
+                                                m_seen, overflow, l_acc, lt_acc, g.c, wave, key0,
+                                                g.n, lane, nullptr, key0, stage);
+                if (write_logits && ++nb == tf) flush();
+            } else {
+                if (nb > 0) flush();
+                fwd_block16_q8<D, true, TRACK>(st, st + 32 * D, sc, sc + 32, qf, o_acc, m_ref,
+                                               m_seen, overflow, l_acc, lt_acc, g.c, wave, key0,
+                                               g.n, lane, lg, key0, nullptr);
+            }
+            // this wave's copies of tile t+1 must have landed; tiles issued
+            // after it may stay in flight
+            wait_later_q(min(STAGES_FQ - 2, c_end - 1 - (t + 1)));
+        }
+        if (nb > 0) flush();
+        if (t_end > tr.n_ct) {   // the chunk tile (S <= 16 here: a single tile)
+            const int key0 = (t_end - 1 - tr.n_ct) * KT;
+            // bf16 K and V rows of this wave's key block in its first two
+            // stages (every copy of this wave has landed; no other wave
+            // touches them); the chunk's K has no scale
+            wait_tiles();
+            uint16_t* mk = (uint16_t*)stg[wave][0];
+            uint16_t* mv = mk + 32 * D;
+            constexpr int CPR = D / 8;
+#pragma unroll
+            for (int u0 = 0; u0 < 32 * CPR; u0 += 64) {
+                const int u = u0 + lane;
+                const int r = u / CPR, cc = u % CPR;
+                const int key = min(key0 + wave * 32 + r, g.S - 1);
+                *(u32x4*)(mk + tile_off<D, false>(r, cc)) =
+                    *(const u32x4*)(kn_bh + (size_t)key * D + cc * 8);
+                *(u32x4*)(mv + tile_off<D, true>(r, cc)) =
+                    *(const u32x4*)(vn_bh + (size_t)key * D + cc * 8);
+            }
+            // the cache blocks set lt = l; this bf16 block adds its rounded weights
+            fwd_block16<D, true, TRACK>(mk, mv, off, qf, o_acc, m_ref, m_seen, overflow, l_acc,
+                                        lt_acc, g.c, wave, key0, g.S, true, g.G, lane, lg,
+                                        g.C + key0, 0, nullptr);
+        }
+    };
+    // the row sum of a lane's row: its 4 lanes (l16 + 16*grp)
+    auto row_sum = [&](float x) {
+        x += xor16(x);
+        return x + xor32(x);
+    };
+
+    // Main sweep: each row's reference is its own base-2 logit against its
+    // diagonal chunk key (bf16); row sums above 2^kHeadroom send the
+    // workgroup to the tracked sweeps.
+    {
+        bool overflow = false;
+        const uint16_t* kself = kn_bh + (size_t)(row_ok ? l16 / g.G : 0) * D + 8 * grp;
+        float dot = 0.f;
+#pragma unroll
+        for (int ks = 0; ks < D / 32; ++ks) {
+            const bf16x8 kv = as_bf16x8(*(const u32x4*)(kself + 32 * ks));
+#pragma unroll
+            for (int e = 0; e < 8; ++e) dot = fmaf((float)qf[ks][e], (float)kv[e], dot);
+        }
+        dot = row_sum(dot);
+        m_ref = row_ok ? dot * g.c : 0.f;
+        zero_state();
+        sweep_tiles(TrackC<false>{}, overflow, true, true);
+        overflow |= !(row_sum(l_acc) <= kSumLimit);
+        if (!__syncthreads_or(overflow)) goto merge;
+    }
+    // tracked sweeps (rare): first-tile reference with every tile max
+    // recorded, then, if still overshot, the exact row max
+    for (int sweep = 0; sweep < 2; ++sweep) {
+        bool overflow = false;
+        m_ref = (sweep == 0) ? -INFINITY : m_seen;
+        zero_state();
+        sweep_tiles(TrackC<true>{}, overflow, false, false);
+        if (!__syncthreads_or(overflow)) break;
+    }
+
+merge:
+    // merge the waves' (m, l, lt, O) through LDS (the stages are free now)
+    {
+        const float l = row_sum(l_acc);
+        const float lt = row_sum(lt_acc);
+        constexpr int XS = D / 4 + 4;   // [NW_S][64 lanes][XS] floats
+        static_assert(NW_S * 64 * XS * 4 <= (int)sizeof(stg), "merge area exceeds the stages");
+        float* xch = (float*)&stg[0][0][0];
+        float* mine = xch + ((size_t)wave * 64 + lane) * XS;
+#pragma unroll
+        for (int db = 0; db < D / 16; ++db) *(f32x4*)(mine + 4 * db) = o_acc[db];
+        mine[D / 4 + 0] = m_ref;
+        mine[D / 4 + 1] = l;
+        mine[D / 4 + 2] = lt;
+        __syncthreads();
+        if (wave != 0) return;
+        float M = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < NW_S; ++w) M = fmaxf(M, xch[((size_t)w * 64 + lane) * XS + D / 4]);
+        float wt[NW_S], L = 0.f, Lt = 0.f;
+#pragma unroll
+        for (int w = 0; w < NW_S; ++w) {
+            const float* o = xch + ((size_t)w * 64 + lane) * XS;
+            wt[w] = (M == -INFINITY) ? 0.f : fast_exp2(o[D / 4] - M);
+            L += wt[w] * o[D / 4 + 1];
+            Lt += wt[w] * o[D / 4 + 2];
+        }
+        if (!row_ok) return;
+        const size_t prow = ((size_t)split * BH + bh) * g.rows_pad + l16;
+        if (grp == 0) *(f32x4*)(ml_part + prow * 4) = f32x4{M, L, Lt, 0.f};
+        float* orow = o_part + prow * D;
+        // lane holds dims 16*db + 4*grp + [0, 4) of its row
+#pragma unroll
+        for (int db = 0; db < D / 16; ++db) {
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int w = 0; w < NW_S; ++w)
+                acc += wt[w] * *(const f32x4*)(xch + ((size_t)w * 64 + lane) * XS + 4 * db);
+            *(f32x4*)(orow + 16 * db + 4 * grp) = acc;
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // sum the row-tile partials in tile order
 // ---------------------------------------------------------------------------
 // With non-null `scores` the kernel also accumulates, as wsum_from_logits_kernel.
@@ -2528,7 +2882,10 @@ hipError_t launch_attention_d(const AttnPlan& pl, const uint16_t* q,
 
     H2O_EVENT(0);
     if constexpr (Q8) {
-        if (pl.small)
+        if (pl.small && g.R <= kFewRows)
+            hipLaunchKernelGGL(attn_fwd_few_q8_kernel<D>, dim3(BH * pl.split1), dim3(NT_S), 0,
+                               stream, g, pl.split1, q, qc, kn, vn, o_part, ml_part, wpart);
+        else if (pl.small)
             hipLaunchKernelGGL(attn_fwd_small_q8_kernel<D>, dim3(BH * pl.split1), dim3(NT_S), 0,
                                stream, g, pl.split1, q, qc, kn, vn, o_part, ml_part, wpart);
         else

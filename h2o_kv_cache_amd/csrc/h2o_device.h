@@ -48,7 +48,9 @@ __device__ __forceinline__ uint32_t pack_lo(uint32_t a, uint32_t b) {
     return (a & 0xFFFFu) | (b << 16);
 }
 __device__ __forceinline__ uint32_t pack_hi(uint32_t a, uint32_t b) {
-    return (a >> 16) | (b & 0xFFFF0000u);
+    // one byte permute: bytes 2, 3 of a, then bytes 2, 3 of b (selector
+    // values 0-3 pick bytes of the second operand, 4-7 of the first)
+    return __builtin_amdgcn_perm(b, a, 0x07060302u);
 }
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) {

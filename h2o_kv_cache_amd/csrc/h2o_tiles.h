@@ -198,8 +198,24 @@ __device__ __forceinline__ int i8_swz_v(int key) {
     return D >= 128 ? ((key & 3) | ((key >> 1) & 4)) : (key & 3);
 }
 
-// SWZ: 0 none, 1 i8_swz (K tiles), 2 i8_swz_v (V tiles); NT: non-temporal
-// copies (rows read once)
+// Tiles of the 16-row pass (32 rows per wave).  K: a 16-lane group reads one
+// chunk of 16 consecutive rows; chunk ^ (key * CPR / 16 mod CPR) puts the 16
+// rows (and the two 8-byte halves the two groups of a half-wave read) on
+// distinct banks.  V, 8-bit transposed read: a 16-lane group reads rows
+// 4g + {0,1,2,3} and 16 + 4g + {0,1,2,3}; the swizzle below gives the 16 rows
+// of a half-wave distinct banks (checked for D = 64 and 128).
+template <int D>
+__device__ __forceinline__ int i8_swz_k16(int key) {
+    return (key * (D / 16) / 16) & (D / 16 - 1);
+}
+template <int D>
+__device__ __forceinline__ int i8_swz_v16(int key) {
+    return D >= 128 ? (((key >> 1) & 3) | (((key >> 4) & 1) << 2))
+                    : (((key >> 2) & 1) | (((key >> 4) & 1) << 1));
+}
+
+// SWZ: 0 none, 1 i8_swz (K tiles), 2 i8_swz_v (V tiles), 3 i8_swz_k16 and
+// 4 i8_swz_v16 (16-row pass); NT: non-temporal copies (rows read once)
 template <int D, int NW, int ROWS = kKeyTile, int SWZ = 0, bool NT = false>
 __device__ __forceinline__ void issue_tile_i8(uint8_t* tile, const int8_t* __restrict__ src,
                                               int key0, int lim, int wave, int lane) {
@@ -212,7 +228,12 @@ __device__ __forceinline__ void issue_tile_i8(uint8_t* tile, const int8_t* __res
         if (blk < NBLK) {
             const int p = blk * 64 + lane;
             const int key = p / CPR;
-            const int c = (p % CPR) ^ (SWZ == 1 ? i8_swz<D>(key) : SWZ == 2 ? i8_swz_v<D>(key) : 0);
+            const int sw = SWZ == 1   ? i8_swz<D>(key)
+                           : SWZ == 2 ? i8_swz_v<D>(key)
+                           : SWZ == 3 ? i8_swz_k16<D>(key)
+                           : SWZ == 4 ? i8_swz_v16<D>(key)
+                                      : 0;
+            const int c = (p % CPR) ^ sw;
             const int gkey = min(key0 + key, lim - 1);
             const uint16_t* g = (const uint16_t*)(src + (size_t)gkey * D + c * 16);
             if constexpr (NT)

@@ -101,6 +101,12 @@ ATTN = [
     ("few_rows_chunk", 1, 8,  2,   128, 700,  8,   650),
     ("few_rows_d64",   1, 3,  3,   64,  257,  20,  257),
     ("g16_multi_tile", 1, 16, 1,   128, 520,  40,  333),
+    # at most 16 rows (G * S): the 16-row kernel
+    ("rows_16",        1, 4,  1,   128, 700,  4,   650),
+    ("rows_15_d64",    2, 6,  2,   64,  333,  5,   300),
+    ("rows_16_g16",    1, 16, 1,   128, 200,  1,   130),
+    ("rows_8_empty",   1, 8,  2,   128, 64,   2,   0),
+    ("rows_1",         1, 1,  1,   128, 100,  1,   100),
 ]
 
 
@@ -117,7 +123,8 @@ def test_attention_q8_small(name, B, Hq, Hkv, D, C, S, n):
 @pytest.mark.parametrize("B,Hq,Hkv,D,C,S,n,slot,col", [
     (1, 4, 1, 128, 1024, 128, 1024, 700, 90),    # row-tile kernel
     (2, 8, 2, 128, 1000, 1, 1000, 300, -1),      # few-row (decode) kernel; the one
-])                                               # chunk key (each row's own) stays plain
+    (1, 4, 1, 64, 600, 2, 600, 100, -1),         # chunk key (each row's own) stays plain
+])
 def test_attention_q8_wide_logit_spread(B, Hq, Hkv, D, C, S, n, slot, col):
     """All-positive queries against one cache slot and one chunk key of
     constant 8.0 (int8 codes 127, scale 8/127): their base-2 logits exceed
