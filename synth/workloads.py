@@ -87,6 +87,12 @@ WORKLOADS = {
     # small chunks at 64k: C=8192, S=128 (the pages' 128-token setting), 36 layers
     "qwen3_4b_64k_s128": Workload("qwen3_4b_64k_s128", 5, 1, 32, 8, 128, 8192, 128,
                                   65536, 36, 1.0, 0.05, 4.0, False),
+    # the same layers with 256- and 512-token chunks (between the 128-token
+    # setting and the 1k/2k chunks)
+    "qwen3_4b_64k_s256": Workload("qwen3_4b_64k_s256", 8, 1, 32, 8, 128, 8192, 256,
+                                  65536, 36, 1.0, 0.05, 4.0, False),
+    "qwen3_4b_64k_s512": Workload("qwen3_4b_64k_s512", 9, 1, 32, 8, 128, 8192, 512,
+                                  65536, 36, 1.0, 0.05, 4.0, False),
     # one GPU's share of the 128k layers under 8-way KV-head sharding: one KV
     # head with its 4 query heads, same cache, chunk and value distribution
     "qwen3_4b_128k_head": Workload("qwen3_4b_128k_head", 7, 1, 4, 1, 128, 16384, 1024,

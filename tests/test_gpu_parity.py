@@ -109,6 +109,17 @@ def test_qwen3_64k_small_chunk_fill_step():
     _steady(wl, heads=[0], step=17, n_valid=17 * wl.chunk_len)
 
 
+@pytest.mark.parametrize("name", ["qwen3_4b_64k_s256", "qwen3_4b_64k_s512"])
+def test_qwen3_64k_mid_chunk_steady_step(name):
+    wl = WORKLOADS[name]
+    _steady(wl, heads=[1, 4], step=wl.fill_steps + 5, layer=2)
+
+
+def test_qwen3_64k_s512_fill_step():
+    wl = WORKLOADS["qwen3_4b_64k_s512"]
+    _steady(wl, heads=[6], step=7, n_valid=7 * wl.chunk_len)
+
+
 def test_decode_steps():
     wl = WORKLOADS["decode"]
     st = state_from_synth(synth.prefilled_state(wl))
