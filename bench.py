@@ -722,8 +722,8 @@ def main():
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU: the H2O step shards by KV head or by "
-              "sequence with no exchange, and runs on more than one GPU are not "
-              "part of this build (use --gpus 1).", file=sys.stderr)
+              "sequence with no exchange, so a run on more than one GPU measures "
+              "nothing a single GPU does not (use --gpus 1).", file=sys.stderr)
         sys.exit(2)
 
     import torch
