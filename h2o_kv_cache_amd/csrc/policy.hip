@@ -192,7 +192,7 @@ __global__ __launch_bounds__(SEL_T) void evict_select_kernel(
     __shared__ uint32_t hist[3][256];
     __shared__ uint32_t sh_scan[2 * (SEL_T / 64)];
     __shared__ unsigned long long sh_min;
-    __shared__ uint32_t sh_kmin, sh_kmax;
+    __shared__ uint32_t sh_lohi[2][SEL_T / 64];   // per wave: smallest and largest key
     __shared__ int32_t sh_slot[DS > 0 ? SEL_SLOTS : 1];   // the choice, for the scatter
 
     const int bh = blockIdx.x, tid = threadIdx.x;
@@ -323,19 +323,20 @@ __global__ __launch_bounds__(SEL_T) void evict_select_kernel(
         lo = min(lo, (uint32_t)__shfl_xor(lo, off, 64));
         hi = max(hi, (uint32_t)__shfl_xor(hi, off, 64));
     }
-    if (tid == 0) {
-        sh_kmin = 0xFFFFFFFFu;
-        sh_kmax = 0u;
+    if ((tid & 63) == 0) {
+        sh_lohi[0][tid >> 6] = lo;
+        sh_lohi[1][tid >> 6] = hi;
     }
     // all three buffers start cleared: the first pass that runs may be any
     for (int i = tid; i < 3 * 256; i += SEL_T) hist[i / 256][i % 256] = 0u;
     __syncthreads();
-    if ((tid & 63) == 0) {
-        atomicMin(&sh_kmin, lo);
-        atomicMax(&sh_kmax, hi);
+    uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
+#pragma unroll
+    for (int w = 0; w < SEL_T / 64; ++w) {
+        kmin = min(kmin, sh_lohi[0][w]);
+        kmax = max(kmax, sh_lohi[1][w]);
     }
-    __syncthreads();
-    const uint32_t kmin = sh_kmin, diff = kmin ^ sh_kmax;
+    const uint32_t diff = kmin ^ kmax;
     const int first = diff == 0u ? 4 : __builtin_clz(diff) / 8;   // passes 0..first-1 skipped
     uint32_t mask = first >= 4 ? 0xFFFFFFFFu : (first == 0 ? 0u : ~0u << (32 - 8 * first));
     uint32_t prefix = kmin & mask, k = (uint32_t)S;   // k: 1-based rank
